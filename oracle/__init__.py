@@ -1,0 +1,207 @@
+"""CPU oracle for the ELMO classifier-head step (ctypes binding of ``elmo_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP product path never imports it and shares no code
+with it.
+
+The C source follows the ELMO pages ("ELMO: Efficiency via Low-precision and Peak Memory Optimization
+in Large Output Spaces": atlas.scime.ai summary, "Approach" and "Surprising findings"; arXiv
+2510.11168 abstract). The readings it implements where the pages are silent are listed in the
+C header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "elmo_oracle.c")
+_LIB = os.path.join(_HERE, "libelmo_oracle.so")
+
+W_BF16 = 0
+W_E4M3 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        u8, u16, u32, u64, i32, i64 = (ctypes.c_uint8, ctypes.c_uint16, ctypes.c_uint32,
+                                       ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64)
+        P = ctypes.c_void_p
+        L.orc_bf16_value.argtypes = [u16]; L.orc_bf16_value.restype = ctypes.c_double
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]; L.orc_bf16_rne.restype = u16
+        L.orc_e4m3_value.argtypes = [u8]; L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_rne_sat.argtypes = [ctypes.c_double]; L.orc_e4m3_rne_sat.restype = u8
+        L.orc_sr_bf16.argtypes = [ctypes.c_float, u32]; L.orc_sr_bf16.restype = u16
+        L.orc_sr_e4m3.argtypes = [ctypes.c_float, u32]; L.orc_sr_e4m3.restype = u8
+        L.orc_philox4x32.argtypes = [P, P, ctypes.c_int, P]; L.orc_philox4x32.restype = None
+        L.orc_r16.argtypes = [u64, u64, u64]; L.orc_r16.restype = u32
+        L.orc_grad_code.argtypes = [ctypes.c_float, ctypes.c_int]; L.orc_grad_code.restype = u16
+        for name in ("orc_bf16_rne_array", "orc_e4m3_rne_sat_array"):
+            getattr(L, name).argtypes = [P, P, i64]; getattr(L, name).restype = None
+        for name in ("orc_sr_bf16_array", "orc_sr_e4m3_array"):
+            getattr(L, name).argtypes = [P, P, P, i64]; getattr(L, name).restype = None
+        L.orc_r16_array.argtypes = [u64, u64, u64, P, i64]; L.orc_r16_array.restype = None
+        L.orc_step.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
+                               ctypes.c_float, u64, u64, P, P, P, P, ctypes.c_int]
+        L.orc_logits.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P,
+                                 ctypes.c_int, P, ctypes.c_int]
+        L.orc_update_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
+                                      ctypes.c_float, u64, u64, P, ctypes.c_int, P, ctypes.c_int]
+        L.orc_dx_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P, P,
+                                  ctypes.c_int, P, ctypes.c_int]
+        L.orc_grad_exact.argtypes = [i64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P]
+        L.orc_topk.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
+                               P, P, ctypes.c_int]
+        for name in ("orc_step", "orc_logits", "orc_update_rows", "orc_dx_rows", "orc_grad_exact",
+                     "orc_topk"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _chk(rc, name):
+    if rc != 0:
+        raise RuntimeError(f"oracle {name} failed with status {rc}")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def wdtype_np(wfmt):
+    return np.uint16 if wfmt == W_BF16 else np.uint8
+
+
+# ---- scalar / elementwise codecs ---------------------------------------------------------------
+
+def bf16_value(codes):
+    c = _c(codes, np.uint16)
+    return np.array([lib().orc_bf16_value(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def bf16_rne(x):
+    x = _c(x, np.float32); out = np.empty(x.shape, np.uint16)
+    lib().orc_bf16_rne_array(_p(x), _p(out), x.size); return out
+
+
+def e4m3_value(codes):
+    c = _c(codes, np.uint8)
+    return np.array([lib().orc_e4m3_value(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e4m3_rne_sat(x):
+    x = _c(x, np.float64); out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_rne_sat_array(_p(x), _p(out), x.size); return out
+
+
+def sr_bf16(t, r):
+    t = _c(t, np.float32); r = _c(np.broadcast_to(r, t.shape), np.uint32)
+    out = np.empty(t.shape, np.uint16); lib().orc_sr_bf16_array(_p(t), _p(r), _p(out), t.size)
+    return out
+
+
+def sr_e4m3(t, r):
+    t = _c(t, np.float32); r = _c(np.broadcast_to(r, t.shape), np.uint32)
+    out = np.empty(t.shape, np.uint8); lib().orc_sr_e4m3_array(_p(t), _p(r), _p(out), t.size)
+    return out
+
+
+def philox4x32(ctr, key, rounds=10):
+    c = _c(ctr, np.uint32); k = _c(key, np.uint32); out = np.empty(4, np.uint32)
+    lib().orc_philox4x32(_p(c), _p(k), rounds, _p(out)); return out
+
+
+def r16(seed, step, idx0, n):
+    out = np.empty(n, np.uint32); lib().orc_r16_array(seed, step, idx0, _p(out), n); return out
+
+
+def grad_code(z, y):
+    return lib().orc_grad_code(float(z), int(y))
+
+
+# ---- the step ----------------------------------------------------------------------------------
+
+def step(wfmt, W, X, row_ptr, ids, lr, seed, step_, want_z=False, want_g=False, want_loss=False,
+         nthreads=0):
+    """Returns (W_new, dX, loss|None, Z|None, G|None); W is not modified."""
+    Wn = np.array(W, dtype=wdtype_np(wfmt), order="C", copy=True)
+    L, D = Wn.shape
+    X = _c(X, np.uint16); B = X.shape[0]
+    rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32)
+    dX = np.empty((B, D), np.float32)
+    Z = np.empty((B, L), np.float32) if want_z else None
+    G = np.empty((B, L), np.uint16) if want_g else None
+    loss = ctypes.c_double(0.0)
+    rc = lib().orc_step(wfmt, _p(Wn), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
+                        float(lr), seed, step_, _p(dX),
+                        ctypes.cast(ctypes.pointer(loss), ctypes.c_void_p) if want_loss else None,
+                        _p(Z), _p(G), nthreads)
+    _chk(rc, "step")
+    return Wn, dX, (loss.value if want_loss else None), Z, G
+
+
+def logits(wfmt, W, X, js, nthreads=0):
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    js = _c(js, np.int64); Z = np.empty((B, js.size), np.float32)
+    _chk(lib().orc_logits(wfmt, _p(W), L, D, _p(X), B, _p(js), js.size, _p(Z), nthreads), "logits")
+    return Z
+
+
+def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0):
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32); js = _c(js, np.int64)
+    out = np.empty((js.size, D), wdtype_np(wfmt))
+    _chk(lib().orc_update_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
+                               float(lr), seed, step_, _p(js), js.size, _p(out), nthreads),
+         "update_rows")
+    return out
+
+
+def dx_rows(wfmt, W, X, row_ptr, ids, bs, nthreads=0):
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32); bs = _c(bs, np.int32)
+    out = np.empty((bs.size, D), np.float32)
+    _chk(lib().orc_dx_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
+                           _p(bs), bs.size, _p(out), nthreads), "dx_rows")
+    return out
+
+
+def grad_exact(W, X, Y):
+    W = _c(W, np.float64); X = _c(X, np.float64); Y = _c(Y, np.float64)
+    L, D = W.shape; B = X.shape[0]
+    Z = np.empty((B, L)); G = np.empty((B, L)); dX = np.empty((B, D)); dW = np.empty((L, D))
+    loss = ctypes.c_double(0.0)
+    _chk(lib().orc_grad_exact(L, D, B, _p(W), _p(X), _p(Y), _p(Z), _p(G), _p(dX), _p(dW),
+                              ctypes.cast(ctypes.pointer(loss), ctypes.c_void_p)), "grad_exact")
+    return Z, G, dX, dW, loss.value
+
+
+def topk(wfmt, W, X, k, nthreads=0):
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); N = X.shape[0]
+    idx = np.empty((N, k), np.int32); score = np.empty((N, k), np.float32)
+    _chk(lib().orc_topk(wfmt, _p(W), L, D, _p(X), N, k, _p(idx), _p(score), nthreads), "topk")
+    return idx, score

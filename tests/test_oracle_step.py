@@ -1,0 +1,259 @@
+"""Pins of the oracle's training step, loss gradient and top-k scoring.
+
+* Finite differences of the summed sigmoid-BCE loss (the loss is not printed on the pages; it is the
+  reading documented with the build) in the unquantised binary64 mode.
+* The closed form G = sigmoid(Z) - Y against scipy's expit, and the W = 0 special case.
+* The three contractions against numpy binary64 matmul of the torch-decoded operands.
+* The SGD + stochastic-rounding update against an exact rational recomputation.
+* Invariants: lr = 0, label-set semantics, sampled entry points equal to the full step.
+* Top-k against numpy lexsort / argmax, with exact ties from duplicated weight rows.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import workloads as wk
+
+
+def _bf16_val(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint16).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _e4m3_val(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _wval(wfmt, W):
+    return _bf16_val(W) if wfmt == wk.W_BF16 else _e4m3_val(W)
+
+
+def _dense_y(B, L, rp, ids):
+    Y = np.zeros((B, L))
+    for b in range(B):
+        Y[b, ids[rp[b]:rp[b + 1]]] = 1.0
+    return Y
+
+
+def _small_case(wfmt, B=9, D=64, L=300, seed=0, lam=3.0):
+    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=B, D=D, L=L, wfmt=wfmt, lam=lam, seed=seed)
+    bt = wk.make_batch(wl)
+    W = wk.make_weights(wl)
+    return wl, W, bt
+
+
+# ---------------------------------------------------------------------------------------------- #
+def test_finite_difference_gradients(orc):
+    g = np.random.default_rng(5)
+    B, D, L = 3, 5, 7
+    W = g.standard_normal((L, D)); X = g.standard_normal((B, D))
+    Y = (g.random((B, L)) < 0.3).astype(np.float64)
+    Z, G, dX, dW, loss = orc.grad_exact(W, X, Y)
+    h = 1e-6
+    for j in range(L):
+        for k in range(D):
+            Wp = W.copy(); Wp[j, k] += h; Wm = W.copy(); Wm[j, k] -= h
+            fd = (orc.grad_exact(Wp, X, Y)[4] - orc.grad_exact(Wm, X, Y)[4]) / (2 * h)
+            assert abs(fd - dW[j, k]) <= 1e-6 * max(1.0, abs(dW[j, k]))
+    for b in range(B):
+        for k in range(D):
+            Xp = X.copy(); Xp[b, k] += h; Xm = X.copy(); Xm[b, k] -= h
+            fd = (orc.grad_exact(W, Xp, Y)[4] - orc.grad_exact(W, Xm, Y)[4]) / (2 * h)
+            assert abs(fd - dX[b, k]) <= 1e-6 * max(1.0, abs(dX[b, k]))
+    # dL/dZ through a bias-like perturbation: shifting z_bj by h is the same as adding h / x_bk * e_jk
+    # to W when only x_bk is non-zero; check directly on a one-hot X instead
+    X1 = np.zeros((B, D)); X1[:, 0] = 1.0
+    Z1, G1, *_ = orc.grad_exact(W, X1, Y)
+    for b in range(B):
+        for j in range(L):
+            Wp = W.copy(); Wp[j, 0] += h; Wm = W.copy(); Wm[j, 0] -= h
+            Yb = Y.copy()
+            lp = orc.grad_exact(Wp, X1, Yb)[4]; lm = orc.grad_exact(Wm, X1, Yb)[4]
+            # with X1, z_bj = W[j, 0] for every b, so the derivative sums over b
+            if b == 0:
+                assert abs((lp - lm) / (2 * h) - G1[:, j].sum()) <= 1e-6
+    # loss definition: sum of softplus(z) - y z
+    assert abs(loss - (np.logaddexp(0, Z) - Y * Z).sum()) <= 1e-12 * abs(loss)
+
+
+def test_gradient_code_matches_expit(orc):
+    g = np.random.default_rng(6)
+    z = np.concatenate([g.standard_normal(4000) * 3, g.uniform(-80, 80, 4000),
+                        [0.0, -0.0, 1e-8, -1e-8, 88.0, -88.0, 200.0, -200.0]]).astype(np.float32)
+    for y in (0, 1):
+        ref64 = scipy.special.expit(z.astype(np.float64)) if y == 0 else -scipy.special.expit(-z.astype(np.float64))
+        ref = torch.from_numpy(ref64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = np.array([orc.grad_code(float(v), y) for v in z], np.uint16)
+        # scipy's expit and binary64 exp may differ in the last binary64 bit: allow mismatches only
+        # where the binary32 value sits on a rounding boundary, i.e. none in practice
+        assert (got != ref).sum() <= 1
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_zero_weights_closed_form(orc, wfmt):
+    wl, W, bt = _small_case(wfmt)
+    W0 = np.zeros_like(W)
+    lr = 0.05
+    Wn, dX, loss, Z, G = orc.step(wfmt, W0, bt.X, bt.row_ptr, bt.ids, lr, 1, 0, want_z=True, want_g=True,
+                                  want_loss=True)
+    Y = _dense_y(wl.B, wl.L, bt.row_ptr, bt.ids)
+    assert np.all(Z == 0.0)
+    assert np.array_equal(_bf16_val(G), 0.5 - Y)
+    assert np.all(dX == 0.0)
+    x = _bf16_val(bt.X)
+    dW = ((0.5 - Y).T @ x).astype(np.float32)      # exact in binary64 at these sizes
+    t = (-np.float64(np.float32(lr)) * dW.astype(np.float64)).astype(np.float32)
+    new = _wval(wfmt, Wn)
+    # stochastic rounding lands on one of the two neighbours of t
+    tab = _bf16_val(np.arange(0, 0x7F80, dtype=np.uint16)) if wfmt == wk.W_BF16 else _e4m3_val(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(t.astype(np.float64))
+    i = np.searchsorted(tab, a, side="right") - 1
+    lo = tab[i]; hi = tab[np.minimum(i + 1, tab.size - 1)]
+    assert np.all((np.abs(new) == lo) | (np.abs(new) == hi))
+    assert abs(loss - wl.B * wl.L * np.log(2.0)) <= 1e-9 * loss
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_contractions_match_numpy_matmul(orc, wfmt):
+    wl, W, bt = _small_case(wfmt, B=17, D=128, L=257)
+    lr = np.float32(0.05)
+    Wn, dX, loss, Z, G = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, lr, 3, 2, want_z=True, want_g=True)
+    w = _wval(wfmt, W)
+    x = _bf16_val(bt.X)
+    xt = x if wfmt == wk.W_BF16 else _e4m3_val(
+        torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    Zref = (xt @ w.T).astype(np.float32)
+    assert np.array_equal(Z, Zref)
+    g = _bf16_val(G)
+    Y = _dense_y(wl.B, wl.L, bt.row_ptr, bt.ids)
+    # G against expit of the oracle's own FP32 logits
+    ref64 = np.where(Y > 0, -scipy.special.expit(-Z.astype(np.float64)), scipy.special.expit(Z.astype(np.float64)))
+    gref = _bf16_val(torch.from_numpy(ref64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert (g != gref).sum() <= 1
+    assert np.array_equal(dX, (g @ w).astype(np.float32))
+    dW = (g.T @ x).astype(np.float32)
+    # update: t = FP32(w - lr * dW) rounded once; SR with the oracle's random bits
+    rng_rows = orc.r16(3, 2, 0, wl.L * wl.D).reshape(wl.L, wl.D)
+    sample = np.random.default_rng(0).integers(0, wl.L * wl.D, 3000)
+    for s in sample:
+        j, k = divmod(int(s), wl.D)
+        exact = Fraction(float(w[j, k])) - Fraction(float(lr)) * Fraction(float(dW[j, k]))
+        t = _round_f32(exact)
+        if wfmt == wk.W_BF16:
+            want = orc.sr_bf16(np.array([t], np.float32), np.array([rng_rows[j, k]], np.uint32))[0]
+        else:
+            want = orc.sr_e4m3(np.array([t], np.float32), np.array([rng_rows[j, k]], np.uint32))[0]
+        assert Wn[j, k] == want
+
+
+def _round_f32(fr: Fraction) -> np.float32:
+    """Correctly rounded (nearest-even) binary32 of a rational."""
+    f = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (int(np.float32(c).view(np.uint32)) & 1) == 0):
+            best = (d, c)
+    return np.float32(best[1])
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_lr_zero_leaves_weights_unchanged(orc, wfmt):
+    wl, W, bt = _small_case(wfmt)
+    Wn, *_ = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, 0.0, 1, 0)
+    # equal values; a negative zero may come back positive (IEEE: -0 * g + -0 is +0 for g < 0)
+    assert np.array_equal(_wval(wfmt, Wn), _wval(wfmt, W))
+    zero_flip = Wn != W
+    assert np.all(_wval(wfmt, W)[zero_flip] == 0.0)
+
+
+def test_label_set_semantics(orc):
+    wl, W, bt = _small_case(wk.W_BF16, B=6, L=120)
+    g = np.random.default_rng(9)
+    rows = [bt.ids[bt.row_ptr[b]:bt.row_ptr[b + 1]] for b in range(wl.B)]
+    rows2 = [g.permutation(np.concatenate([r, r[: len(r) // 2 + 1]])) for r in rows]  # shuffled, duplicated
+    rows2[2] = np.zeros(0, np.int32)                                                   # an empty row
+    rows1 = [np.unique(r) for r in rows2]
+    def csr(rs):
+        rp = np.zeros(len(rs) + 1, np.int32); rp[1:] = np.cumsum([len(r) for r in rs])
+        return rp, (np.concatenate(rs).astype(np.int32) if sum(map(len, rs)) else np.zeros(0, np.int32))
+    a = orc.step(0, W, bt.X, *csr(rows1), 0.05, 4, 1)
+    b = orc.step(0, W, bt.X, *csr(rows2), 0.05, 4, 1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    with pytest.raises(RuntimeError):
+        rp, ids = csr(rows1); ids = ids.copy(); ids[0] = wl.L
+        orc.step(0, W, bt.X, rp, ids, 0.05, 4, 1)
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_sampled_entry_points_equal_full_step(orc, wfmt):
+    wl, W, bt = _small_case(wfmt, B=11, D=64, L=333)
+    Wn, dX, _, Z, _ = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, wl.lr, 5, 3, want_z=True)
+    js = np.array([0, 1, 17, 200, 332], np.int64)
+    assert np.array_equal(orc.logits(wfmt, W, bt.X, js), Z[:, js])
+    assert np.array_equal(orc.update_rows(wfmt, W, bt.X, bt.row_ptr, bt.ids, wl.lr, 5, 3, js), Wn[js])
+    bs = np.array([0, 4, 10], np.int32)
+    d = orc.dx_rows(wfmt, W, bt.X, bt.row_ptr, bt.ids, bs)
+    # same definition, different binary64 summation order: equal up to one binary32 ulp
+    assert np.all(np.abs(d - dX[bs]) <= np.spacing(np.abs(dX[bs])))
+
+
+def test_saturated_dyadic_step_is_exact(orc):
+    """X, W in {+-2^-3} with a dominant first column make |z| >= 116, so the FP32 sigmoid is exactly
+    0 or 1 and every intermediate is exact; the result is predicted without the oracle."""
+    g = np.random.default_rng(11)
+    B, D, L = 8, 64, 96
+    xs = g.choice([-1.0, 1.0], (B, D)) * 0.125
+    ws = g.choice([-1.0, 1.0], (L, D)) * 0.125
+    xs[:, 0] = g.choice([-128.0, 128.0], B)
+    ws[:, 0] = g.choice([-1.0, 1.0], L)
+    X = wk.to_bf16_codes(xs); W = wk.to_bf16_codes(ws)
+    Y = (g.random((B, L)) < 0.2)
+    rp = np.zeros(B + 1, np.int32); rp[1:] = np.cumsum(Y.sum(1))
+    ids = np.concatenate([np.nonzero(Y[b])[0] for b in range(B)]).astype(np.int32)
+    lr = 2.0**-10
+    Wn, dX, _, Z, G = orc.step(0, W, X, rp, ids, lr, 0, 0, want_z=True, want_g=True)
+    z = xs @ ws.T
+    assert np.all(np.abs(z) >= 116) and np.array_equal(Z, z.astype(np.float32))
+    gexp = (z > 0).astype(np.float64) - Y
+    assert np.array_equal(_bf16_val(G), gexp)
+    assert np.array_equal(dX, (gexp @ ws).astype(np.float32))
+    t = ws - lr * (gexp.T @ xs)                    # exact dyadic rationals
+    new = _bf16_val(Wn)
+    tab = _bf16_val(np.arange(0, 0x7F80, dtype=np.uint16))
+    i = np.searchsorted(tab, np.abs(t), side="right") - 1
+    assert np.all((np.abs(new) == tab[i]) | (np.abs(new) == tab[i + 1]))
+    exact = tab[i] == np.abs(t)
+    assert np.array_equal(new[exact], t[exact])
+
+
+# ---------------------------------------------------------------------------------------------- #
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_topk_matches_lexsort(orc, wfmt):
+    wl, W, bt = _small_case(wfmt, B=13, D=64, L=500)
+    W = W.copy()
+    W[100] = W[7]; W[499] = W[7]; W[250] = W[3]   # exact ties: the smaller label must win
+    k = 6
+    idx, score = orc.topk(wfmt, W, bt.X, k)
+    w = _wval(wfmt, W); x = _bf16_val(bt.X)
+    xt = x if wfmt == wk.W_BF16 else _e4m3_val(
+        torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    S = (xt @ w.T).astype(np.float32)
+    for n in range(S.shape[0]):
+        order = np.lexsort((np.arange(wl.L), -S[n].astype(np.float64)))[:k]
+        assert np.array_equal(idx[n], order)
+        assert np.array_equal(score[n], S[n, order])
+    idx1, _ = orc.topk(wfmt, W, bt.X, 1)
+    assert np.array_equal(idx1[:, 0], np.argmax(S, axis=1))
+
+
+def test_topk_nan_ranks_last(orc):
+    wl, W, bt = _small_case(wk.W_BF16, B=4, D=64, L=50)
+    W = W.copy(); W[:, 0] = 0x7FC0                # every score NaN ...
+    W[10] = wk.to_bf16_codes(np.full(64, 0.01))   # ... except rows 10 and 20
+    W[20] = wk.to_bf16_codes(np.full(64, -0.01))
+    idx, score = orc.topk(0, W, bt.X, 4)
+    assert np.all(np.sort(idx[:, :2], axis=1) == [10, 20])
+    assert np.all(np.isnan(score[:, 2:])) and np.array_equal(idx[:, 2:], np.tile([0, 1], (4, 1)))
