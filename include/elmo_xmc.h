@@ -1,0 +1,138 @@
+/*
+ * elmo_xmc — MI355X (gfx950) library for the chunked, fused, low-precision training step of an
+ * extreme-multilabel (XMC) linear classifier head, and its top-k scoring pass.
+ *
+ * Method: "ELMO: Efficiency via Low-precision and Peak Memory Optimization in Large Output Spaces"
+ * (atlas.scime.ai summary, sections "Approach" and "Surprising findings"; arXiv 2510.11168,
+ * abstract). The classifier weights are stored in pure BF16 or FP8 E4M3 with no FP32 master copy
+ * and no tensor scaling; the weight gradient is fused into a momentum-free SGD update that writes
+ * the weights back in place with stochastic rounding; the label dimension is processed in chunks
+ * so that transient memory is bounded by one chunk.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (allocated by the caller on the current HIP device) unless noted.
+ *     The library never allocates or frees device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is enqueued asynchronously on
+ *     it; the call returns before the device finishes. Device-side faults surface at the caller's
+ *     next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a negative elmo_status is
+ *     returned and nothing runs. After each launch the HIP error state is checked (ELMO_EHIP).
+ *   - Pointers must be 16-byte aligned. Buffers must not alias each other.
+ *   - No C++ exception crosses this interface. Nothing is printed.
+ */
+#ifndef ELMO_XMC_H
+#define ELMO_XMC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ELMO_OK = 0,
+  ELMO_EINVAL = -1,        /* null pointer, misalignment, bad scalar argument            */
+  ELMO_ESHAPE = -2,        /* B, D, L, N, k or chunk outside the supported ranges        */
+  ELMO_EDTYPE = -3,        /* unknown weight format                                      */
+  ELMO_EWORKSPACE = -4,    /* workspace missing or smaller than the *_workspace_bytes   */
+  ELMO_EHIP = -5,          /* a HIP runtime call or kernel launch failed                 */
+  ELMO_EUNSUPPORTED = -6   /* valid request that this build does not implement           */
+} elmo_status;
+
+/* Weight storage formats. BF16: uint16 codes. E4M3: OCP FP8 E4M3FN codes (uint8; max 448, no
+ * infinity, 0x7F/0xFF NaN) — the "E4M3" of the summary page's "Surprising findings". */
+enum { ELMO_W_BF16 = 0, ELMO_W_E4M3 = 1 };
+
+/* Supported shapes: 1 <= B <= 256; 64 <= D <= 1024 with D % 64 == 0; 1 <= L < 2^31;
+ * chunk >= 1 (rounded down internally to a multiple of 128 labels, at least 128). */
+#define ELMO_MAX_B 256
+#define ELMO_MAX_D 1024
+#define ELMO_MAX_TOPK 32
+
+int elmo_abi_version(void);
+const char* elmo_status_str(int status);
+
+/*
+ * One training step of the classifier head (summary page, "Approach": pure low-precision
+ * classifier, stochastic rounding, no momentum, gradient computation fused with the SGD update,
+ * label dimension chunked; arXiv abstract: "gradient fusion and chunking").
+ *
+ *   W        [L, D] row-major weight codes (BF16 or E4M3 per `wdtype`), updated IN PLACE.
+ *   X        [B, D] row-major BF16 codes (encoder features). Read only.
+ *   row_ptr  [B+1] int32, ids [nnz] int32: the positive labels of each sample in CSR form; set
+ *            semantics (duplicates collapse, any order, empty rows allowed). Ids outside [0, L)
+ *            are skipped and raise bit ELMO_FLAG_LABEL_RANGE in the workspace flags word;
+ *            row_ptr must be non-decreasing with row_ptr[0] = 0 and row_ptr[B] = nnz (violations
+ *            raise ELMO_FLAG_ROW_PTR). `nnz` is the host-side count.
+ *   lr       SGD learning rate (cast to FP32 by the caller's value).
+ *   seed, step  key the counter-based RNG of the stochastic rounding: Philox4x32-10 with key =
+ *            seed, counter = ((j*D + k) >> 3, step). Calling with the same (seed, step) on the same
+ *            inputs reproduces the same W bit for bit, whatever the chunk size.
+ *   chunk    labels per chunk: bounds the transient G buffer to B_pad * chunk * 2 bytes.
+ *   dX       [B, D] FP32, OVERWRITTEN with sum_j G[b, j] * W_old[j, :] (pre-update weights).
+ *   loss_sum nullable; if given, receives the FP32 value of the summed BCE over all (b, j).
+ *   workspace, workspace_bytes: at least elmo_xmc_step_workspace_bytes(...) bytes of device
+ *            memory, used for label buckets, padded/cast copies of X, one chunk of G and the dX
+ *            partial sums. Its first 4 bytes are the flags word after the step completes.
+ * Per element: z = X~ . w_j (X~ = X, or E4M3-RNE(X) for E4M3 weights), g = BF16-RNE(sigmoid(z) - y),
+ * dX += g W_old, dW = g^T X, t = fmaf(-lr, dW, w), W = SR(t).
+ */
+#define ELMO_FLAG_LABEL_RANGE 1u
+#define ELMO_FLAG_ROW_PTR 2u
+size_t elmo_xmc_step_workspace_bytes(int B, int D, int64_t L, int64_t chunk, int wdtype,
+                                     int64_t max_nnz);
+int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B,
+                  const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr, uint64_t seed,
+                  uint64_t step, int64_t chunk, float* dX, float* loss_sum, void* workspace,
+                  size_t workspace_bytes, void* stream);
+/* Copies the flags word of a step's workspace to *flags (HOST pointer); synchronises `stream`. */
+int elmo_xmc_step_flags(const void* workspace, uint32_t* flags, void* stream);
+
+/*
+ * Top-k scoring for precision@k (summary page, "Experimental setup": P@1, P@3, P@5).
+ *   W [L, D] codes, X [N, D] BF16 codes (E4M3 weights score against E4M3-RNE(X), as in training).
+ *   out_idx [N, k] int32: labels ranked by (FP32 logit desc, label asc), NaN logits last.
+ *   out_score [N, k] FP32 logits, nullable.  1 <= k <= min(ELMO_MAX_TOPK, L), N >= 1.
+ */
+size_t elmo_xmc_topk_workspace_bytes(int N, int D, int64_t L, int k, int wdtype);
+int elmo_xmc_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, int k,
+                  int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Diagnostic: FP32 logits Z [B, l1 - l0] (row-major) of labels [l0, l1) computed by the same
+ * forward kernel the step uses. Workspace as for elmo_xmc_step with chunk = l1 - l0, nnz = 0.
+ */
+int elmo_xmc_logits(const void* W, int wdtype, int64_t L, int D, int64_t l0, int64_t l1,
+                    const void* X, int B, float* Z, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Diagnostic: the step's forward kernel over labels [l0, l1) with the step's label handling,
+ * writing the FP32 logits Z and/or the BF16 gradient codes G = BF16(sigmoid(Z) - Y) that a step
+ * with the same inputs uses (each [B, l1 - l0] row-major, nullable but not both). Weights are not
+ * touched. Labels as for elmo_xmc_step (row_ptr/ids may be NULL when nnz = 0). Workspace as for
+ * elmo_xmc_step with chunk = l1 - l0 and max_nnz = nnz.
+ */
+int elmo_xmc_forward(const void* W, int wdtype, int64_t L, int D, const void* X, int B,
+                     const int32_t* row_ptr, const int32_t* ids, int64_t nnz, int64_t l0, int64_t l1,
+                     float* Z, uint16_t* G, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: the device codec, stochastic rounding and RNG applied elementwise to n elements.
+ *   op 0  BF16 RNE encode:      in0 float[n]            -> out uint16[n]
+ *   op 1  E4M3 RNE-sat encode:  in0 float[n]            -> out uint8[n]
+ *   op 2  E4M3 decode:          in0 uint8[n]            -> out float[n]
+ *   op 3  SR to BF16:           in0 float[n], in1 uint32 r[n] -> out uint16[n]
+ *   op 4  SR to E4M3:           in0 float[n], in1 uint32 r[n] -> out uint8[n]
+ *   op 5  RNG 16-bit draws:     r16(seed, step, idx0 + i), idx0 = *(const uint64_t*)in0 (HOST) -> out uint32[n]
+ *   op 6  gradient code:        in0 float z[n], in1 uint32 y[n] -> out uint16[n] (BF16(sigmoid(z) - y))
+ */
+int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n,
+                        uint64_t seed, uint64_t step, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ELMO_XMC_H */

@@ -63,6 +63,8 @@ def lib():
         L.orc_r16_array.argtypes = [u64, u64, u64, P, i64]; L.orc_r16_array.restype = None
         L.orc_step.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
                                ctypes.c_float, u64, u64, P, P, P, P, ctypes.c_int]
+        L.orc_update_from_g.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_float,
+                                        u64, u64, P, ctypes.c_int]
         L.orc_logits.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P,
                                  ctypes.c_int, P, ctypes.c_int]
         L.orc_update_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
@@ -72,7 +74,7 @@ def lib():
         L.orc_grad_exact.argtypes = [i64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P]
         L.orc_topk.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                P, P, ctypes.c_int]
-        for name in ("orc_step", "orc_logits", "orc_update_rows", "orc_dx_rows", "orc_grad_exact",
+        for name in ("orc_step", "orc_update_from_g", "orc_logits", "orc_update_rows", "orc_dx_rows", "orc_grad_exact",
                      "orc_topk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -162,6 +164,16 @@ def step(wfmt, W, X, row_ptr, ids, lr, seed, step_, want_z=False, want_g=False, 
                         _p(Z), _p(G), nthreads)
     _chk(rc, "step")
     return Wn, dX, (loss.value if want_loss else None), Z, G
+
+
+def update_from_g(wfmt, W, X, G, lr, seed, step_, nthreads=0):
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    G = _c(G, np.uint16)
+    assert G.shape == (B, L)
+    out = np.empty_like(W)
+    _chk(lib().orc_update_from_g(wfmt, _p(W), L, D, _p(X), B, _p(G), float(lr), seed, step_, _p(out), nthreads),
+         "update_from_g")
+    return out
 
 
 def logits(wfmt, W, X, js, nthreads=0):

@@ -347,6 +347,27 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
   return ORC_OK;
 }
 
+int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
+                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, int nthreads) {
+  int rc = check_common(wfmt, W, L, D, X, B);
+  if (rc) return rc;
+  if (!G || !Wout) return ORC_EINVAL;
+  set_threads(nthreads);
+  double* xb = backward_x(X, B, D);
+  if (!xb) return ORC_ENOMEM;
+  #pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < L; j++) {
+    for (int k = 0; k < D; k++) {
+      double s = 0.0;
+      for (int b = 0; b < B; b++) s += orc_bf16_value(G[(int64_t)b * L + j]) * xb[(int64_t)b * D + k];
+      int64_t i = j * (int64_t)D + k;
+      store_update(wfmt, Wout, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i);
+    }
+  }
+  free(xb);
+  return ORC_OK;
+}
+
 int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                const int64_t* js, int nj, float* Z, int nthreads) {
   int rc = check_common(wfmt, W, L, D, X, B);

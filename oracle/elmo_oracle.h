@@ -61,6 +61,12 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
              const int32_t* row_ptr, const int32_t* ids, float lr, uint64_t seed, uint64_t step,
              float* dX, double* loss, float* Z, uint16_t* G, int nthreads);
 
+/* The weight half of the step given the gradient codes G ([B][L] BF16): dW = FP32(G^T X) with the
+ * BF16 X, t = fmaf(-lr, dW, w), W_out = SR(t). W is not modified; Wout receives [L][D] codes.
+ * orc_step's weights equal this function applied to orc_step's own G. */
+int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
+                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, int nthreads);
+
 /* Sampled outputs of the same step for large shapes, without modifying W:
  *   orc_logits:      Z[b][i] for labels js[i] (all b)                      -> Z [B][nj]
  *   orc_update_rows: the updated codes of weight rows js[i]                 -> Wrows [nj][D]

@@ -1,0 +1,47 @@
+// CDNA4 (gfx950) matrix-core and LDS helpers.
+//
+// Operand layouts (checked on the device with exact-integer inputs):
+//   v_mfma_f32_32x32x16_bf16  A: lane l holds row m = l%32, k = 8*(l/32) + e, e = 0..7
+//                             B: lane l holds col n = l%32, k = 8*(l/32) + e
+//                             C: lane l, register i holds col n = l%32, row m = 8*(i/4) + 4*(l/32) + i%4
+//   v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, no block scaling): as above with k = 32*(l/32) + e,
+//                             e = 0..31 bytes; it reads 0x7E as 448 and honours subnormals.
+//   ds_read_b64_tr_b16        a group of 16 lanes reads a 4 x 16 block of 16-bit elements whose
+//                             row r is supplied (4 consecutive elements each) by lanes 4r..4r+3;
+//                             lane i of the group receives column i (rows 0..3).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace elmo {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ f32x16_t mfma_bf16(s16x8_t a, s16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
+  // format 0 = E4M3 for both operands; zero scale operands select the unscaled instruction
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// p must point into __shared__ memory and be 8-byte aligned
+__device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<uint16_t*>(p)));
+}
+
+__device__ __forceinline__ s16x8_t join(s16x4_t lo, s16x4_t hi) {
+  return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+}  // namespace elmo

@@ -1,0 +1,123 @@
+// Device numerics for the XMC head step on gfx950: BF16 and OCP-E4M3 codecs, stochastic rounding,
+// the counter-based RNG that drives it, and the sigmoid-BCE gradient.
+//
+// Method context: "ELMO: Efficiency via Low-precision and Peak Memory Optimization in Large Output
+// Spaces" (summary page, "Approach" and "Surprising findings"): pure BF16/FP8-E4M3 classifier
+// weights without master weights or tensor scaling, updated with stochastic rounding. The pages do
+// not give the rounding mechanism or RNG; the rules implemented here are:
+//   * RNE for X -> E4M3 and for G -> BF16; E4M3 encode saturates to +-448 (no infinity in E4M3FN);
+//   * SR of an FP32 value t with 16 random bits r: keep the truncated magnitude, add one unit in
+//     the last place iff (dropped fraction, as a 16-bit fixed-point number q) + r >= 2^16;
+//   * r comes from Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3",
+//     SC'11) with key = seed and counter = (element index >> 3, step); element idx = j*D + k uses
+//     16-bit half (idx & 1) of output word (idx >> 1) & 3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace elmo {
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ---- BF16 -------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return u2f(h << 16); }
+
+// round-to-nearest-even: add 0x7FFF plus the lowest kept bit, then truncate; NaN stays quiet NaN
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- OCP E4M3 (E4M3FN) --------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;               // m * 2^-9
+  else if (e == 15 && m == 7) v = u2f(0x7fc00000u);       // NaN
+  else v = u2f(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// E4M3 values have at most 4 significant bits and exponents inside BF16's range: exact
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
+
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
+  uint32_t u = f2u(x);
+  uint32_t s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return s | 0x7fu;                  // NaN
+  if (a >= 0x43e00000u) return s | 0x7eu;                 // |x| >= 448 (and inf): saturate
+  if (a < 0x3c800000u) {                                  // below 2^-6: multiples of 2^-9
+    float v = __builtin_rintf(u2f(a) * 512.0f);           // exact scaling, then round-half-even
+    return s | (uint32_t)v;                               // 8 -> code 0x08 = 2^-6, as wanted
+  }
+  uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+  return s | (r - 960u);                                  // rebias exponent 127 -> 7
+}
+
+// ---- stochastic rounding ------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t sr_bf16(float t, uint32_t r16) {
+  uint32_t u = f2u(t);
+  uint32_t s = u & 0x80000000u, a = u & 0x7fffffffu;
+  if (a >= 0x7f800000u) return (a > 0x7f800000u) ? ((u >> 16) | 0x40u) : (u >> 16);
+  return (s | (a + r16)) >> 16;   // carry from the dropped half rounds the magnitude up
+}
+
+__device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) {
+  uint32_t u = f2u(t);
+  uint32_t s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return s | 0x7fu;
+  if (a >= 0x43e00000u) return s | 0x7eu;
+  if (a >= 0x3c800000u) {
+    uint32_t q = (a >> 4) & 0xffffu;                      // top 16 of the 20 dropped bits
+    return s | ((a >> 20) - 960u + ((q + r16) >> 16));
+  }
+  float v = u2f(a) * 512.0f;                              // units of the subnormal spacing 2^-9
+  float k = __builtin_floorf(v);
+  uint32_t q = (uint32_t)((v - k) * 65536.0f);           // exact fraction, truncated
+  return s | ((uint32_t)k + ((q + r16) >> 16));
+}
+
+// ---- Philox4x32-10 ------------------------------------------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    u32x4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+  }
+  return c;
+}
+
+// the 8 random 16-bit values of element block g = idx >> 3, packed two per word
+__device__ __forceinline__ u32x4 rng_block(uint64_t seed, uint64_t step, uint64_t g) {
+  u32x4 c{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = idx & 7
+  uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// ---- sigmoid-BCE gradient -----------------------------------------------------------------------
+// g = sigmoid(z) - y in the cancellation-free forms 1/(1+e^-z) (y = 0) and -1/(1+e^z) (y = 1)
+__device__ __forceinline__ float bce_grad(float z, bool y) {
+  return y ? -1.0f / (1.0f + expf(z)) : 1.0f / (1.0f + expf(-z));
+}
+
+// summed-loss term: max(z, 0) - y z + log1p(e^-|z|)
+__device__ __forceinline__ float bce_loss(float z, bool y) {
+  return fmaxf(z, 0.0f) - (y ? z : 0.0f) + log1pf(expf(-fabsf(z)));
+}
+
+}  // namespace elmo

@@ -1,0 +1,544 @@
+// The chunked, fused XMC classifier-head training step on gfx950.
+//
+// Method: "ELMO: Efficiency via Low-precision and Peak Memory Optimization in Large Output Spaces"
+// (summary page, "Approach": pure BF16/FP8 classifier with stochastic rounding, no momentum, the
+// classifier gradient fused with the SGD update, the label dimension chunked to cut transient
+// memory; arXiv abstract: "gradient fusion and chunking").
+//
+// Per label chunk [c0, c0 + clen) two kernels run on the caller's stream:
+//   k_fwd_g       label tiles of 128 x all B: Z = X~ W_c^T on the matrix cores (BF16, or E4M3 in
+//                 FP8 mode), then G = BF16(sigmoid(Z) - Y) in the epilogue straight from the
+//                 accumulators; writes the chunk's G (the only chunk-sized transient).
+//   k_bwd_update  (d-slice, label range) work-groups: one LDS-staged G tile feeds both backward
+//                 contractions — dX^T += W_old^T G^T (FP32 accumulators that live across the whole
+//                 label range) and dW^T = X^T G — and dW goes straight into t = fmaf(-lr, dW, w)
+//                 and the stochastic rounding; the updated weights are written back in place with
+//                 coalesced 16-byte stores. dW is never stored outside the work-group.
+// Label handling, X preparation and the final dX reduction are small kernels around them.
+#include "step_kernels.hpp"
+
+#include "fwd_tile.hpp"
+#include "mfma.hpp"
+#include "numerics.hpp"
+
+namespace elmo {
+
+// ------------------------------------------------------------------------------------------------
+// small kernels
+// ------------------------------------------------------------------------------------------------
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// one block per sample: validate its CSR row and count its labels per 128-label tile
+__global__ void k_label_count(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
+                              int B, int64_t nnz, int64_t L, uint32_t* __restrict__ tile_cnt,
+                              uint32_t* __restrict__ flags) {
+  const int b = blockIdx.x;
+  int64_t r0 = row_ptr[b], r1 = row_ptr[b + 1];
+  if (threadIdx.x == 0) {
+    bool bad = r0 < 0 || r1 < r0 || r1 > nnz || (b == 0 && r0 != 0) || (b == B - 1 && r1 != nnz);
+    if (bad) atomicOr(flags, ELMO_FLAG_ROW_PTR_);
+  }
+  r0 = r0 < 0 ? 0 : (r0 > nnz ? nnz : r0);
+  r1 = r1 < r0 ? r0 : (r1 > nnz ? nnz : r1);
+  for (int64_t i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= L) { atomicOr(flags, ELMO_FLAG_LABEL_RANGE_); continue; }
+    atomicAdd(&tile_cnt[id / TJ1], 1u);
+  }
+}
+
+// exclusive scan of the per-tile counts (one block of 1024 threads); cnt becomes the scatter cursor
+__global__ __launch_bounds__(1024) void k_label_scan(uint32_t* __restrict__ cnt, uint32_t* __restrict__ off,
+                                                     int64_t ntiles) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t seg = (ntiles + 1023) / 1024;
+  const int64_t a = tid * seg, e = (a + seg < ntiles) ? a + seg : ntiles;
+  uint32_t s = 0;
+  for (int64_t i = a; i < e; ++i) s += cnt[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {      // inclusive Hillis-Steele scan
+    uint32_t v = tid >= o ? part[tid - o] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t run = tid ? part[tid - 1] : 0u;
+  for (int64_t i = a; i < e; ++i) {
+    uint32_t c = cnt[i];
+    off[i] = run;
+    cnt[i] = run;
+    run += c;
+  }
+  if (tid == 1023) off[ntiles] = part[1023];
+}
+
+// bucket capacity is nnz: with a malformed row_ptr (overlapping rows) entries beyond it are dropped
+__global__ void k_label_scatter(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
+                                int64_t nnz, int64_t L, uint32_t* __restrict__ cursor,
+                                uint32_t* __restrict__ bucket) {
+  const int b = blockIdx.x;
+  int64_t r0 = row_ptr[b], r1 = row_ptr[b + 1];
+  r0 = r0 < 0 ? 0 : (r0 > nnz ? nnz : r0);
+  r1 = r1 < r0 ? r0 : (r1 > nnz ? nnz : r1);
+  for (int64_t i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= L) continue;
+    uint32_t pos = atomicAdd(&cursor[id / TJ1], 1u);
+    if (pos < (uint64_t)nnz) bucket[pos] = ((uint32_t)b << 16) | (uint32_t)(id % TJ1);
+  }
+}
+
+// zero-padded BF16 copy of X ([MB][D]) and, in FP8 mode, its E4M3-RNE cast for the forward MFMA
+__global__ void k_prep_x(const uint16_t* __restrict__ X, int B, int D, int MB, uint16_t* __restrict__ Xb,
+                         uint8_t* __restrict__ Xq) {
+  const int64_t n = (int64_t)MB * D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t v = (i / D) < B ? X[i] : 0u;
+    Xb[i] = (uint16_t)v;
+    if (Xq) Xq[i] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(v));
+  }
+}
+
+// dX[b][d] = sum over label ranges r (fixed order) of the FP32 partials
+__global__ void k_dx_reduce(const float* __restrict__ part, int NR, int MB, int D, int B, float* __restrict__ dX) {
+  const int64_t n = (int64_t)B * D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int r = 0; r < NR; ++r) s += part[(int64_t)r * MB * D + i];
+    dX[i] = s;
+  }
+}
+
+// summed loss: per-tile FP32 partials added in binary64 in a fixed order
+__global__ __launch_bounds__(256) void k_loss_reduce(const float* __restrict__ lp, int64_t n, float* __restrict__ out) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += (double)lp[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = (float)red[0];
+}
+
+// ------------------------------------------------------------------------------------------------
+// forward + gradient: Z = X~ W_c^T, G = BF16(sigmoid(Z) - Y)
+// ------------------------------------------------------------------------------------------------
+template <int MB, int WF, bool LOSS, bool ZOUT>
+__global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
+                                               int D, int64_t c0, int clen,
+                                               const uint32_t* __restrict__ tile_off,
+                                               const uint32_t* __restrict__ bucket, int64_t bucket_cap,
+                                               int B, uint16_t* __restrict__ G, int64_t gpitch,
+                                               float* __restrict__ loss_part,
+                                               float* __restrict__ Z, uint16_t* __restrict__ Gout,
+                                               int64_t zpitch, int64_t zoff) {
+  constexpr int WB = MB >= 64 ? 2 : 1, WJ = 4 / WB;
+  constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
+  constexpr int MI = RW / 32, NI = CW / 32;
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  constexpr int GP = TJ1 + 8;                  // G staging pitch in elements
+  static_assert(MB * GP * 2 <= fwd_smem_bytes(MB), "G staging must fit in the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB)];
+  __shared__ uint32_t ybits[MB * (TJ1 / 32)];
+  __shared__ float lred[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wb = wave / WJ, wj = wave % WJ;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tile = blockIdx.x;
+  const int64_t tg = c0 / TJ1 + tile;          // global 128-label tile index
+  const int jbase = tile * TJ1;                // first label of the tile, relative to c0
+  const int64_t rowbytes = (int64_t)D * ESZ;
+
+  for (int i = tid; i < MB * (TJ1 / 32); i += 256) ybits[i] = 0u;
+  __syncthreads();
+  {
+    const uint64_t e0 = tile_off[tg];
+    const uint64_t e1 = tile_off[tg + 1] < (uint64_t)bucket_cap ? tile_off[tg + 1] : (uint64_t)bucket_cap;
+    for (uint64_t e = e0 + tid; e < e1; e += 256) {
+      uint32_t v = bucket[e];
+      uint32_t b = v >> 16, jl = v & (TJ1 - 1);
+      if (b < (uint32_t)MB) atomicOr(&ybits[b * (TJ1 / 32) + (jl >> 5)], 1u << (jl & 31));
+    }
+  }
+
+  f32x16_t acc[MI][NI];
+  fwd_tile<MB, WF, RW, CW>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj);
+
+  // epilogue: gradient straight from the accumulators, staged in LDS for coalesced stores
+  uint16_t* Gs = (uint16_t*)smem;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        const int jl = wj * CW + ni * 32 + l32;
+        const float z = acc[mi][ni][i];
+        const bool valid = (b < B) && (jbase + jl < clen);
+        const bool y = (ybits[b * (TJ1 / 32) + (jl >> 5)] >> (jl & 31)) & 1u;
+        const uint16_t code = valid ? (uint16_t)f32_to_bf16_rne(bce_grad(z, y)) : (uint16_t)0;
+        if constexpr (LOSS) if (valid) lsum += bce_loss(z, y);
+        if constexpr (ZOUT) {
+          const int64_t lab = c0 + jbase + jl;
+          if (valid && lab >= zoff) {
+            if (Z) Z[(int64_t)b * zpitch + (lab - zoff)] = z;
+            if (Gout) Gout[(int64_t)b * zpitch + (lab - zoff)] = code;
+          }
+        } else {
+          Gs[b * GP + jl] = code;
+        }
+      }
+  if constexpr (ZOUT) return;
+  __syncthreads();
+  for (int ci = tid; ci < MB * (TJ1 / 8); ci += 256) {
+    const int row = ci / (TJ1 / 8), part = ci % (TJ1 / 8);
+    *(i32x4_t*)(G + row * gpitch + jbase + part * 8) = *(const i32x4_t*)(Gs + row * GP + part * 8);
+  }
+  if constexpr (LOSS) {
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) lred[wave] = lsum;
+    __syncthreads();
+    if (tid == 0) loss_part[tg] = ((lred[0] + lred[1]) + lred[2]) + lred[3];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// backward + fused update over one d-slice and one label range of the chunk
+// ------------------------------------------------------------------------------------------------
+template <int MB, int WF, int DS>
+__global__ __launch_bounds__(256) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
+                                                    const uint16_t* __restrict__ Xb,
+                                                    const uint16_t* __restrict__ G, int64_t gpitch,
+                                                    float* __restrict__ part, int NR, int NS, float lr,
+                                                    uint64_t seed, uint64_t step) {
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  constexpr int NWM = DS / 32;                 // waves that own a 32-wide d block
+  constexpr int NB = MB / 32;
+  constexpr int GPE = TJ2 + 8;                 // G tile pitch (elements)
+  constexpr int WPE = DS + 8;                  // W tile pitch (BF16 elements)
+  constexpr int DWP = DS + 4;                  // dW tile pitch (floats)
+  constexpr int GPT = MB * (TJ2 / 8) / 256;    // 16-byte G chunks per thread
+  constexpr int WCPR = DS * ESZ / 16;          // 16-byte W chunks per tile row
+  constexpr int WPT = TJ2 * WCPR / 256;        // W chunks per thread
+  constexpr int EPC = 16 / ESZ;                // weights per chunk
+  static_assert(GPT >= 1 && WPT >= 1, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[MB * GPE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[TJ2 * WPE];
+  __shared__ __attribute__((aligned(16))) float dWs[TJ2 * DWP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5, q = lane >> 4, li = lane & 15;
+  // work-groups of one label range share its G tiles: keep them on one XCD (dispatch is round-robin)
+  const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
+  const int r = (kq / NS) * 8 + xcd, s = kq % NS;
+  if (r >= NR) return;
+  const int nt = (clen + TJ2 - 1) / TJ2;
+  const int t0 = (int)((int64_t)nt * r / NR), t1 = (int)((int64_t)nt * (r + 1) / NR);
+  const int dsl = s * DS;
+  const int64_t rowbytes = (int64_t)D * ESZ;
+
+  s16x8_t xT[MB / 16];                         // stationary X^T fragments: lane (d, 8 samples)
+  if (wave < NWM) {
+    const int d = dsl + wave * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < MB / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xT[kk][e] = (short)Xb[(kk * 16 + hi * 8 + e) * D + d];
+  }
+  f32x16_t accX[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) accX[nb] = f32x16_t{};
+
+  i32x4_t gst[GPT], wst[WPT], wcur[WPT];
+  auto load = [&](int t) {
+    const int jb = t * TJ2;
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+      const int ci = tid + c * 256, row = ci >> 3, p = ci & 7;
+      gst[c] = *(const i32x4_t*)(G + row * gpitch + jb + p * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
+      i32x4_t v = {0, 0, 0, 0};
+      if (jb + jr < clen) v = *(const i32x4_t*)(W + (c0 + jb + jr) * rowbytes + (int64_t)dsl * ESZ + p * 16);
+      wst[c] = v;
+    }
+  };
+
+  if (t0 < t1) load(t0);
+  for (int t = t0; t < t1; ++t) {
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+      const int ci = tid + c * 256, row = ci >> 3, p = ci & 7;
+      *(i32x4_t*)(Gs + row * GPE + p * 8) = gst[c];
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
+      wcur[c] = wst[c];
+      if constexpr (WF == W_BF16_) {
+        *(i32x4_t*)(Ws + jr * WPE + p * 8) = wst[c];
+      } else {
+        i32x4_t lo, hi4;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = (uint32_t)wst[c][w];
+          const uint32_t p0 = e4m3_to_bf16(v & 0xff) | (e4m3_to_bf16((v >> 8) & 0xff) << 16);
+          const uint32_t p1 = e4m3_to_bf16((v >> 16) & 0xff) | (e4m3_to_bf16(v >> 24) << 16);
+          if (w < 2) { lo[2 * w] = (int)p0; lo[2 * w + 1] = (int)p1; }
+          else { hi4[2 * (w - 2)] = (int)p0; hi4[2 * (w - 2) + 1] = (int)p1; }
+        }
+        *(i32x4_t*)(Ws + jr * WPE + p * 16) = lo;
+        *(i32x4_t*)(Ws + jr * WPE + p * 16 + 8) = hi4;
+      }
+    }
+    __syncthreads();
+    if (t + 1 < t1) load(t + 1);               // next tile's loads overlap this tile's math
+
+    if (wave < NWM) {
+      // dX^T[d][b] += sum_j W^T[d][j] G[b][j]        (M = d, N = b, K = j)
+#pragma unroll
+      for (int kk = 0; kk < TJ2 / 16; ++kk) {
+        const uint16_t* pa = Ws + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * WPE + wave * 32 + 16 * (q & 1) + 4 * (li & 3);
+        const s16x8_t a = join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const s16x8_t bv = *(const s16x8_t*)(Gs + (nb * 32 + l32) * GPE + kk * 16 + hi * 8);
+          accX[nb] = mfma_bf16(a, bv, accX[nb]);
+        }
+      }
+      // dW^T[d][j] = sum_b X^T[d][b] G[b][j]         (M = d, N = j, K = b)
+      f32x16_t accW[TJ2 / 32];
+#pragma unroll
+      for (int nj = 0; nj < TJ2 / 32; ++nj) accW[nj] = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < MB / 16; ++kk)
+#pragma unroll
+        for (int nj = 0; nj < TJ2 / 32; ++nj) {
+          const uint16_t* pb = Gs + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * GPE + nj * 32 + 16 * (q & 1) + 4 * (li & 3);
+          accW[nj] = mfma_bf16(xT[kk], join(lds_read_tr16(pb), lds_read_tr16(pb + 4 * GPE)), accW[nj]);
+        }
+#pragma unroll
+      for (int nj = 0; nj < TJ2 / 32; ++nj)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          f32x4_t v = {accW[nj][4 * ig], accW[nj][4 * ig + 1], accW[nj][4 * ig + 2], accW[nj][4 * ig + 3]};
+          *(f32x4_t*)(dWs + (nj * 32 + l32) * DWP + wave * 32 + 8 * ig + 4 * hi) = v;
+        }
+    }
+    __syncthreads();
+
+    // fused SGD + stochastic rounding, in place, 16 bytes per thread-chunk
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
+      const int jb = t * TJ2;
+      if (jb + jr >= clen) continue;
+      const int64_t jg = c0 + jb + jr;
+      const int d0 = p * EPC;
+      const float* dw = dWs + jr * DWP + d0;
+      const uint64_t idx0 = (uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + d0);
+      i32x4_t out;
+      if constexpr (WF == W_BF16_) {
+        const u32x4 rnd = rng_block(seed, step, idx0 >> 3);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = (uint32_t)wcur[c][w];
+          const float t0f = fmaf(-lr, dw[2 * w], bf16_to_f32(v & 0xffffu));
+          const float t1f = fmaf(-lr, dw[2 * w + 1], bf16_to_f32(v >> 16));
+          out[w] = (int)(sr_bf16(t0f, rng_pick(rnd, 2 * w)) | (sr_bf16(t1f, rng_pick(rnd, 2 * w + 1)) << 16));
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 rnd = rng_block(seed, step, (idx0 >> 3) + h);
+#pragma unroll
+          for (int w = 2 * h; w < 2 * h + 2; ++w) {
+            const uint32_t v = (uint32_t)wcur[c][w];
+            uint32_t o = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tf = fmaf(-lr, dw[4 * w + e], e4m3_to_f32((v >> (8 * e)) & 0xffu));
+              o |= sr_e4m3(tf, rng_pick(rnd, 4 * (w - 2 * h) + e)) << (8 * e);
+            }
+            out[w] = (int)o;
+          }
+        }
+      }
+      *(i32x4_t*)(W + jg * rowbytes + (int64_t)(dsl + d0) * ESZ) = out;
+    }
+  }
+
+  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic)
+  if (wave < NWM) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int b = nb * 32 + l32;
+        const int d = dsl + wave * 32 + 8 * ig + 4 * hi;
+        f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
+        f32x4_t v = *pp;
+        v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
+        v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
+        *pp = v;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host side: workspace layout, chunk scheduler, launches
+// ------------------------------------------------------------------------------------------------
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int padded_batch(int B) { return B <= 32 ? 32 : B <= 64 ? 64 : B <= 128 ? 128 : 256; }
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64_t max_nnz) {
+  StepLayout s{};
+  s.MB = padded_batch(B);
+  s.DS = (D % 128 == 0) ? 128 : 64;
+  s.NS = D / s.DS;
+  int64_t Lr = (L + TJ1 - 1) / TJ1 * TJ1;
+  int64_t c = chunk - chunk % TJ1;
+  if (c < TJ1) c = TJ1;
+  if (c > Lr) c = Lr;
+  s.Cc = c;
+  s.ntiles = (L + TJ1 - 1) / TJ1;
+  int64_t nt2 = (c + TJ2 - 1) / TJ2;
+  int cap = device_cus() / s.NS;
+  if (cap < 1) cap = 1;
+  s.NR = (int)(nt2 < cap ? nt2 : cap);
+  size_t off = 0;
+  const size_t A = 256;
+  s.flags = off;    off = align_up(off + 64, A);
+  s.tile_cnt = off; off = align_up(off + 4 * (size_t)(s.ntiles + 1), A);
+  s.tile_off = off; off = align_up(off + 4 * (size_t)(s.ntiles + 1), A);
+  s.bucket = off;   off = align_up(off + 4 * (size_t)(max_nnz > 0 ? max_nnz : 1), A);
+  s.xb = off;       off = align_up(off + 2 * (size_t)s.MB * D, A);
+  s.xq = off;       off = align_up(off + (wdtype == W_E4M3_ ? (size_t)s.MB * D : 0), A);
+  s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
+  s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
+  s.loss = off;     off = align_up(off + 4 * (size_t)s.ntiles, A);
+  s.total = off;
+  return s;
+}
+
+#define LAUNCH_CHECK() do { if (hipGetLastError() != hipSuccess) return ELMO_EHIP_; } while (0)
+
+template <int MB, int WF>
+static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t st) {
+  uint8_t* W = (uint8_t*)a.W;
+  const uint8_t* Xf = WF == W_BF16_ ? ws + s.xb : ws + s.xq;
+  uint16_t* Gc = (uint16_t*)(ws + s.g);
+  const uint32_t* toff = (const uint32_t*)(ws + s.tile_off);
+  const uint32_t* bucket = (const uint32_t*)(ws + s.bucket);
+  float* part = (float*)(ws + s.part);
+  float* lpart = (float*)(ws + s.loss);
+  const int64_t l_end = a.l1;
+  for (int64_t c0 = a.l0; c0 < l_end; c0 += s.Cc) {
+    const int clen = (int)((l_end - c0) < s.Cc ? (l_end - c0) : s.Cc);
+    const int nt1 = (clen + TJ1 - 1) / TJ1;
+    if (a.forward_only()) {
+      hipLaunchKernelGGL((k_fwd_g<MB, WF, false, true>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, a.Z, a.Gout, a.zpitch, a.zoff);
+      LAUNCH_CHECK();
+      continue;
+    }
+    if (a.loss)
+      hipLaunchKernelGGL((k_fwd_g<MB, WF, true, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+    else
+      hipLaunchKernelGGL((k_fwd_g<MB, WF, false, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+    LAUNCH_CHECK();
+    const int nt2 = (clen + TJ2 - 1) / TJ2;
+    const int NR = nt2 < s.NR ? nt2 : s.NR;
+    const int grid2 = 8 * s.NS * ((NR + 7) / 8);
+    if (s.DS == 128)
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
+                         (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
+    else
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
+                         (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
+    LAUNCH_CHECK();
+  }
+  return ELMO_OK_;
+}
+
+int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_t st) {
+  uint8_t* ws = (uint8_t*)workspace;
+  uint32_t* flags = (uint32_t*)(ws + s.flags);
+  uint32_t* cnt = (uint32_t*)(ws + s.tile_cnt);
+  uint32_t* off = (uint32_t*)(ws + s.tile_off);
+  // zero flags, tile counts and (for a training step) the dX partial sums
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags, (int64_t)16, 0u);
+  hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, cnt, s.ntiles + 1, 0u);
+  LAUNCH_CHECK();
+  if (!a.forward_only()) {
+    hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, st, (uint32_t*)(ws + s.part),
+                       (int64_t)s.NR * s.MB * a.D, 0u);
+    LAUNCH_CHECK();
+  }
+  if (a.B > 0 && a.row_ptr) {
+    hipLaunchKernelGGL(k_label_count, dim3(a.B), dim3(64), 0, st, a.row_ptr, a.ids, a.B, a.nnz, a.L, cnt, flags);
+    LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(k_label_scan, dim3(1), dim3(1024), 0, st, cnt, off, s.ntiles);
+  LAUNCH_CHECK();
+  if (a.B > 0 && a.row_ptr && a.nnz > 0) {
+    hipLaunchKernelGGL(k_label_scatter, dim3(a.B), dim3(64), 0, st, a.row_ptr, a.ids, a.nnz, a.L, cnt,
+                       (uint32_t*)(ws + s.bucket));
+    LAUNCH_CHECK();
+  }
+  {
+    const int64_t n = (int64_t)s.MB * a.D;
+    const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(k_prep_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)a.X, a.B, a.D, s.MB,
+                       (uint16_t*)(ws + s.xb), a.wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr);
+    LAUNCH_CHECK();
+  }
+  int rc;
+  const int MB = s.MB;
+  if (a.wdtype == W_BF16_) {
+    rc = MB == 32 ? run_chunks<32, W_BF16_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_BF16_>(a, s, ws, st)
+       : MB == 128 ? run_chunks<128, W_BF16_>(a, s, ws, st) : run_chunks<256, W_BF16_>(a, s, ws, st);
+  } else {
+    rc = MB == 32 ? run_chunks<32, W_E4M3_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_E4M3_>(a, s, ws, st)
+       : MB == 128 ? run_chunks<128, W_E4M3_>(a, s, ws, st) : run_chunks<256, W_E4M3_>(a, s, ws, st);
+  }
+  if (rc != ELMO_OK_ || a.forward_only()) return rc;
+  {
+    const int64_t n = (int64_t)a.B * a.D;
+    const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+    hipLaunchKernelGGL(k_dx_reduce, dim3(blocks), dim3(256), 0, st, (const float*)(ws + s.part), s.NR, s.MB,
+                       a.D, a.B, a.dX);
+    LAUNCH_CHECK();
+  }
+  if (a.loss) {
+    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, st, (const float*)(ws + s.loss), s.ntiles, a.loss);
+    LAUNCH_CHECK();
+  }
+  return ELMO_OK_;
+}
+
+}  // namespace elmo

@@ -1,0 +1,200 @@
+// Top-k label scoring for precision@k (ELMO summary page, "Experimental setup": P@1, P@3, P@5).
+//
+// score[n][j] = X~[n] . W[j] with the training forward's operands (X~ = E4M3-RNE(X) for E4M3
+// weights), never materialised: each work-group owns 128 samples and one label range, computes
+// 128 x 128 score tiles on the matrix cores (the same forward tile as the training step), stages
+// each tile in LDS and lets two threads per sample keep running top-KK lists in registers (KK is k
+// rounded up to 8 or 32). Lists are ordered by (score desc, label asc) with NaN after numbers.
+// A second kernel merges the per-range lists of each sample.
+#include <float.h>
+
+#include "fwd_tile.hpp"
+#include "mfma.hpp"
+#include "numerics.hpp"
+#include "step_kernels.hpp"
+
+namespace elmo {
+
+constexpr int TN = 128;                 // samples per work-group
+
+__device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb) {
+  const bool na = sa != sa, nb = sb != sb;
+  if (na != nb) return nb;
+  if (!na && sa != sb) return sa > sb;
+  return ja < jb;
+}
+
+template <int KK>
+__device__ __forceinline__ void list_insert(float (&ls)[KK], int (&lj)[KK], float s, int j) {
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    if (ranks_before(s, j, ls[i], lj[i])) {
+      const float ts = ls[i]; const int tj = lj[i];
+      ls[i] = s; lj[i] = j; s = ts; j = tj;
+    }
+  }
+}
+
+template <int KK>
+__device__ __forceinline__ void list_init(float (&ls)[KK], int (&lj)[KK]) {
+#pragma unroll
+  for (int i = 0; i < KK; ++i) { ls[i] = __builtin_nanf(""); lj[i] = INT32_MAX; }
+}
+
+template <int WF, int KK>
+__global__ __launch_bounds__(256) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
+                                                   const uint8_t* __restrict__ Xf, int nbn, int NRg,
+                                                   float* __restrict__ cs, int* __restrict__ ci) {
+  constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  constexpr int SP = TJ1 + 4;           // score tile pitch (floats)
+  static_assert(MB * SP * 4 <= fwd_smem_bytes(MB), "score staging fits in the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB)];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wb = wave >> 1, wj = wave & 1, l32 = lane & 31, hi = lane >> 5;
+  const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
+  const int r = (kq / nbn) * 8 + xcd, nb = kq % nbn;   // one range's work-groups share an XCD
+  if (r >= NRg) return;
+  const int64_t ntile = (L + TJ1 - 1) / TJ1;
+  const int64_t t0 = ntile * r / NRg, t1 = ntile * (r + 1) / NRg;
+  const int64_t rowbytes = (int64_t)D * ESZ;
+  const uint8_t* Xblk = Xf + (int64_t)nb * MB * rowbytes;
+
+  float ls[KK]; int lj[KK];
+  list_init<KK>(ls, lj);
+  const int srow = tid >> 1, half = tid & 1;
+  float* sc = (float*)smem;
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t j0 = t * TJ1;
+    const int nvalid = (int)((L - j0) < TJ1 ? (L - j0) : TJ1);
+    f32x16_t acc[MI][NI];
+    fwd_tile<MB, WF, RW, CW>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int n = wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const int jl = wj * CW + ni * 32 + l32;
+          sc[n * SP + jl] = acc[mi][ni][i];
+        }
+    __syncthreads();
+    const int jend = nvalid < (half + 1) * 64 ? nvalid : (half + 1) * 64;
+    for (int jl = half * 64; jl < jend; ++jl) {
+      const float s = sc[srow * SP + jl];
+      const int j = (int)(j0 + jl);
+      if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+    }
+    __syncthreads();                    // scores consumed before the next tile's staging
+  }
+
+  // merge the two half lists of each sample through LDS, then write this range's candidates
+  float* ms = (float*)smem;
+  int* mj = (int*)(smem + MB * KK * 4);
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < KK; ++i) { ms[srow * KK + i] = ls[i]; mj[srow * KK + i] = lj[i]; }
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int i = 0; i < KK; ++i) {
+      const float s = ms[srow * KK + i]; const int j = mj[srow * KK + i];
+      if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+    }
+    const int64_t base = ((int64_t)r * nbn * MB + (int64_t)nb * MB + srow) * KK;
+#pragma unroll
+    for (int i = 0; i < KK; ++i) { cs[base + i] = ls[i]; ci[base + i] = lj[i]; }
+  }
+}
+
+template <int KK>
+__global__ void k_topk_merge(const float* __restrict__ cs, const int* __restrict__ ci, int N, int Npad, int NRg,
+                             int k, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float ls[KK]; int lj[KK];
+  list_init<KK>(ls, lj);
+  for (int r = 0; r < NRg; ++r) {
+    const int64_t base = ((int64_t)r * Npad + n) * KK;
+    for (int i = 0; i < KK; ++i) {
+      const float s = cs[base + i]; const int j = ci[base + i];
+      if (!ranks_before(s, j, ls[KK - 1], lj[KK - 1])) break;   // per-range lists are sorted
+      list_insert<KK>(ls, lj, s, j);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KK; ++i)
+    if (i < k) {
+      out_idx[(int64_t)n * k + i] = lj[i];
+      if (out_score) out_score[(int64_t)n * k + i] = ls[i];
+    }
+}
+
+__global__ void k_prep_eval_x(const uint16_t* __restrict__ X, int N, int D, int Npad, uint16_t* __restrict__ Xb,
+                              uint8_t* __restrict__ Xq) {
+  const int64_t n = (int64_t)Npad * D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t v = (i / D) < N ? X[i] : 0u;
+    if (Xb) Xb[i] = (uint16_t)v;
+    if (Xq) Xq[i] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(v));
+  }
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+TopkLayout topk_layout(int N, int D, int64_t L, int k, int wdtype) {
+  TopkLayout s{};
+  const int KK = k <= 8 ? 8 : 32;
+  const int nbn = (N + TN - 1) / TN;
+  s.MB = nbn * TN;                                    // padded sample count
+  const int64_t ntile = (L + TJ1 - 1) / TJ1;
+  int64_t want = (2 * (int64_t)device_cus() + nbn - 1) / nbn;
+  if (want < 1) want = 1;
+  s.NRg = (int)(want < ntile ? want : ntile);
+  s.ncand = (int64_t)s.NRg * s.MB * KK;
+  size_t off = 0;
+  s.xb = off; off = align256(off + (wdtype == W_BF16_ ? 2 * (size_t)s.MB * D : 0));
+  s.xq = off; off = align256(off + (wdtype == W_E4M3_ ? (size_t)s.MB * D : 0));
+  s.cand_s = off; off = align256(off + 4 * (size_t)s.ncand);
+  s.cand_i = off; off = align256(off + 4 * (size_t)s.ncand);
+  s.total = off;
+  return s;
+}
+
+template <int KK>
+static int topk_launch(const void* W, int wdtype, int64_t L, int D, int N, int k, int32_t* idx, float* score,
+                       const TopkLayout& s, uint8_t* ws, hipStream_t st) {
+  const int nbn = s.MB / TN;
+  const int grid = 8 * nbn * ((s.NRg + 7) / 8);
+  float* cs = (float*)(ws + s.cand_s);
+  int* ci = (int*)(ws + s.cand_i);
+  if (wdtype == W_BF16_)
+    hipLaunchKernelGGL((k_topk_scan<W_BF16_, KK>), dim3(grid), dim3(256), 0, st, (const uint8_t*)W, L, D,
+                       (const uint8_t*)(ws + s.xb), nbn, s.NRg, cs, ci);
+  else
+    hipLaunchKernelGGL((k_topk_scan<W_E4M3_, KK>), dim3(grid), dim3(256), 0, st, (const uint8_t*)W, L, D,
+                       (const uint8_t*)(ws + s.xq), nbn, s.NRg, cs, ci);
+  if (hipGetLastError() != hipSuccess) return ELMO_EHIP_;
+  hipLaunchKernelGGL((k_topk_merge<KK>), dim3((N + 127) / 128), dim3(128), 0, st, cs, ci, N, s.MB, s.NRg, k, idx,
+                     score);
+  return hipGetLastError() == hipSuccess ? ELMO_OK_ : ELMO_EHIP_;
+}
+
+int run_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, int k, int32_t* idx, float* score,
+             const TopkLayout& s, void* workspace, hipStream_t st) {
+  uint8_t* ws = (uint8_t*)workspace;
+  const int64_t n = (int64_t)s.MB * D;
+  const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+  hipLaunchKernelGGL(k_prep_eval_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)X, N, D, s.MB,
+                     wdtype == W_BF16_ ? (uint16_t*)(ws + s.xb) : (uint16_t*)nullptr,
+                     wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr);
+  if (hipGetLastError() != hipSuccess) return ELMO_EHIP_;
+  return k <= 8 ? topk_launch<8>(W, wdtype, L, D, N, k, idx, score, s, ws, st)
+                : topk_launch<32>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
+}
+
+}  // namespace elmo

@@ -1,0 +1,82 @@
+"""The C-ABI library loads and exports every entry point that include/elmo_xmc.h declares, and
+rejects invalid arguments on the host (no GPU needed: validation happens before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "elmo_xmc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(elmo_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import precision_label_chunk_amd as elmo
+    if not os.path.exists(elmo.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return elmo.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["elmo_xmc_step", "elmo_xmc_topk", "elmo_xmc_step_workspace_bytes", "elmo_xmc_topk_workspace_bytes",
+              "elmo_xmc_logits", "elmo_numerics_probe", "elmo_status_str", "elmo_abi_version", "elmo_xmc_step_flags"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"missing export {n}"
+
+
+def test_status_strings_and_version(L):
+    assert L.elmo_abi_version() == 1
+    assert L.elmo_status_str(0) == b"ok"
+    assert L.elmo_status_str(-4).startswith(b"workspace")
+
+
+@pytest.mark.parametrize("B,D,Lab,chunk,wd", [(0, 768, 1000, 128, 0), (257, 768, 1000, 128, 0), (4, 96, 1000, 128, 0),
+                                              (4, 2048, 1000, 128, 0), (4, 768, 0, 128, 0), (4, 768, 1000, 0, 0),
+                                              (4, 768, 1000, 128, 7), (4, 768, 2**31, 128, 0)])
+def test_workspace_query_rejects_bad_shapes(L, B, D, Lab, chunk, wd):
+    assert L.elmo_xmc_step_workspace_bytes(B, D, Lab, chunk, wd, 10) == 0
+
+
+def test_step_rejects_invalid_arguments_before_launch(L):
+    null = None
+    # unknown format
+    assert L.elmo_xmc_step(null, 5, 1000, 768, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, 0, null) == -3
+    # bad shapes
+    assert L.elmo_xmc_step(null, 0, 1000, 100, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, 0, null) == -2
+    # null pointers
+    assert L.elmo_xmc_step(null, 0, 1000, 128, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, 0, null) == -1
+    # non-finite learning rate
+    p = ctypes.c_void_p(4096)
+    assert L.elmo_xmc_step(p, 0, 1000, 128, p, 4, p, p, 1, float("nan"), 0, 0, 128, p, null, p, 1 << 30, null) == -1
+    # misaligned pointer
+    q = ctypes.c_void_p(4097)
+    assert L.elmo_xmc_step(q, 0, 1000, 128, p, 4, p, p, 1, 0.1, 0, 0, 128, p, null, p, 1 << 30, null) == -1
+    # workspace too small (validation precedes any device work)
+    assert L.elmo_xmc_step(p, 0, 1000, 128, p, 4, p, p, 1, 0.1, 0, 0, 128, p, null, p, 16, null) == -4
+
+
+def test_topk_rejects_invalid_arguments(L):
+    null = None
+    assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 0, null, null, null, 0, null) == -2
+    assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 33, null, null, null, 0, null) == -2
+    assert L.elmo_xmc_topk(null, 0, 10, 128, null, 4, 11, null, null, null, 0, null) == -2
+    assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 5, null, null, null, 0, null) == -1
+    assert L.elmo_xmc_topk_workspace_bytes(4, 128, 1000, 0, 0) == 0
+
+
+def test_numerics_probe_rejects_bad_op(L):
+    assert L.elmo_numerics_probe(9, None, None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
+    assert L.elmo_numerics_probe(3, ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1

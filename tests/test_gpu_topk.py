@@ -1,0 +1,90 @@
+"""Top-k scoring parity against the CPU oracle. Indices must match exactly wherever the oracle's
+ranking is decided by more than the FP32 logit error; exact ties (duplicated weight rows) must go to
+the smaller label bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wk
+from tests._helpers import RTOL, assert_close, to_dev_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def elmo():
+    import precision_label_chunk_amd as m
+    m.lib()
+    return m
+
+
+def _xdev(X):
+    return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).cuda()
+
+
+def _check(idx_g, sc_g, idx_r, sc_r, Zfull, rtol):
+    """Compare unique parts exactly; where neighbouring oracle scores are closer than the logit
+    error, accept any order that is valid for the GPU's own scores."""
+    assert_close(sc_g, sc_r, rtol)
+    for n in range(idx_r.shape[0]):
+        if np.array_equal(idx_g[n], idx_r[n]):
+            continue
+        # the GPU's labels must be a valid top-k under a perturbation within the logit error
+        tol = 2 * rtol * max(np.abs(sc_r[n]).max(), 1e-6)
+        kth = sc_r[n, -1]
+        for j, s in zip(idx_g[n], sc_g[n]):
+            assert Zfull[n, j] >= kth - tol, (n, j)
+        assert len(set(idx_g[n].tolist())) == idx_g.shape[1]
+
+
+@pytest.mark.parametrize("N,D,L,k,wfmt", [(13, 64, 500, 5, wk.W_BF16), (300, 128, 5000, 5, wk.W_E4M3),
+                                          (129, 768, 3000, 1, wk.W_BF16), (64, 192, 2000, 32, wk.W_BF16),
+                                          (257, 256, 4099, 8, wk.W_E4M3), (4, 64, 40, 32, wk.W_E4M3)])
+def test_topk_matches_oracle(elmo, orc, N, D, L, k, wfmt):
+    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
+    W0 = wk.make_weights(wl)
+    X = wk.make_eval_x(wl, N)
+    print(f"  topk N={N} D={D} L={L} k={k} wfmt={wfmt}", flush=True)
+    idx, sc = elmo.topk(to_dev_codes(W0), _xdev(X), k)
+    torch.cuda.synchronize()
+    idx_r, sc_r = orc.topk(wfmt, W0, X, k)
+    Zfull = orc.logits(wfmt, W0, X, np.arange(L))
+    _check(idx.cpu().numpy(), sc.cpu().numpy(), idx_r, sc_r, Zfull, RTOL[wfmt])
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_topk_exact_ties_go_to_smaller_label(elmo, orc, wfmt):
+    """Dyadic inputs with few bits make every logit exact; duplicated rows then tie exactly."""
+    g = np.random.default_rng(3)
+    N, D, L, k = 40, 128, 2000, 6
+    xs = g.choice([-1.0, 0.0, 1.0], (N, D)) * 0.25
+    ws = g.choice([-1.0, 0.0, 1.0], (L, D)) * 0.125
+    for a, b in [(7, 100), (7, 1999), (3, 250), (1500, 20), (900, 901)]:
+        ws[b] = ws[a]
+    X = wk.to_bf16_codes(xs)
+    W0 = wk.to_bf16_codes(ws) if wfmt == wk.W_BF16 else wk.to_e4m3_codes(ws)
+    idx, sc = elmo.topk(to_dev_codes(W0), _xdev(X), k)
+    idx_r, sc_r = orc.topk(wfmt, W0, X, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.array_equal(sc.cpu().numpy(), sc_r)
+
+
+def test_topk_k1_is_argmax(elmo, orc):
+    g = np.random.default_rng(4)
+    xs = g.choice([-1.0, 1.0], (50, 64)) * 0.5
+    ws = g.choice([-1.0, 0.0, 1.0], (1000, 64)) * 0.25
+    X = wk.to_bf16_codes(xs); W0 = wk.to_bf16_codes(ws)
+    idx, _ = elmo.topk(to_dev_codes(W0), _xdev(X), 1)
+    S = xs @ ws.T
+    assert np.array_equal(idx.cpu().numpy()[:, 0], np.argmax(S, axis=1))
+
+
+def test_topk_nan_scores_rank_last(elmo, orc):
+    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=4, D=64, L=300, wfmt=wk.W_BF16)
+    W0 = wk.make_weights(wl).copy()
+    W0[:, 0] = 0x7FC0
+    W0[10] = wk.to_bf16_codes(np.full(64, 0.01)); W0[200] = wk.to_bf16_codes(np.full(64, -0.01))
+    X = wk.make_eval_x(wl, 4)
+    idx, sc = elmo.topk(to_dev_codes(W0), _xdev(X), 4)
+    idx_r, sc_r = orc.topk(wk.W_BF16, W0, X, 4)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)

@@ -200,6 +200,13 @@ def test_sampled_entry_points_equal_full_step(orc, wfmt):
     assert np.all(np.abs(d - dX[bs]) <= np.spacing(np.abs(dX[bs])))
 
 
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_update_from_g_is_the_weight_half_of_the_step(orc, wfmt):
+    wl, W, bt = _small_case(wfmt, B=10, D=64, L=150)
+    Wn, _, _, _, G = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, wl.lr, 8, 2, want_g=True)
+    assert np.array_equal(orc.update_from_g(wfmt, W, bt.X, G, wl.lr, 8, 2), Wn)
+
+
 def test_saturated_dyadic_step_is_exact(orc):
     """X, W in {+-2^-3} with a dominant first column make |z| >= 116, so the FP32 sigmoid is exactly
     0 or 1 and every intermediate is exact; the result is predicted without the oracle."""
