@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the fused, chunked XMC classifier-head training step on one MI355X.
+
+A step is one pass of the whole training hot path over one synthetic batch: label bucketing, the
+forward contraction with the sigmoid-BCE gradient epilogue, the input gradient with the pre-update
+weights, and the weight gradient fused into SGD with stochastic rounding, chunk by chunk, then the
+dX reduction. The default workload is the 3M-label E4M3 head (B=256, D=768, L=3,000,000,
+chunk 131,072, lr 0.1), with inputs resident in HBM before timing. The top-k scoring pass is timed
+separately (its own object in the JSON line) because the metric is the training step.
+
+Prints one JSON line: samples/s (value), TFLOP/s, MFMA-roofline fraction, HBM use, the dominant
+kernel's roofline from live HIP-event timing, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "classifier train-step samples/sec + TFLOP/s (% MFMA peak), L=3M D=768 FP8"
+PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "hbm": 8.0e12}   # MI355X dense MFMA and HBM3E peaks
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="e4m3_3m",
+                    help="one of tiny, bf16_131k, bf16_670k, e4m3_3m, bf16_8p6m")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--topk-n", type=int, default=4096)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, W_dev, batch, target_s):
+    """The oracle as it stands, on the first L' labels of the same weights and batch (all B samples,
+    all D features), L' sized for about `target_s` seconds; scaled to samples/s over all L labels."""
+    import numpy as np
+
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+
+    def run(Ls):
+        W = W_dev[:Ls].cpu().numpy()
+        W = W.view(np.uint16) if W.dtype == np.int16 else W
+        keep = batch.ids < Ls
+        rows = [keep[batch.row_ptr[b]:batch.row_ptr[b + 1]].sum() for b in range(wl.B)]
+        rp = np.zeros(wl.B + 1, np.int32); rp[1:] = np.cumsum(rows)
+        t0 = time.perf_counter()
+        oracle.step(wl.wfmt, W, batch.X, rp, batch.ids[keep], wl.lr, wl.seed, 0, nthreads=threads)
+        return time.perf_counter() - t0
+
+    Ls = min(wl.L, 512)
+    t = run(Ls)
+    Ls2 = int(min(wl.L, max(Ls, Ls * target_s / max(t, 1e-3))))
+    if Ls2 > Ls:
+        Ls, t = Ls2, run(Ls2)
+    per_label = t / Ls
+    return {"value": wl.B / (per_label * wl.L), "unit": "samples/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle step over the first {Ls} of {wl.L} labels (B={wl.B}, D={wl.D}, same weights "
+                      f"and batch) took {t:.2f} s; scaled linearly to all labels",
+            "seconds": round(t, 3), "labels": Ls}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU (--gpus 1); multi-GPU runs are not part of it",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_label_chunk_amd as elmo
+    import workloads as wk
+
+    wl = wk.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    elmo.lib()
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    # inputs resident in HBM before timing
+    W = wk.make_w_device(wl.L, wl.D, wl.wfmt, seed=wl.seed, device=dev)
+    nb = args.warmup + args.steps
+    host_batches = [wk.make_batch(wl, step=s) for s in range(nb)]
+    batches = []
+    for bt in host_batches:
+        batches.append((torch.from_numpy(bt.X.view(np.int16)).to(dev), torch.from_numpy(bt.row_ptr).to(dev),
+                        torch.from_numpy(bt.ids).to(dev)))
+    max_nnz = max(int(b[2].numel()) for b in batches)
+    ws = torch.empty((elmo.step_workspace_bytes(wl.B, wl.D, wl.L, wl.chunk, wl.wfmt, max_nnz),), dtype=torch.uint8,
+                     device=dev)
+    dX = torch.empty((wl.B, wl.D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        X, rp, ids = batches[s]
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
+    torch.cuda.synchronize()
+
+    elmo.kernel_timing(True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for s in range(args.warmup, nb):
+        X, rp, ids = batches[s]
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elmo.kernel_timing(False)
+    kt = elmo.kernel_timing_read()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / args.steps
+    peak_hbm = torch.cuda.max_memory_allocated(dev)
+
+    B, D, L = wl.B, wl.D, wl.L
+    flops = 6.0 * B * D * L
+    fwd_peak = PEAK["fp8"] if wl.wfmt == wk.W_E4M3 else PEAK["bf16"]
+    t_ideal = 2.0 * B * D * L / fwd_peak + 4.0 * B * D * L / PEAK["bf16"]
+    alg_bytes = 2.0 * L * D * wl.wbytes
+    samples_s = B * args.steps / (total_ms / 1e3)
+
+    # dominant kernel roofline from the live per-launch events
+    kern = {}
+    for name, per_label, peak in (("bwd", 4.0 * B * D, PEAK["bf16"]), ("fwd", 2.0 * B * D, fwd_peak)):
+        ms, n, labels = kt[name]
+        if n:
+            ach = labels * per_label / (ms / 1e3)
+            kern[name] = {"ms_total": ms, "launches": n, "avg_ms": ms / n, "achieved": ach, "peak": peak}
+    dom = max(kern, key=lambda k: kern[k]["ms_total"])
+    kd = kern[dom]
+    roofline = {"kernel": "k_bwd_update" if dom == "bwd" else "k_fwd_g", "bound": "mfma",
+                "achieved": round(kd["achieved"] / 1e12, 2), "peak": round(kd["peak"] / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(kd["achieved"] / kd["peak"], 4), "traffic": None,
+                "avg_launch_ms": round(kd["avg_ms"], 4), "launches": kd["launches"],
+                "flops_per_label": (4 if dom == "bwd" else 2) * B * D}
+    other = [k for k in kern if k != dom]
+    if other:
+        ko = kern[other[0]]
+        roofline["other_kernel"] = {"kernel": "k_fwd_g" if other[0] == "fwd" else "k_bwd_update",
+                                    "achieved_tflops": round(ko["achieved"] / 1e12, 2),
+                                    "peak_tflops": round(ko["peak"] / 1e12, 1),
+                                    "frac": round(ko["achieved"] / ko["peak"], 4),
+                                    "avg_launch_ms": round(ko["avg_ms"], 4)}
+
+    out = {"metric": METRIC, "value": round(samples_s, 1), "unit": "samples/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "e4m3+bf16" if wl.wfmt == wk.W_E4M3 else "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "B": B, "D": D, "L": L, "chunk": wl.chunk,
+                      "weights": "e4m3" if wl.wfmt == wk.W_E4M3 else "bf16", "lr": wl.lr},
+           "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
+           "mfma_roofline_frac": round(t_ideal / (ms_step / 1e3), 4),
+           "alg_hbm_gbs": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
+           "hbm_frac": round(alg_bytes / (ms_step / 1e3) / PEAK["hbm"], 4),
+           "peak_hbm_bytes": int(peak_hbm),
+           "weights_bytes": int(L * D * wl.wbytes),
+           "roofline": roofline}
+
+    if not args.no_topk:
+        N, k = args.topk_n, (wl.topk or 5)
+        Xe = torch.from_numpy(wk.make_eval_x(wl, N).view(np.int16)).to(dev)
+        tws = torch.empty((elmo.topk_workspace_bytes(N, D, L, k, wl.wfmt),), dtype=torch.uint8, device=dev)
+        elmo.topk(W, Xe, k, workspace=tws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        elmo.topk(W, Xe, k, workspace=tws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tk = e0.elapsed_time(e1)
+        tf = 2.0 * N * D * L
+        out["topk"] = {"N": N, "k": k, "ms": round(tk, 3), "samples_s": round(N / (tk / 1e3), 1),
+                       "tflops": round(tf / (tk / 1e3) / 1e12, 2),
+                       "frac": round(tf / (tk / 1e3) / fwd_peak, 4)}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, W, host_batches[0], args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,6 +120,16 @@ int elmo_xmc_forward(const void* W, int wdtype, int64_t L, int D, const void* X,
                      float* Z, uint16_t* G, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement aid (off by default; process-wide, not thread-safe): while enabled, each launch of
+ * the step's forward (index 0) and backward/update (index 1) kernels is bracketed by HIP events on
+ * the launch stream. elmo_xmc_kernel_timing_read waits for the recorded events and fills, for each
+ * of the two kernels (HOST arrays of 2): summed milliseconds, number of launches and labels
+ * processed; the records are then cleared.
+ */
+int elmo_xmc_kernel_timing(int enable);
+int elmo_xmc_kernel_timing_read(double* ms, int64_t* launches, double* labels);
+
+/*
  * Test hook: the device codec, stochastic rounding and RNG applied elementwise to n elements.
  *   op 0  BF16 RNE encode:      in0 float[n]            -> out uint16[n]
  *   op 1  E4M3 RNE-sat encode:  in0 float[n]            -> out uint8[n]

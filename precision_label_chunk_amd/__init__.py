@@ -65,6 +65,8 @@ def lib():
         L.elmo_xmc_logits.restype = i32
         L.elmo_xmc_forward.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, i64, i64, P, P, P, sz, P]
         L.elmo_xmc_forward.restype = i32
+        L.elmo_xmc_kernel_timing.argtypes = [i32]; L.elmo_xmc_kernel_timing.restype = i32
+        L.elmo_xmc_kernel_timing_read.argtypes = [P, P, P]; L.elmo_xmc_kernel_timing_read.restype = i32
         L.elmo_numerics_probe.argtypes = [i32, P, P, P, i64, u64, u64, P]
         L.elmo_numerics_probe.restype = i32
         _lib = L
@@ -184,6 +186,18 @@ def forward(W, X, row_ptr, ids, l0, l1, want_z=True, want_g=True):
                                                     _ptr(ids) if nnz else None, nnz, l0, l1, _ptr(Z), _ptr(G),
                                                     _ptr(ws), ws.numel(), _stream()))
     return Z, G
+
+
+def kernel_timing(enable: bool):
+    """Bracket each forward / backward kernel launch of later steps with HIP events."""
+    _chk("elmo_xmc_kernel_timing", lib().elmo_xmc_kernel_timing(1 if enable else 0))
+
+
+def kernel_timing_read():
+    """{'fwd': (ms, launches, labels), 'bwd': (...)} summed since the last read (synchronises)."""
+    ms = (ctypes.c_double * 2)(); n = (ctypes.c_int64 * 2)(); lab = (ctypes.c_double * 2)()
+    _chk("elmo_xmc_kernel_timing_read", lib().elmo_xmc_kernel_timing_read(ms, n, lab))
+    return {"fwd": (ms[0], n[0], lab[0]), "bwd": (ms[1], n[1], lab[1])}
 
 
 def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):

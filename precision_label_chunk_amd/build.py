@@ -31,6 +31,12 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    # a kernel template whose host stub was silently not instantiated shows up as an undefined
+    # symbol of this library: refuse such a build instead of failing at load time
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "elmo" in ln]
+    if missing:
+        raise RuntimeError("libelmo_xmc.so has undefined library symbols: " + ", ".join(missing[:5]))
     os.replace(tmp, LIB)
     return LIB
 

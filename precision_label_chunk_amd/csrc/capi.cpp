@@ -118,6 +118,16 @@ int elmo_xmc_topk(const void* W, int wdtype, int64_t L, int D, const void* X, in
   return elmo::run_topk(W, wdtype, L, D, X, N, k, out_idx, out_score, s, workspace, (hipStream_t)stream);
 }
 
+int elmo_xmc_kernel_timing(int enable) {
+  elmo::kernel_timing_enable(enable);
+  return ELMO_OK;
+}
+
+int elmo_xmc_kernel_timing_read(double* ms, int64_t* launches, double* labels) {
+  if (!ms || !launches || !labels) return ELMO_EINVAL;
+  return elmo::kernel_timing_read(ms, launches, labels);
+}
+
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                         uint64_t step, void* stream) {
   return elmo::run_numerics_probe(op, in0, in1, out, n, seed, step, (hipStream_t)stream);

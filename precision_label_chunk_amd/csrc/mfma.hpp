@@ -40,6 +40,12 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<uint16_t*>(p)));
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i writes lds_base + 16 i (the
+// wave-uniform base goes to M0). Kept out of lambdas: the builtin only exists for the device.
+__device__ __forceinline__ void global_load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+}
+
 __device__ __forceinline__ s16x8_t join(s16x4_t lo, s16x4_t hi) {
   return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }

@@ -31,14 +31,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 }
 
 // ---- OCP E4M3 (E4M3FN) --------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float v;
-  if (e == 0) v = (float)m * 0.001953125f;               // m * 2^-9
-  else if (e == 15 && m == 7) v = u2f(0x7fc00000u);       // NaN
-  else v = u2f(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -v : v;
-}
+// gfx950's FP8 conversions use the OCP encoding (0x7E = 448, 0x7F/0xFF NaN, subnormals kept).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // E4M3 values have at most 4 significant bits and exponents inside BF16's range: exact
 __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
@@ -57,27 +51,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
 }
 
 // ---- stochastic rounding ------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t sr_bf16(float t, uint32_t r16) {
-  uint32_t u = f2u(t);
-  uint32_t s = u & 0x80000000u, a = u & 0x7fffffffu;
-  if (a >= 0x7f800000u) return (a > 0x7f800000u) ? ((u >> 16) | 0x40u) : (u >> 16);
-  return (s | (a + r16)) >> 16;   // carry from the dropped half rounds the magnitude up
+// gfx950's v_cvt_sr_bf16_f32 / v_cvt_sr_fp8_f32, fed the 16 random bits in the upper half of the
+// random operand, implement exactly the rule above (checked over all 2^16 random values on finite
+// inputs, subnormals included). The FP8 instruction turns |t| >= 448 into NaN rather than
+// saturating, so the input is clamped first; a NaN input gives a NaN code.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// BF16 SR of t into the low (hi = false) or high half of `old`; rhi holds the random bits in 31..16
+__device__ __forceinline__ uint32_t sr_bf16_into(uint32_t old, float t, uint32_t rhi, bool hi) {
+  bf16x2_t o = __builtin_bit_cast(bf16x2_t, old);
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_sr_bf16_f32(o, t, rhi, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_sr_bf16_f32(o, t, rhi, false));
 }
 
-__device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) {
-  uint32_t u = f2u(t);
-  uint32_t s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return s | 0x7fu;
-  if (a >= 0x43e00000u) return s | 0x7eu;
-  if (a >= 0x3c800000u) {
-    uint32_t q = (a >> 4) & 0xffffu;                      // top 16 of the 20 dropped bits
-    return s | ((a >> 20) - 960u + ((q + r16) >> 16));
-  }
-  float v = u2f(a) * 512.0f;                              // units of the subnormal spacing 2^-9
-  float k = __builtin_floorf(v);
-  uint32_t q = (uint32_t)((v - k) * 65536.0f);           // exact fraction, truncated
-  return s | ((uint32_t)k + ((q + r16) >> 16));
+__device__ __forceinline__ float clamp_e4m3(float t) {
+  return __builtin_fabsf(t) >= 448.0f ? __builtin_copysignf(448.0f, t) : t;   // NaN stays NaN
 }
+
+// E4M3 SR of t into byte `sel` of `old`; rhi holds the random bits in 31..16
+template <int SEL>
+__device__ __forceinline__ uint32_t sr_e4m3_into(uint32_t old, float t, uint32_t rhi) {
+  return (uint32_t)__builtin_amdgcn_cvt_sr_fp8_f32(clamp_e4m3(t), (int)rhi, (int)old, SEL);
+}
+
+__device__ __forceinline__ uint32_t sr_bf16(float t, uint32_t r16) { return sr_bf16_into(0u, t, r16 << 16, false) & 0xffffu; }
+__device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) { return sr_e4m3_into<0>(0u, t, r16 << 16) & 0xffu; }
 
 // ---- Philox4x32-10 ------------------------------------------------------------------------------
 struct u32x4 { uint32_t x, y, z, w; };
@@ -107,6 +105,12 @@ __device__ __forceinline__ u32x4 rng_block(uint64_t seed, uint64_t step, uint64_
 __device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = idx & 7
   uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// the same 16 bits placed in bits 31..16 (the form the SR instructions take)
+__device__ __forceinline__ uint32_t rng_pick_hi(const u32x4& r, int e) {
+  uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
+  return (e & 1) ? (w & 0xffff0000u) : (w << 16);
 }
 
 // ---- sigmoid-BCE gradient -----------------------------------------------------------------------

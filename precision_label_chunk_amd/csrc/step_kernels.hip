@@ -17,6 +17,8 @@
 // Label handling, X preparation and the final dX reduction are small kernels around them.
 #include "step_kernels.hpp"
 
+#include <vector>
+
 #include "fwd_tile.hpp"
 #include "mfma.hpp"
 #include "numerics.hpp"
@@ -216,28 +218,45 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
 // ------------------------------------------------------------------------------------------------
 // backward + fused update over one d-slice and one label range of the chunk
 // ------------------------------------------------------------------------------------------------
+// Work-group: 2 * DS/32 waves (two per SIMD for DS = 128). Wave w works on the 32 features
+// [dsl + 32 (w % ND), +32) of the slice; the two waves of a feature block split the other MFMA
+// dimension (samples for dX, labels for dW) between them.
+// Per 64-label tile t (double buffered in LDS, the next tile's loads in flight during this one):
+//   G tile  [MB][64] BF16, fetched straight into LDS (global_load_lds), 16-byte chunks XOR-swizzled
+//           by row so that both the row reads (dX operand) and the transposing reads (dW operand)
+//           are free of bank conflicts;
+//   W tile  [64][DS] decoded to BF16 in LDS;
+//   dX^T[d][b] += sum_j W^T[d][j] G[b][j]   (A = W^T via ds_read_b64_tr_b16, B = G rows)
+//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]   (A = stationary X^T fragments in registers, B = G^T)
+//   dW -> LDS; each thread then updates 8 consecutive weights of a row with one Philox block:
+//   t = fmaf(-lr, dW, w), hardware stochastic rounding, one coalesced store.
 template <int MB, int WF, int DS>
-__global__ __launch_bounds__(256) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
-                                                    const uint16_t* __restrict__ Xb,
-                                                    const uint16_t* __restrict__ G, int64_t gpitch,
-                                                    float* __restrict__ part, int NR, int NS, float lr,
-                                                    uint64_t seed, uint64_t step) {
+__global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
+                                                       const uint16_t* __restrict__ Xb,
+                                                       const uint16_t* __restrict__ G, int64_t gpitch,
+                                                       float* __restrict__ part, int NR, int NS, float lr,
+                                                       uint64_t seed, uint64_t step) {
+  constexpr int ND = DS / 32;                  // feature blocks
+  constexpr int NWV = 2 * ND, NT = 64 * NWV;   // waves, threads
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  constexpr int NWM = DS / 32;                 // waves that own a 32-wide d block
   constexpr int NB = MB / 32;
-  constexpr int GPE = TJ2 + 8;                 // G tile pitch (elements)
+  constexpr bool SPLIT_B = NB >= 2;            // dX: the two waves split samples, else split K
+  constexpr int NBW = SPLIT_B ? NB / 2 : NB;   // sample blocks per wave for dX
+  constexpr int GTE = MB * TJ2;                // G tile elements (rows of 64 labels = 128 bytes)
   constexpr int WPE = DS + 8;                  // W tile pitch (BF16 elements)
   constexpr int DWP = DS + 4;                  // dW tile pitch (floats)
-  constexpr int GPT = MB * (TJ2 / 8) / 256;    // 16-byte G chunks per thread
   constexpr int WCPR = DS * ESZ / 16;          // 16-byte W chunks per tile row
-  constexpr int WPT = TJ2 * WCPR / 256;        // W chunks per thread
-  constexpr int EPC = 16 / ESZ;                // weights per chunk
-  static_assert(GPT >= 1 && WPT >= 1, "tile split");
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[MB * GPE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[TJ2 * WPE];
+  constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
+  constexpr int UPR = DS / 8;                  // update units (8 weights) per row
+  constexpr int UPT = TJ2 * UPR / NT;          // update units per thread
+  static_assert(WPT >= 1 && UPT >= 1 && TJ2 == 64, "tile split");
+  __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][GTE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][TJ2 * WPE];
   __shared__ __attribute__((aligned(16))) float dWs[TJ2 * DWP];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dblk = wave % ND, half = wave / ND;
   const int l32 = lane & 31, hi = lane >> 5, q = lane >> 4, li = lane & 15;
   // work-groups of one label range share its G tiles: keep them on one XCD (dispatch is round-robin)
   const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
@@ -248,49 +267,45 @@ __global__ __launch_bounds__(256) void k_bwd_update(uint8_t* __restrict__ W, int
   const int dsl = s * DS;
   const int64_t rowbytes = (int64_t)D * ESZ;
 
-  s16x8_t xT[MB / 16];                         // stationary X^T fragments: lane (d, 8 samples)
-  if (wave < NWM) {
-    const int d = dsl + wave * 32 + l32;
+  // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples)
+  s16x8_t xT[MB / 16];
+  {
+    const int d = dsl + dblk * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < MB / 16; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) xT[kk][e] = (short)Xb[(kk * 16 + hi * 8 + e) * D + d];
   }
-  f32x16_t accX[NB];
+  f32x16_t accX[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) accX[nb] = f32x16_t{};
+  for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
 
-  i32x4_t gst[GPT], wst[WPT], wcur[WPT];
-  auto load = [&](int t) {
+  // G tile: instruction i fills rows 8i..8i+7; lane -> (row, swizzled chunk position)
+  auto load_g = [&](int t, int buf) {
+    const int jb = t * TJ2;
+    for (int inst = wave; inst < MB / 8; inst += NWV) {
+      const int row = inst * 8 + (lane >> 3), pos = lane & 7;
+      const int chunk = pos ^ (row & 7);
+      global_load_lds16(G + row * gpitch + jb + chunk * 8, &Gs[buf][inst * 512]);
+    }
+  };
+  i32x4_t wst[WPT];
+  auto load_w = [&](int t) {
     const int jb = t * TJ2;
 #pragma unroll
-    for (int c = 0; c < GPT; ++c) {
-      const int ci = tid + c * 256, row = ci >> 3, p = ci & 7;
-      gst[c] = *(const i32x4_t*)(G + row * gpitch + jb + p * 8);
-    }
-#pragma unroll
     for (int c = 0; c < WPT; ++c) {
-      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
+      const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
       i32x4_t v = {0, 0, 0, 0};
       if (jb + jr < clen) v = *(const i32x4_t*)(W + (c0 + jb + jr) * rowbytes + (int64_t)dsl * ESZ + p * 16);
       wst[c] = v;
     }
   };
-
-  if (t0 < t1) load(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < GPT; ++c) {
-      const int ci = tid + c * 256, row = ci >> 3, p = ci & 7;
-      *(i32x4_t*)(Gs + row * GPE + p * 8) = gst[c];
-    }
+  auto store_w = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < WPT; ++c) {
-      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
-      wcur[c] = wst[c];
+      const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
       if constexpr (WF == W_BF16_) {
-        *(i32x4_t*)(Ws + jr * WPE + p * 8) = wst[c];
+        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 8]) = wst[c];
       } else {
         i32x4_t lo, hi4;
 #pragma unroll
@@ -301,107 +316,179 @@ __global__ __launch_bounds__(256) void k_bwd_update(uint8_t* __restrict__ W, int
           if (w < 2) { lo[2 * w] = (int)p0; lo[2 * w + 1] = (int)p1; }
           else { hi4[2 * (w - 2)] = (int)p0; hi4[2 * (w - 2) + 1] = (int)p1; }
         }
-        *(i32x4_t*)(Ws + jr * WPE + p * 16) = lo;
-        *(i32x4_t*)(Ws + jr * WPE + p * 16 + 8) = hi4;
+        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 16]) = lo;
+        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 16 + 8]) = hi4;
       }
     }
-    __syncthreads();
-    if (t + 1 < t1) load(t + 1);               // next tile's loads overlap this tile's math
+  };
+  // swizzled element offset of (row b, label column j) in a G tile
+  auto gidx = [](int b, int j) { return b * TJ2 + (((j >> 3) ^ (b & 7)) << 3) + (j & 7); };
 
-    if (wave < NWM) {
-      // dX^T[d][b] += sum_j W^T[d][j] G[b][j]        (M = d, N = b, K = j)
+  if (t0 < t1) {
+    load_g(t0, 0);
+    load_w(t0);
+    store_w(0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    __syncthreads();                           // tile t resident; iteration t-1 fully done
+    if (t + 1 < t1) { load_g(t + 1, buf ^ 1); load_w(t + 1); }
+    const uint16_t* gs = Gs[buf];
+    const uint16_t* ws = Ws[buf];
+
+    // dX^T[d][b] += W^T[d][j] G[b][j]      (M = d, N = b, K = j)
 #pragma unroll
-      for (int kk = 0; kk < TJ2 / 16; ++kk) {
-        const uint16_t* pa = Ws + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * WPE + wave * 32 + 16 * (q & 1) + 4 * (li & 3);
-        const s16x8_t a = join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
+    for (int kk = 0; kk < TJ2 / 16; ++kk) {
+      if (!SPLIT_B && (kk >> 1) != half) continue;
+      const uint16_t* pa = ws + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * WPE + dblk * 32 + 16 * (q & 1) + 4 * (li & 3);
+      const s16x8_t a = join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
+      s16x8_t bv[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const s16x8_t bv = *(const s16x8_t*)(Gs + (nb * 32 + l32) * GPE + kk * 16 + hi * 8);
-          accX[nb] = mfma_bf16(a, bv, accX[nb]);
-        }
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int b = (SPLIT_B ? half * NBW + nb : nb) * 32 + l32;
+        bv[nb] = *(const s16x8_t*)(gs + gidx(b, kk * 16 + hi * 8));
       }
-      // dW^T[d][j] = sum_b X^T[d][b] G[b][j]         (M = d, N = j, K = b)
-      f32x16_t accW[TJ2 / 32];
 #pragma unroll
-      for (int nj = 0; nj < TJ2 / 32; ++nj) accW[nj] = f32x16_t{};
-#pragma unroll
-      for (int kk = 0; kk < MB / 16; ++kk)
-#pragma unroll
-        for (int nj = 0; nj < TJ2 / 32; ++nj) {
-          const uint16_t* pb = Gs + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * GPE + nj * 32 + 16 * (q & 1) + 4 * (li & 3);
-          accW[nj] = mfma_bf16(xT[kk], join(lds_read_tr16(pb), lds_read_tr16(pb + 4 * GPE)), accW[nj]);
-        }
-#pragma unroll
-      for (int nj = 0; nj < TJ2 / 32; ++nj)
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          f32x4_t v = {accW[nj][4 * ig], accW[nj][4 * ig + 1], accW[nj][4 * ig + 2], accW[nj][4 * ig + 3]};
-          *(f32x4_t*)(dWs + (nj * 32 + l32) * DWP + wave * 32 + 8 * ig + 4 * hi) = v;
-        }
+      for (int nb = 0; nb < NBW; ++nb) accX[nb] = mfma_bf16(a, bv[nb], accX[nb]);
     }
-    __syncthreads();
-
-    // fused SGD + stochastic rounding, in place, 16 bytes per thread-chunk
+    // dW^T[d][j] = X^T[d][b] G[b][j]         (M = d, N = j, K = b): this wave's 32 labels = half
+    f32x16_t accW = f32x16_t{};
 #pragma unroll
-    for (int c = 0; c < WPT; ++c) {
-      const int ci = tid + c * 256, jr = ci / WCPR, p = ci % WCPR;
+    for (int kk = 0; kk < MB / 16; ++kk) {
+      const int b0 = kk * 16 + 8 * (q >> 1) + (li >> 2), j0 = half * 32 + 16 * (q & 1) + 4 * (li & 3);
+      const s16x8_t bv = join(lds_read_tr16(gs + gidx(b0, j0)), lds_read_tr16(gs + gidx(b0 + 4, j0)));
+      accW = mfma_bf16(xT[kk], bv, accW);
+    }
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const f32x4_t v = {accW[4 * ig], accW[4 * ig + 1], accW[4 * ig + 2], accW[4 * ig + 3]};
+      *(f32x4_t*)(dWs + (half * 32 + l32) * DWP + dblk * 32 + 8 * ig + 4 * hi) = v;
+    }
+    __syncthreads();                           // dW tile complete
+
+    // fused SGD + stochastic rounding: 8 consecutive weights of one row per unit
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int ui = tid + u * NT, jr = ui / UPR, d0 = (ui % UPR) * 8;
       const int jb = t * TJ2;
       if (jb + jr >= clen) continue;
       const int64_t jg = c0 + jb + jr;
-      const int d0 = p * EPC;
-      const float* dw = dWs + jr * DWP + d0;
-      const uint64_t idx0 = (uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + d0);
-      i32x4_t out;
+      const f32x4_t dw0 = *(const f32x4_t*)(dWs + jr * DWP + d0);
+      const f32x4_t dw1 = *(const f32x4_t*)(dWs + jr * DWP + d0 + 4);
+      const i32x4_t wv = *(const i32x4_t*)(ws + jr * WPE + d0);
+      const u32x4 rnd = rng_block(seed, step, ((uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + d0)) >> 3);
+      float tv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wb = (uint32_t)wv[e >> 1];
+        const float w = u2f((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+        tv[e] = fmaf(-lr, e < 4 ? dw0[e] : dw1[e - 4], w);
+      }
+      uint8_t* dst = W + jg * rowbytes + (int64_t)(dsl + d0) * ESZ;
       if constexpr (WF == W_BF16_) {
-        const u32x4 rnd = rng_block(seed, step, idx0 >> 3);
+        i32x4_t out;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t v = (uint32_t)wcur[c][w];
-          const float t0f = fmaf(-lr, dw[2 * w], bf16_to_f32(v & 0xffffu));
-          const float t1f = fmaf(-lr, dw[2 * w + 1], bf16_to_f32(v >> 16));
-          out[w] = (int)(sr_bf16(t0f, rng_pick(rnd, 2 * w)) | (sr_bf16(t1f, rng_pick(rnd, 2 * w + 1)) << 16));
+          const uint32_t lo = sr_bf16_into(0u, tv[2 * w], rng_pick_hi(rnd, 2 * w), false);
+          out[w] = (int)sr_bf16_into(lo, tv[2 * w + 1], rng_pick_hi(rnd, 2 * w + 1), true);
         }
+        *(i32x4_t*)dst = out;
       } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 rnd = rng_block(seed, step, (idx0 >> 3) + h);
-#pragma unroll
-          for (int w = 2 * h; w < 2 * h + 2; ++w) {
-            const uint32_t v = (uint32_t)wcur[c][w];
-            uint32_t o = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float tf = fmaf(-lr, dw[4 * w + e], e4m3_to_f32((v >> (8 * e)) & 0xffu));
-              o |= sr_e4m3(tf, rng_pick(rnd, 4 * (w - 2 * h) + e)) << (8 * e);
-            }
-            out[w] = (int)o;
-          }
-        }
+        uint32_t o0 = 0, o1 = 0;
+        o0 = sr_e4m3_into<0>(o0, tv[0], rng_pick_hi(rnd, 0));
+        o0 = sr_e4m3_into<1>(o0, tv[1], rng_pick_hi(rnd, 1));
+        o0 = sr_e4m3_into<2>(o0, tv[2], rng_pick_hi(rnd, 2));
+        o0 = sr_e4m3_into<3>(o0, tv[3], rng_pick_hi(rnd, 3));
+        o1 = sr_e4m3_into<0>(o1, tv[4], rng_pick_hi(rnd, 4));
+        o1 = sr_e4m3_into<1>(o1, tv[5], rng_pick_hi(rnd, 5));
+        o1 = sr_e4m3_into<2>(o1, tv[6], rng_pick_hi(rnd, 6));
+        o1 = sr_e4m3_into<3>(o1, tv[7], rng_pick_hi(rnd, 7));
+        *(uint2*)dst = make_uint2(o0, o1);
       }
-      *(i32x4_t*)(W + jg * rowbytes + (int64_t)(dsl + d0) * ESZ) = out;
+    }
+    if (t + 1 < t1) {
+      store_w(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(0);           // this thread's G and W loads for tile t+1 landed
     }
   }
 
-  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic)
-  if (wave < NWM) {
+  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic).
+  // With the K split (one sample block) the two waves of a feature block add in turn.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int pass = 0; pass < (SPLIT_B ? 1 : 2); ++pass) {
+    if (SPLIT_B || half == pass) {
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const int b = nb * 32 + l32;
-        const int d = dsl + wave * 32 + 8 * ig + 4 * hi;
-        f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
-        f32x4_t v = *pp;
-        v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
-        v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
-        *pp = v;
-      }
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int b = (SPLIT_B ? half * NBW + nb : nb) * 32 + l32;
+          const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
+          f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
+          f32x4_t v = *pp;
+          v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
+          v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
+          *pp = v;
+        }
+    }
+    if (!SPLIT_B && pass == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// host side: workspace layout, chunk scheduler, launches
+// host side: optional kernel timing, workspace layout, chunk scheduler, launches
 // ------------------------------------------------------------------------------------------------
+namespace {
+struct KTRec { int kind; int64_t labels; hipEvent_t a, b; };
+struct KTState {
+  int on = 0;
+  std::vector<KTRec> recs;      // pending launches (events reused through `pool`)
+  std::vector<hipEvent_t> pool;
+};
+KTState& kt() { static KTState s; return s; }
+hipEvent_t kt_event() {
+  KTState& s = kt();
+  if (!s.pool.empty()) { hipEvent_t e = s.pool.back(); s.pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void kernel_timing_enable(int on) { kt().on = on; }
+
+void kt_begin(int kind, hipStream_t st, int64_t labels) {
+  KTState& s = kt();
+  if (!s.on) return;
+  KTRec r{kind, labels, kt_event(), kt_event()};
+  if (!r.a || !r.b) return;
+  hipEventRecord(r.a, st);
+  s.recs.push_back(r);
+}
+
+void kt_end(int kind, hipStream_t st) {
+  KTState& s = kt();
+  if (!s.on || s.recs.empty() || s.recs.back().kind != kind) return;
+  hipEventRecord(s.recs.back().b, st);
+}
+
+int kernel_timing_read(double* ms, int64_t* launches, double* labels) {
+  KTState& s = kt();
+  for (int k = 0; k < 2; ++k) { ms[k] = 0.0; launches[k] = 0; labels[k] = 0.0; }
+  int rc = ELMO_OK_;
+  for (const KTRec& r : s.recs) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) rc = ELMO_EHIP_;
+    ms[r.kind] += t; launches[r.kind] += 1; labels[r.kind] += (double)r.labels;
+    s.pool.push_back(r.a); s.pool.push_back(r.b);
+  }
+  s.recs.clear();
+  return rc;
+}
+
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int padded_batch(int B) { return B <= 32 ? 32 : B <= 64 ? 64 : B <= 128 ? 128 : 256; }
@@ -464,6 +551,7 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
       LAUNCH_CHECK();
       continue;
     }
+    kt_begin(KT_FWD, st, clen);
     if (a.loss)
       hipLaunchKernelGGL((k_fwd_g<MB, WF, true, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
                          toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
@@ -471,16 +559,19 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
       hipLaunchKernelGGL((k_fwd_g<MB, WF, false, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
                          toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
     LAUNCH_CHECK();
+    kt_end(KT_FWD, st);
     const int nt2 = (clen + TJ2 - 1) / TJ2;
     const int NR = nt2 < s.NR ? nt2 : s.NR;
     const int grid2 = 8 * s.NS * ((NR + 7) / 8);
+    kt_begin(KT_BWD, st, clen);
     if (s.DS == 128)
-      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(512), 0, st, W, a.D, c0, clen,
                          (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
     else
       hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
                          (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
     LAUNCH_CHECK();
+    kt_end(KT_BWD, st);
   }
   return ELMO_OK_;
 }

@@ -34,6 +34,15 @@ struct StepArgs {
   bool forward_only() const { return Z != nullptr || Gout != nullptr; }
 };
 
+// Optional per-launch HIP-event timing of the two chunk kernels (a measurement aid; off by default).
+// When enabled, every forward / backward launch of a step is bracketed by events on the launch
+// stream; kernel_timing_read() synchronises those events and returns the summed milliseconds.
+enum { KT_FWD = 0, KT_BWD = 1 };
+void kernel_timing_enable(int on);
+int kernel_timing_read(double* ms, int64_t* launches, double* labels);
+void kt_begin(int kind, hipStream_t st, int64_t labels);
+void kt_end(int kind, hipStream_t st);
+
 int padded_batch(int B);
 int device_cus();
 StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64_t max_nnz);
