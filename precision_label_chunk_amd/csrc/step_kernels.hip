@@ -224,12 +224,13 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
 // Per 64-label tile t (double buffered in LDS, the next tile's loads in flight during this one):
 //   G tile  [MB][64] BF16, fetched straight into LDS (global_load_lds), 16-byte chunks XOR-swizzled
 //           by row so that both the row reads (dX operand) and the transposing reads (dW operand)
-//           are free of bank conflicts;
+//           avoid bank conflicts;
 //   W tile  [64][DS] decoded to BF16 in LDS;
 //   dX^T[d][b] += sum_j W^T[d][j] G[b][j]   (A = W^T via ds_read_b64_tr_b16, B = G rows)
 //   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]   (A = stationary X^T fragments in registers, B = G^T)
-//   dW -> LDS; each thread then updates 8 consecutive weights of a row with one Philox block:
-//   t = fmaf(-lr, dW, w), hardware stochastic rounding, one coalesced store.
+//   dW stays in the accumulators: one permlane32 swap gives every lane 2 x 8 consecutive features
+//   of one label, which it updates with one Philox block each: t = fmaf(-lr, dW, w), hardware
+//   stochastic rounding, one coalesced store per 8 weights. One barrier per tile.
 template <int MB, int WF, int DS>
 __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
                                                        const uint16_t* __restrict__ Xb,
@@ -244,15 +245,11 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
   constexpr int NBW = SPLIT_B ? NB / 2 : NB;   // sample blocks per wave for dX
   constexpr int GTE = MB * TJ2;                // G tile elements (rows of 64 labels = 128 bytes)
   constexpr int WPE = DS + 8;                  // W tile pitch (BF16 elements)
-  constexpr int DWP = DS + 4;                  // dW tile pitch (floats)
   constexpr int WCPR = DS * ESZ / 16;          // 16-byte W chunks per tile row
   constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
-  constexpr int UPR = DS / 8;                  // update units (8 weights) per row
-  constexpr int UPT = TJ2 * UPR / NT;          // update units per thread
-  static_assert(WPT >= 1 && UPT >= 1 && TJ2 == 64, "tile split");
+  static_assert(WPT >= 1 && TJ2 == 64, "tile split");
   __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][GTE];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][TJ2 * WPE];
-  __shared__ __attribute__((aligned(16))) float dWs[TJ2 * DWP];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -280,7 +277,17 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
 
-  // G tile: instruction i fills rows 8i..8i+7; lane -> (row, swizzled chunk position)
+  // loop-invariant LDS element offsets (the G swizzle only depends on the row's low 3 bits)
+  //   dX operand B, row b = ... + l32, label chunk 2 kk + hi  -> offset gB + kk-dependent chunk
+  //   dW operand B (transposing reads), rows b0 + {0..3}, labels j0 .. j0 + 3
+  const int bX0 = (SPLIT_B ? half * NBW : 0) * 32 + l32;             // + 32 nb
+  const int sX = l32 & 7;
+  const int b0W = 8 * (q >> 1) + (li >> 2);                          // + 16 kk (+ 4 for the 2nd read)
+  const int j0W = half * 32 + 16 * (q & 1) + 4 * (li & 3);
+  const int offW0 = b0W * TJ2 + (((j0W >> 3) ^ (b0W & 7)) << 3) + (j0W & 7);
+  const int offW1 = (b0W + 4) * TJ2 + (((j0W >> 3) ^ ((b0W + 4) & 7)) << 3) + (j0W & 7);
+  const int offA = (8 * (q >> 1) + (li >> 2)) * WPE + dblk * 32 + 16 * (q & 1) + 4 * (li & 3);
+
   auto load_g = [&](int t, int buf) {
     const int jb = t * TJ2;
     for (int inst = wave; inst < MB / 8; inst += NWV) {
@@ -321,8 +328,6 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
       }
     }
   };
-  // swizzled element offset of (row b, label column j) in a G tile
-  auto gidx = [](int b, int j) { return b * TJ2 + (((j >> 3) ^ (b & 7)) << 3) + (j & 7); };
 
   if (t0 < t1) {
     load_g(t0, 0);
@@ -337,79 +342,103 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
     const uint16_t* gs = Gs[buf];
     const uint16_t* ws = Ws[buf];
 
-    // dX^T[d][b] += W^T[d][j] G[b][j]      (M = d, N = b, K = j)
-#pragma unroll
-    for (int kk = 0; kk < TJ2 / 16; ++kk) {
-      if (!SPLIT_B && (kk >> 1) != half) continue;
-      const uint16_t* pa = ws + (kk * 16 + 8 * (q >> 1) + (li >> 2)) * WPE + dblk * 32 + 16 * (q & 1) + 4 * (li & 3);
-      const s16x8_t a = join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
-      s16x8_t bv[NBW];
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const int b = (SPLIT_B ? half * NBW + nb : nb) * 32 + l32;
-        bv[nb] = *(const s16x8_t*)(gs + gidx(b, kk * 16 + hi * 8));
-      }
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) accX[nb] = mfma_bf16(a, bv[nb], accX[nb]);
-    }
-    // dW^T[d][j] = X^T[d][b] G[b][j]         (M = d, N = j, K = b): this wave's 32 labels = half
+    // The two contractions, interleaved so that the independent dX MFMAs fill the dependency gaps
+    // of the dW chain, with every LDS fragment read issued two steps ahead of its MFMA:
+    //   dX^T[d][b] += W^T[d][j] G[b][j]      (M = d, N = b, K = j)   NDX MFMAs
+    //   dW^T[d][j]  = X^T[d][b] G[b][j]      (M = d, N = j, K = b)   NDW MFMAs, one chain
+    constexpr int NDW = MB / 16;
+    constexpr int KXN = SPLIT_B ? TJ2 / 16 : TJ2 / 32;     // dX K steps of this wave
+    constexpr int NDX = KXN * NBW;
+    constexpr int NST = NDW > NDX ? NDW : NDX;
+    constexpr int PF = 2;                                  // prefetch distance (steps)
+    const int kx0 = SPLIT_B ? 0 : half * KXN;
+    auto ldW = [&](int kk) {
+      return join(lds_read_tr16(gs + offW0 + kk * 16 * TJ2), lds_read_tr16(gs + offW1 + kk * 16 * TJ2));
+    };
+    auto ldXa = [&](int kx) {
+      const uint16_t* pa = ws + offA + (kx0 + kx) * 16 * WPE;
+      return join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
+    };
+    auto ldXb = [&](int x) {
+      const int kx = x / NBW, nb = x % NBW;
+      const int cx = ((2 * (kx0 + kx) + hi) ^ sX) << 3;
+      return *(const s16x8_t*)(gs + (bX0 + nb * 32) * TJ2 + cx);
+    };
+    s16x8_t fW[NST + PF], fXa[KXN + 1], fXb[NST + PF];
     f32x16_t accW = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < MB / 16; ++kk) {
-      const int b0 = kk * 16 + 8 * (q >> 1) + (li >> 2), j0 = half * 32 + 16 * (q & 1) + 4 * (li & 3);
-      const s16x8_t bv = join(lds_read_tr16(gs + gidx(b0, j0)), lds_read_tr16(gs + gidx(b0 + 4, j0)));
-      accW = mfma_bf16(xT[kk], bv, accW);
+    for (int i = 0; i < PF; ++i) {
+      if (i < NDW) fW[i] = ldW(i);
+      if (i < NDX) { if (i % NBW == 0) fXa[i / NBW] = ldXa(i / NBW); fXb[i] = ldXb(i); }
     }
 #pragma unroll
-    for (int ig = 0; ig < 4; ++ig) {
-      const f32x4_t v = {accW[4 * ig], accW[4 * ig + 1], accW[4 * ig + 2], accW[4 * ig + 3]};
-      *(f32x4_t*)(dWs + (half * 32 + l32) * DWP + dblk * 32 + 8 * ig + 4 * hi) = v;
+    for (int i = 0; i < NST; ++i) {
+      const int p = i + PF;
+      if (p < NDW) fW[p] = ldW(p);
+      if (p < NDX) { if (p % NBW == 0) fXa[p / NBW] = ldXa(p / NBW); fXb[p] = ldXb(p); }
+      if (i < NDW) accW = mfma_bf16(xT[i], fW[i], accW);
+      if (i < NDX) accX[i % NBW] = mfma_bf16(fXa[i / NBW], fXb[i], accX[i % NBW]);
     }
-    __syncthreads();                           // dW tile complete
 
-    // fused SGD + stochastic rounding: 8 consecutive weights of one row per unit
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int ui = tid + u * NT, jr = ui / UPR, d0 = (ui % UPR) * 8;
-      const int jb = t * TJ2;
-      if (jb + jr >= clen) continue;
-      const int64_t jg = c0 + jb + jr;
-      const f32x4_t dw0 = *(const f32x4_t*)(dWs + jr * DWP + d0);
-      const f32x4_t dw1 = *(const f32x4_t*)(dWs + jr * DWP + d0 + 4);
-      const i32x4_t wv = *(const i32x4_t*)(ws + jr * WPE + d0);
-      const u32x4 rnd = rng_block(seed, step, ((uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + d0)) >> 3);
-      float tv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wb = (uint32_t)wv[e >> 1];
-        const float w = u2f((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
-        tv[e] = fmaf(-lr, e < 4 ? dw0[e] : dw1[e - 4], w);
-      }
-      uint8_t* dst = W + jg * rowbytes + (int64_t)(dsl + d0) * ESZ;
-      if constexpr (WF == W_BF16_) {
-        i32x4_t out;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = sr_bf16_into(0u, tv[2 * w], rng_pick_hi(rnd, 2 * w), false);
-          out[w] = (int)sr_bf16_into(lo, tv[2 * w + 1], rng_pick_hi(rnd, 2 * w + 1), true);
-        }
-        *(i32x4_t*)dst = out;
-      } else {
-        uint32_t o0 = 0, o1 = 0;
-        o0 = sr_e4m3_into<0>(o0, tv[0], rng_pick_hi(rnd, 0));
-        o0 = sr_e4m3_into<1>(o0, tv[1], rng_pick_hi(rnd, 1));
-        o0 = sr_e4m3_into<2>(o0, tv[2], rng_pick_hi(rnd, 2));
-        o0 = sr_e4m3_into<3>(o0, tv[3], rng_pick_hi(rnd, 3));
-        o1 = sr_e4m3_into<0>(o1, tv[4], rng_pick_hi(rnd, 4));
-        o1 = sr_e4m3_into<1>(o1, tv[5], rng_pick_hi(rnd, 5));
-        o1 = sr_e4m3_into<2>(o1, tv[6], rng_pick_hi(rnd, 6));
-        o1 = sr_e4m3_into<3>(o1, tv[7], rng_pick_hi(rnd, 7));
-        *(uint2*)dst = make_uint2(o0, o1);
-      }
-    }
+    // the next tile's operands: wait for this thread's loads (issued a whole MFMA phase ago; the
+    // previous tile's weight stores have had as long) and stage the W tile. The stores of this
+    // tile's update then overlap the next tile's MFMAs instead of being waited for here.
     if (t + 1 < t1) {
+      __builtin_amdgcn_s_waitcnt(0);
       store_w(buf ^ 1);
-      __builtin_amdgcn_s_waitcnt(0);           // this thread's G and W loads for tile t+1 landed
+    }
+
+    // fused SGD + stochastic rounding straight from the accumulators. Lane (l32, hi) holds label
+    // half*32 + l32 and features 8 (i/4) + 4 hi + i%4; swapping register groups 1<->0 and 3<->2
+    // across the two lane halves leaves features [16u + 8hi, +8) for u = 0, 1 in each lane.
+    {
+      const int jr = half * 32 + l32;
+      const int jb = t * TJ2;
+      const bool live = jb + jr < clen;
+      const int64_t jg = c0 + jb + jr;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float dw[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (copy to scalars first: bit-casting an ext-vector element reference reads element 0)
+          const float lo_v = accW[8 * u + e], hi_v = accW[8 * u + 4 + e];
+          const auto sw = __builtin_amdgcn_permlane32_swap(f2u(lo_v), f2u(hi_v), false, false);
+          dw[e] = __builtin_bit_cast(float, (uint32_t)sw[0]);
+          dw[4 + e] = __builtin_bit_cast(float, (uint32_t)sw[1]);
+        }
+        const int dl = dblk * 32 + 16 * u + 8 * hi;            // feature offset within the slice
+        const i32x4_t wv = *(const i32x4_t*)(ws + jr * WPE + dl);
+        const u32x4 rnd = rng_block(seed, step, ((uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + dl)) >> 3);
+        float tv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wb = (uint32_t)wv[e >> 1];
+          const float w = u2f((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+          tv[e] = fmaf(-lr, dw[e], w);
+        }
+        uint8_t* dst = W + jg * rowbytes + (int64_t)(dsl + dl) * ESZ;
+        if constexpr (WF == W_BF16_) {
+          i32x4_t out;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = sr_bf16_into(0u, tv[2 * w], rng_pick_hi(rnd, 2 * w), false);
+            out[w] = (int)sr_bf16_into(lo, tv[2 * w + 1], rng_pick_hi(rnd, 2 * w + 1), true);
+          }
+          if (live) *(i32x4_t*)dst = out;
+        } else {
+          uint32_t o0 = 0, o1 = 0;
+          o0 = sr_e4m3_into<0>(o0, tv[0], rng_pick_hi(rnd, 0));
+          o0 = sr_e4m3_into<1>(o0, tv[1], rng_pick_hi(rnd, 1));
+          o0 = sr_e4m3_into<2>(o0, tv[2], rng_pick_hi(rnd, 2));
+          o0 = sr_e4m3_into<3>(o0, tv[3], rng_pick_hi(rnd, 3));
+          o1 = sr_e4m3_into<0>(o1, tv[4], rng_pick_hi(rnd, 4));
+          o1 = sr_e4m3_into<1>(o1, tv[5], rng_pick_hi(rnd, 5));
+          o1 = sr_e4m3_into<2>(o1, tv[6], rng_pick_hi(rnd, 6));
+          o1 = sr_e4m3_into<3>(o1, tv[7], rng_pick_hi(rnd, 7));
+          if (live) *(uint2*)dst = make_uint2(o0, o1);
+        }
+      }
     }
   }
 
@@ -511,9 +540,12 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   if (c > Lr) c = Lr;
   s.Cc = c;
   s.ntiles = (L + TJ1 - 1) / TJ1;
+  // backward work-groups hold a whole CU (LDS) and those of one label range share an XCD: give
+  // each of the 8 XCDs at most as many work-groups as it has CUs, so the launch is one round
   int64_t nt2 = (c + TJ2 - 1) / TJ2;
-  int cap = device_cus() / s.NS;
-  if (cap < 1) cap = 1;
+  int per_xcd = (device_cus() / 8) / s.NS;
+  if (per_xcd < 1) per_xcd = 1;
+  const int cap = 8 * per_xcd;
   s.NR = (int)(nt2 < cap ? nt2 : cap);
   size_t off = 0;
   const size_t A = 256;
