@@ -23,11 +23,15 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(flo
 // ---- BF16 -------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return u2f(h << 16); }
 
-// round-to-nearest-even: add 0x7FFF plus the lowest kept bit, then truncate; NaN stays quiet NaN
+// round-to-nearest-even (v_cvt_pk_bf16_f32); NaN stays NaN
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = f2u(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// two values packed low / high
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
 // ---- OCP E4M3 (E4M3FN) --------------------------------------------------------------------------
@@ -114,9 +118,28 @@ __device__ __forceinline__ uint32_t rng_pick_hi(const u32x4& r, int e) {
 }
 
 // ---- sigmoid-BCE gradient -----------------------------------------------------------------------
-// g = sigmoid(z) - y in the cancellation-free forms 1/(1+e^-z) (y = 0) and -1/(1+e^z) (y = 1)
+// g = sigmoid(z) - y = s / (1 + e^a) with a = -z, s = 1 (y = 0) or a = z, s = -1 (y = 1): the
+// cancellation-free forms. e^a = 2^(a log2 e) with the product carried to ~48 bits so that its
+// rounding does not reach the result, v_exp_f32, one correction of the exponent's low part, then
+// v_rcp_f32 refined by one Newton step: about 2 FP32 ulp overall, close to expf + IEEE division.
+// Where the reciprocal leaves the normal range (|z| > 80) the exact-division form is used.
 __device__ __forceinline__ float bce_grad(float z, bool y) {
-  return y ? -1.0f / (1.0f + expf(z)) : 1.0f / (1.0f + expf(-z));
+  const float a = y ? z : -z;
+  float r;
+  if (__builtin_expect(__builtin_fabsf(a) > 80.0f, 0)) {
+    r = 1.0f / (1.0f + expf(a));
+  } else {
+    constexpr float L2E_HI = 1.44269502162933349609375f;       // FP32(log2 e)
+    constexpr float L2E_LO = 1.925962989e-08f;                 // log2 e - L2E_HI
+    const float p = a * L2E_HI;
+    const float pl = fmaf(a, L2E_HI, -p) + a * L2E_LO;         // p + pl = a log2 e
+    float e = __builtin_amdgcn_exp2f(p);
+    e = fmaf(e, pl * 0.693147180559945309f, e);                // e * 2^pl
+    const float d = 1.0f + e;
+    r = __builtin_amdgcn_rcpf(d);
+    r = fmaf(fmaf(-d, r, 1.0f), r, r);
+  }
+  return y ? -r : r;
 }
 
 // summed-loss term: max(z, 0) - y z + log1p(e^-|z|)

@@ -146,10 +146,8 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
   constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
   constexpr int MI = RW / 32, NI = CW / 32;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  constexpr int GP = TJ1 + 8;                  // G staging pitch in elements
-  static_assert(MB * GP * 2 <= fwd_smem_bytes(MB), "G staging must fit in the operand buffers");
   __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB)];
-  __shared__ uint32_t ybits[MB * (TJ1 / 32)];
+  __shared__ uint32_t ybits[TJ1 * (MB / 32)];    // positives, label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -160,7 +158,7 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
   const int jbase = tile * TJ1;                // first label of the tile, relative to c0
   const int64_t rowbytes = (int64_t)D * ESZ;
 
-  for (int i = tid; i < MB * (TJ1 / 32); i += 256) ybits[i] = 0u;
+  for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
   __syncthreads();
   {
     const uint64_t e0 = tile_off[tg];
@@ -168,45 +166,58 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
     for (uint64_t e = e0 + tid; e < e1; e += 256) {
       uint32_t v = bucket[e];
       uint32_t b = v >> 16, jl = v & (TJ1 - 1);
-      if (b < (uint32_t)MB) atomicOr(&ybits[b * (TJ1 / 32) + (jl >> 5)], 1u << (jl & 31));
+      if (b < (uint32_t)MB) atomicOr(&ybits[jl * (MB / 32) + (b >> 5)], 1u << (b & 31));
     }
   }
 
   f32x16_t acc[MI][NI];
   fwd_tile<MB, WF, RW, CW>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj);
 
-  // epilogue: gradient straight from the accumulators, staged in LDS for coalesced stores
-  uint16_t* Gs = (uint16_t*)smem;
+  // epilogue: gradient straight from the accumulators. A lane holds one label and 4 groups of 4
+  // consecutive samples of each 32 x 32 block; packing pairs to BF16 and swapping groups 1 <-> 0 and
+  // 3 <-> 2 across the lane halves leaves 8 consecutive samples per lane and group pair, written
+  // with one 16-byte store into the label-major chunk buffer G[label][sample].
   float lsum = 0.0f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int ni = 0; ni < NI; ++ni) {
+      const int jl = wj * CW + ni * 32 + l32;
+      const bool jvalid = jbase + jl < clen;
+      const int bb = wb * RW + mi * 32;
+      const uint32_t yw = ybits[jl * (MB / 32) + (bb >> 5)];
+      float gv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int b = wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const int jl = wj * CW + ni * 32 + l32;
+        const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+        const bool valid = jvalid && (bb + bl < B);
+        const bool y = (yw >> bl) & 1u;
         const float z = acc[mi][ni][i];
-        const bool valid = (b < B) && (jbase + jl < clen);
-        const bool y = (ybits[b * (TJ1 / 32) + (jl >> 5)] >> (jl & 31)) & 1u;
-        const uint16_t code = valid ? (uint16_t)f32_to_bf16_rne(bce_grad(z, y)) : (uint16_t)0;
+        gv[i] = valid ? bce_grad(z, y) : 0.0f;
         if constexpr (LOSS) if (valid) lsum += bce_loss(z, y);
         if constexpr (ZOUT) {
           const int64_t lab = c0 + jbase + jl;
           if (valid && lab >= zoff) {
-            if (Z) Z[(int64_t)b * zpitch + (lab - zoff)] = z;
-            if (Gout) Gout[(int64_t)b * zpitch + (lab - zoff)] = code;
+            const int64_t o = (int64_t)(bb + bl) * zpitch + (lab - zoff);
+            if (Z) Z[o] = z;
+            if (Gout) Gout[o] = (uint16_t)f32_to_bf16_rne(gv[i]);
           }
-        } else {
-          Gs[b * GP + jl] = code;
         }
       }
-  if constexpr (ZOUT) return;
-  __syncthreads();
-  for (int ci = tid; ci < MB * (TJ1 / 8); ci += 256) {
-    const int row = ci / (TJ1 / 8), part = ci % (TJ1 / 8);
-    *(i32x4_t*)(G + row * gpitch + jbase + part * 8) = *(const i32x4_t*)(Gs + row * GP + part * 8);
-  }
+      if constexpr (!ZOUT) {
+        uint32_t pk[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
+        uint16_t* grow = G + (int64_t)(jbase + jl) * gpitch;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
+          const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+          *(i32x4_t*)(grow + bb + 16 * u + 8 * hi) = out;
+        }
+      }
+    }
   if constexpr (LOSS) {
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     if (lane == 0) lred[wave] = lsum;
@@ -218,23 +229,37 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
 // ------------------------------------------------------------------------------------------------
 // backward + fused update over one d-slice and one label range of the chunk
 // ------------------------------------------------------------------------------------------------
+// LDS tiles keep rows of CPR 16-byte chunks; chunk c of row j sits at slot c ^ row_swz<CPR>(j).
+// gfx950's LDS has 64 four-byte banks: ds_read_b128 serves 16 lanes per cycle, ds_read_b64 and
+// ds_read_b64_tr_b16 32 lanes, so a read is conflict-free when each such lane group covers 256
+// distinct bytes modulo 256. The swizzle makes that hold for the two read shapes used below:
+// one chunk of 16 consecutive rows (ds_read_b128), and 4 consecutive chunks of 4 consecutive rows
+// (the 32-lane view of a transposing read), for rows of 512/256 bytes (a 4-bit XOR), 128 bytes
+// (2 rows per bank window) and 64 bytes (4 rows per window).
+template <int CPR>
+__device__ __forceinline__ int row_swz(int j) {
+  const int j0 = j & 1, j1 = (j >> 1) & 1, j2 = (j >> 2) & 1, j3 = (j >> 3) & 1;
+  if constexpr (CPR >= 16) return j2 | (j0 << 1) | (j1 << 2) | ((j0 ^ j3) << 3);
+  else if constexpr (CPR == 8) return j2 | (j3 << 1) | (j1 << 2);
+  else return j2 | (j3 << 1);
+}
+
 // Work-group: 2 * DS/32 waves (two per SIMD for DS = 128). Wave w works on the 32 features
 // [dsl + 32 (w % ND), +32) of the slice; the two waves of a feature block split the other MFMA
 // dimension (samples for dX, labels for dW) between them.
 // Per 64-label tile t (double buffered in LDS, the next tile's loads in flight during this one):
-//   G tile  [MB][64] BF16, fetched straight into LDS (global_load_lds), 16-byte chunks XOR-swizzled
-//           by row so that both the row reads (dX operand) and the transposing reads (dW operand)
-//           avoid bank conflicts;
+//   G tile  [64][MB] BF16 (label-major, as the forward kernel writes it), fetched straight into LDS
+//           with global_load_lds;
 //   W tile  [64][DS] decoded to BF16 in LDS;
-//   dX^T[d][b] += sum_j W^T[d][j] G[b][j]   (A = W^T via ds_read_b64_tr_b16, B = G rows)
-//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]   (A = stationary X^T fragments in registers, B = G^T)
+//   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]  (A = W^T and B = G^T, both by ds_read_b64_tr_b16)
+//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]    (A = stationary X^T fragments in registers, B = G rows)
 //   dW stays in the accumulators: one permlane32 swap gives every lane 2 x 8 consecutive features
 //   of one label, which it updates with one Philox block each: t = fmaf(-lr, dW, w), hardware
 //   stochastic rounding, one coalesced store per 8 weights. One barrier per tile.
 template <int MB, int WF, int DS>
 __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
                                                        const uint16_t* __restrict__ Xb,
-                                                       const uint16_t* __restrict__ G, int64_t gpitch,
+                                                       const uint16_t* __restrict__ G,
                                                        float* __restrict__ part, int NR, int NS, float lr,
                                                        uint64_t seed, uint64_t step) {
   constexpr int ND = DS / 32;                  // feature blocks
@@ -243,13 +268,14 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
   constexpr int NB = MB / 32;
   constexpr bool SPLIT_B = NB >= 2;            // dX: the two waves split samples, else split K
   constexpr int NBW = SPLIT_B ? NB / 2 : NB;   // sample blocks per wave for dX
-  constexpr int GTE = MB * TJ2;                // G tile elements (rows of 64 labels = 128 bytes)
-  constexpr int WPE = DS + 8;                  // W tile pitch (BF16 elements)
-  constexpr int WCPR = DS * ESZ / 16;          // 16-byte W chunks per tile row
+  constexpr int GTE = TJ2 * MB;                // G tile elements
+  constexpr int GCM = MB / 8 - 1;              // G row: chunk mask
+  constexpr int GRI = 512 / MB;                // G rows per 1 KiB global_load_lds instruction
+  constexpr int WCPR = DS * ESZ / 16;          // 16-byte global W chunks per tile row
   constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
   static_assert(WPT >= 1 && TJ2 == 64, "tile split");
   __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][GTE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][TJ2 * WPE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ws[2][TJ2 * DS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -277,23 +303,40 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
 
-  // loop-invariant LDS element offsets (the G swizzle only depends on the row's low 3 bits)
-  //   dX operand B, row b = ... + l32, label chunk 2 kk + hi  -> offset gB + kk-dependent chunk
-  //   dW operand B (transposing reads), rows b0 + {0..3}, labels j0 .. j0 + 3
-  const int bX0 = (SPLIT_B ? half * NBW : 0) * 32 + l32;             // + 32 nb
-  const int sX = l32 & 7;
-  const int b0W = 8 * (q >> 1) + (li >> 2);                          // + 16 kk (+ 4 for the 2nd read)
-  const int j0W = half * 32 + 16 * (q & 1) + 4 * (li & 3);
-  const int offW0 = b0W * TJ2 + (((j0W >> 3) ^ (b0W & 7)) << 3) + (j0W & 7);
-  const int offW1 = (b0W + 4) * TJ2 + (((j0W >> 3) ^ ((b0W + 4) & 7)) << 3) + (j0W & 7);
-  const int offA = (8 * (q >> 1) + (li >> 2)) * WPE + dblk * 32 + 16 * (q & 1) + 4 * (li & 3);
+  // loop-invariant LDS element offsets
+  //   dW operand B: G row j = half*32 + l32, chunk 2 kk + hi  = 2 (kk ^ gW1) + hW
+  const int jW = half * 32 + l32;
+  const int gW = row_swz<MB / 8>(jW);
+  const int offW = jW * MB + 8 * (hi ^ (gW & 1));
+  const int gW1 = gW >> 1;
+  //   dX operands (transposing reads): rows jX and jX + 4 of each 16-label K step
+  const int jX = 8 * (q >> 1) + (li >> 2);
+  const int sA0 = row_swz<DS / 8>(jX), sA1 = row_swz<DS / 8>(jX + 4);
+  const int sB0 = row_swz<MB / 8>(jX), sB1 = row_swz<MB / 8>(jX + 4);
+  const int kx0 = SPLIT_B ? 0 : half * (TJ2 / 32);
+  //     A = W^T: features dblk*32 + 16 (q&1) + 4 (li&3) .. +3
+  const int cA = 4 * dblk + 2 * (q & 1) + ((li & 3) >> 1);
+  const int offA0 = (16 * kx0 + jX) * DS + ((cA ^ sA0) << 3) + 4 * (li & 1);
+  const int offA1 = (16 * kx0 + jX + 4) * DS + ((cA ^ sA1) << 3) + 4 * (li & 1);
+  //     B = G^T: samples 32 blk + 16 (q&1) + 4 (li&3) .. +3 of sample block blk
+  int offB0[NBW], offB1[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int blk = (SPLIT_B ? half * NBW : 0) + nb;
+    const int cB = 4 * blk + 2 * (q & 1) + ((li & 3) >> 1);
+    offB0[nb] = (16 * kx0 + jX) * MB + ((cB ^ sB0) << 3) + 4 * (li & 1);
+    offB1[nb] = (16 * kx0 + jX + 4) * MB + ((cB ^ sB1) << 3) + 4 * (li & 1);
+  }
+  //   update: W row jW, chunks 4 dblk + 2u + hi
+  const int sU = row_swz<DS / 8>(jW);
+  const int offU0 = jW * DS + (((4 * dblk + hi) ^ sU) << 3);
+  const int offU1 = jW * DS + (((4 * dblk + 2 + hi) ^ sU) << 3);
 
   auto load_g = [&](int t, int buf) {
-    const int jb = t * TJ2;
+    const uint16_t* gt = G + (int64_t)t * TJ2 * MB;
     for (int inst = wave; inst < MB / 8; inst += NWV) {
-      const int row = inst * 8 + (lane >> 3), pos = lane & 7;
-      const int chunk = pos ^ (row & 7);
-      global_load_lds16(G + row * gpitch + jb + chunk * 8, &Gs[buf][inst * 512]);
+      const int row = inst * GRI + lane / (MB / 8), pos = lane & GCM;
+      global_load_lds16(gt + row * MB + ((pos ^ row_swz<MB / 8>(row)) << 3), &Gs[buf][inst * 512]);
     }
   };
   i32x4_t wst[WPT];
@@ -311,8 +354,10 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
 #pragma unroll
     for (int c = 0; c < WPT; ++c) {
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
+      const int sw = row_swz<DS / 8>(jr);
+      uint16_t* row = &Ws[buf][jr * DS];
       if constexpr (WF == W_BF16_) {
-        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 8]) = wst[c];
+        *(i32x4_t*)(row + ((p ^ sw) << 3)) = wst[c];
       } else {
         i32x4_t lo, hi4;
 #pragma unroll
@@ -323,8 +368,8 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
           if (w < 2) { lo[2 * w] = (int)p0; lo[2 * w + 1] = (int)p1; }
           else { hi4[2 * (w - 2)] = (int)p0; hi4[2 * (w - 2) + 1] = (int)p1; }
         }
-        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 16]) = lo;
-        *(i32x4_t*)(&Ws[buf][jr * WPE + p * 16 + 8]) = hi4;
+        *(i32x4_t*)(row + (((2 * p) ^ sw) << 3)) = lo;
+        *(i32x4_t*)(row + (((2 * p + 1) ^ sw) << 3)) = hi4;
       }
     }
   };
@@ -344,25 +389,20 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
 
     // The two contractions, interleaved so that the independent dX MFMAs fill the dependency gaps
     // of the dW chain, with every LDS fragment read issued two steps ahead of its MFMA:
-    //   dX^T[d][b] += W^T[d][j] G[b][j]      (M = d, N = b, K = j)   NDX MFMAs
+    //   dX^T[d][b] += W^T[d][j] G^T[j][b]    (M = d, N = b, K = j)   NDX MFMAs
     //   dW^T[d][j]  = X^T[d][b] G[b][j]      (M = d, N = j, K = b)   NDW MFMAs, one chain
     constexpr int NDW = MB / 16;
     constexpr int KXN = SPLIT_B ? TJ2 / 16 : TJ2 / 32;     // dX K steps of this wave
     constexpr int NDX = KXN * NBW;
     constexpr int NST = NDW > NDX ? NDW : NDX;
     constexpr int PF = 2;                                  // prefetch distance (steps)
-    const int kx0 = SPLIT_B ? 0 : half * KXN;
-    auto ldW = [&](int kk) {
-      return join(lds_read_tr16(gs + offW0 + kk * 16 * TJ2), lds_read_tr16(gs + offW1 + kk * 16 * TJ2));
-    };
+    auto ldW = [&](int kk) { return *(const s16x8_t*)(gs + offW + 16 * (kk ^ gW1)); };
     auto ldXa = [&](int kx) {
-      const uint16_t* pa = ws + offA + (kx0 + kx) * 16 * WPE;
-      return join(lds_read_tr16(pa), lds_read_tr16(pa + 4 * WPE));
+      return join(lds_read_tr16(ws + offA0 + kx * 16 * DS), lds_read_tr16(ws + offA1 + kx * 16 * DS));
     };
     auto ldXb = [&](int x) {
       const int kx = x / NBW, nb = x % NBW;
-      const int cx = ((2 * (kx0 + kx) + hi) ^ sX) << 3;
-      return *(const s16x8_t*)(gs + (bX0 + nb * 32) * TJ2 + cx);
+      return join(lds_read_tr16(gs + offB0[nb] + kx * 16 * MB), lds_read_tr16(gs + offB1[nb] + kx * 16 * MB));
     };
     s16x8_t fW[NST + PF], fXa[KXN + 1], fXb[NST + PF];
     f32x16_t accW = f32x16_t{};
@@ -408,7 +448,7 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
           dw[4 + e] = __builtin_bit_cast(float, (uint32_t)sw[1]);
         }
         const int dl = dblk * 32 + 16 * u + 8 * hi;            // feature offset within the slice
-        const i32x4_t wv = *(const i32x4_t*)(ws + jr * WPE + dl);
+        const i32x4_t wv = *(const i32x4_t*)(ws + (u ? offU1 : offU0));
         const u32x4 rnd = rng_block(seed, step, ((uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + dl)) >> 3);
         float tv[8];
 #pragma unroll
@@ -579,17 +619,17 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     const int nt1 = (clen + TJ1 - 1) / TJ1;
     if (a.forward_only()) {
       hipLaunchKernelGGL((k_fwd_g<MB, WF, false, true>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, a.Z, a.Gout, a.zpitch, a.zoff);
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, a.Z, a.Gout, a.zpitch, a.zoff);
       LAUNCH_CHECK();
       continue;
     }
     kt_begin(KT_FWD, st, clen);
     if (a.loss)
       hipLaunchKernelGGL((k_fwd_g<MB, WF, true, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
     else
       hipLaunchKernelGGL((k_fwd_g<MB, WF, false, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)s.Cc, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
     LAUNCH_CHECK();
     kt_end(KT_FWD, st);
     const int nt2 = (clen + TJ2 - 1) / TJ2;
@@ -598,10 +638,10 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     kt_begin(KT_BWD, st, clen);
     if (s.DS == 128)
       hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(512), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
+                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
     else
       hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, (int64_t)s.Cc, part, NR, s.NS, a.lr, a.seed, a.step);
+                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
     LAUNCH_CHECK();
     kt_end(KT_BWD, st);
   }
