@@ -38,7 +38,61 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--topk-n", type=int, default=4096)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (3 times) and exit: the "
+                         "known-size reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    """SHA-256 over the library's kernel sources: byte counters taken on other sources are stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "precision_label_chunk_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (read + write) from the committed counter summary of this
+    workload, or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fetch = write = None
+    sha = None
+    with open(path) as fh:
+        for line in fh:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "source_sha256":
+                sha = t[1]
+            elif t[0].startswith(kernel + "<") and "bytes" in t:
+                v = float(t[t.index("bytes") + 1])
+                if t[1] == "fetch_size_kib":
+                    fetch = v
+                elif t[1] == "write_size_kib":
+                    write = v
+    if sha != kernel_source_hash() or fetch is None or write is None:
+        return None
+    return {"bytes": fetch + write, "read": fetch, "write": write}
+
+
+def copy_reference(nbytes):
+    """A plain copy of `nbytes` bytes, three times: each launch reads and writes exactly nbytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def cpu_baseline(wl, W_dev, batch, target_s):
@@ -78,6 +132,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU (--gpus 1); multi-GPU runs are not part of it",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_reference(args.copy_bytes)
+        return
 
     import numpy as np
     import torch
@@ -142,9 +199,13 @@ def main():
             kern[name] = {"ms_total": ms, "launches": n, "avg_ms": ms / n, "achieved": ach, "peak": peak}
     dom = max(kern, key=lambda k: kern[k]["ms_total"])
     kd = kern[dom]
-    roofline = {"kernel": "k_bwd_update" if dom == "bwd" else "k_fwd_g", "bound": "mfma",
+    kname = "k_bwd_update" if dom == "bwd" else "k_fwd_g"
+    tr = measured_traffic(args.workload, kname)
+    roofline = {"kernel": kname, "bound": "mfma",
                 "achieved": round(kd["achieved"] / 1e12, 2), "peak": round(kd["peak"] / 1e12, 1),
-                "unit": "TFLOP/s", "frac": round(kd["achieved"] / kd["peak"], 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(kd["achieved"] / kd["peak"], 4),
+                "traffic": None if tr is None else int(tr["bytes"]),
+                "traffic_read_write": None if tr is None else [int(tr["read"]), int(tr["write"])],
                 "avg_launch_ms": round(kd["avg_ms"], 4), "launches": kd["launches"],
                 "flops_per_label": (4 if dom == "bwd" else 2) * B * D}
     other = [k for k in kern if k != dom]
