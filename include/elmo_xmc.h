@@ -45,7 +45,8 @@ typedef enum {
 enum { ELMO_W_BF16 = 0, ELMO_W_E4M3 = 1 };
 
 /* Supported shapes: 1 <= B <= 256; 64 <= D <= 1024 with D % 64 == 0; 1 <= L < 2^31;
- * chunk >= 1 (rounded down internally to a multiple of 128 labels, at least 128). */
+ * chunk >= 1 (rounded down internally to a multiple of 128 labels, at least 128, and capped so that
+ * one chunk of weight rows stays below 2 GiB). */
 #define ELMO_MAX_B 256
 #define ELMO_MAX_D 1024
 #define ELMO_MAX_TOPK 32
@@ -138,6 +139,8 @@ int elmo_xmc_kernel_timing_read(double* ms, int64_t* launches, double* labels);
  *   op 4  SR to E4M3:           in0 float[n], in1 uint32 r[n] -> out uint8[n]
  *   op 5  RNG 16-bit draws:     r16(seed, step, idx0 + i), idx0 = *(const uint64_t*)in0 (HOST) -> out uint32[n]
  *   op 6  gradient code:        in0 float z[n], in1 uint32 y[n] -> out uint16[n] (BF16(sigmoid(z) - y))
+ *   op 7  E4M3 -> BF16, 4 codes per word as the backward kernel decodes its weight tiles:
+ *                               in0 uint32[n] -> out uint32[2n] (BF16 pairs of bytes 0,1 and 2,3)
  */
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n,
                         uint64_t seed, uint64_t step, void* stream);

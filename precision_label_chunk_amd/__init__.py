@@ -203,11 +203,11 @@ def kernel_timing_read():
 def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):
     """Device codec / SR / RNG / gradient applied elementwise (test hook; see elmo_xmc.h)."""
     out_dtype = {0: torch.int16, 1: torch.uint8, 2: torch.float32, 3: torch.int16, 4: torch.uint8,
-                 5: torch.int32, 6: torch.int16}[op]
+                 5: torch.int32, 6: torch.int16, 7: torch.int32}[op]
     if n is None:
         n = in0.numel()
     dev = in0.device if in0 is not None else torch.device("cuda")
-    out = torch.empty((n,), dtype=out_dtype, device=dev)
+    out = torch.empty((2 * n if op == 7 else n,), dtype=out_dtype, device=dev)
     if op == 5:
         host = ctypes.c_uint64(idx0)
         rc = lib().elmo_numerics_probe(op, ctypes.cast(ctypes.byref(host), ctypes.c_void_p), None, _ptr(out), n,

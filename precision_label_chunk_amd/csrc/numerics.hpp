@@ -41,6 +41,13 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdg
 // E4M3 values have at most 4 significant bits and exponents inside BF16's range: exact
 __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
 
+// the four E4M3 codes in the bytes of v as BF16 codes: lo = bytes 0 | 1 << 16, hi = bytes 2 | 3 << 16
+// (gfx950's paired FP8 -> BF16 conversion with unit scale; exact, as above)
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v, 1.0f, true));
+}
+
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
   uint32_t u = f2u(x);
   uint32_t s = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
@@ -68,8 +75,9 @@ __device__ __forceinline__ uint32_t sr_bf16_into(uint32_t old, float t, uint32_t
             : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_sr_bf16_f32(o, t, rhi, false));
 }
 
+// NaN-propagating (IEEE 754-2019 maximum / minimum: v_maximum3_f32, v_minimum3_f32)
 __device__ __forceinline__ float clamp_e4m3(float t) {
-  return __builtin_fabsf(t) >= 448.0f ? __builtin_copysignf(448.0f, t) : t;   // NaN stays NaN
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(t, -448.0f), 448.0f);
 }
 
 // E4M3 SR of t into byte `sel` of `old`; rhi holds the random bits in 31..16
@@ -84,26 +92,39 @@ __device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) { return sr_e
 // ---- Philox4x32-10 ------------------------------------------------------------------------------
 struct u32x4 { uint32_t x, y, z, w; };
 
-__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+// a ^ b ^ k in one instruction (gfx950's three-input bitwise op, truth table 0x96 = parity); the
+// key k is wave-uniform
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// one Philox4x32 round with round key (k0, k1) (wave-uniform); round i of the 10 uses the key
+// (seed_lo + i * 0x9E3779B9, seed_hi + i * 0xBB67AE85)
+__device__ __forceinline__ u32x4 philox_round(u32x4 c, uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+  return u32x4{xor3_key((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
+               xor3_key((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0};
+}
+__device__ __forceinline__ uint32_t philox_key0(uint64_t seed, int i) { return (uint32_t)seed + (uint32_t)i * 0x9E3779B9u; }
+__device__ __forceinline__ uint32_t philox_key1(uint64_t seed, int i) { return (uint32_t)(seed >> 32) + (uint32_t)i * 0xBB67AE85u; }
+
+// the counter of element block g at `step`
+__device__ __forceinline__ u32x4 philox_counter(uint64_t g, uint64_t step) {
+  return u32x4{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
+}
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint64_t seed) {
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    if (i) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-    uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
-    uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    u32x4 n;
-    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
-    n.y = (uint32_t)p1;
-    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
-    n.w = (uint32_t)p0;
-    c = n;
-  }
+  for (int i = 0; i < 10; ++i) c = philox_round(c, philox_key0(seed, i), philox_key1(seed, i));
   return c;
 }
 
-// the 8 random 16-bit values of element block g = idx >> 3, packed two per word
+// the 8 random 16-bit values of element block g = idx >> 3, packed two per word (seed wave-uniform)
 __device__ __forceinline__ u32x4 rng_block(uint64_t seed, uint64_t step, uint64_t g) {
-  u32x4 c{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
-  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return philox4x32_10(philox_counter(g, step), seed);
 }
 
 __device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = idx & 7

@@ -25,6 +25,13 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
         ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_rne(bce_grad(z, y));
         break;
       }
+      case 7: {
+        uint32_t lo, hi;
+        e4m3x4_to_bf16x4(((const uint32_t*)in0)[i], lo, hi);
+        ((uint32_t*)out)[2 * i] = lo;
+        ((uint32_t*)out)[2 * i + 1] = hi;
+        break;
+      }
       default: break;
     }
   }
@@ -32,7 +39,7 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
 
 int run_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                        uint64_t step, hipStream_t st) {
-  if (op < 0 || op > 6 || n < 0 || !out) return ELMO_EINVAL_;
+  if (op < 0 || op > 7 || n < 0 || !out) return ELMO_EINVAL_;
   if (op != 5 && !in0) return ELMO_EINVAL_;
   if ((op == 3 || op == 4 || op == 6) && !in1) return ELMO_EINVAL_;
   if (n == 0) return ELMO_OK_;

@@ -17,6 +17,7 @@
 // Label handling, X preparation and the final dX reduction are small kernels around them.
 #include "step_kernels.hpp"
 
+#include <type_traits>
 #include <vector>
 
 #include "fwd_tile.hpp"
@@ -244,42 +245,126 @@ __device__ __forceinline__ int row_swz(int j) {
   else return j2 | (j3 << 1);
 }
 
-// Work-group: 2 * DS/32 waves (two per SIMD for DS = 128). Wave w works on the 32 features
-// [dsl + 32 (w % ND), +32) of the slice; the two waves of a feature block split the other MFMA
-// dimension (samples for dX, labels for dW) between them.
-// Per 64-label tile t (double buffered in LDS, the next tile's loads in flight during this one):
-//   G tile  [64][MB] BF16 (label-major, as the forward kernel writes it), fetched straight into LDS
-//           with global_load_lds;
-//   W tile  [64][DS] decoded to BF16 in LDS;
-//   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]  (A = W^T and B = G^T, both by ds_read_b64_tr_b16)
-//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]    (A = stationary X^T fragments in registers, B = G rows)
-//   dW stays in the accumulators: one permlane32 swap gives every lane 2 x 8 consecutive features
-//   of one label, which it updates with one Philox block each: t = fmaf(-lr, dW, w), hardware
-//   stochastic rounding, one coalesced store per 8 weights. One barrier per tile.
+// The fused SGD step with stochastic rounding for one wave's 32 labels x 32 features, straight
+// from its dW accumulators. Lane (l32, hi) holds label l32 and features 8 (i/4) + 4 hi + i%4 in
+// register i; swapping register groups 1<->0 and 3<->2 across the two lane halves leaves features
+// [16u + 8hi, +8) for u = 0, 1 in each lane, which it updates with one Philox block each:
+// t = fmaf(-lr, dW, w), hardware stochastic rounding, one 16- or 8-byte store per 8 weights.
+// The work is cut into UPD_PHASES phases so that it can be spread between the MFMAs of the next
+// tile: 0 swaps and RNG counters, 1..10 the Philox rounds, 11 old-weight reads, 12..19 two weights
+// each (rounding and packing; the last of each 8 also stores them).
+//   ow0/1 the old weights of those features (8 BF16 each, u = 0 / 1) in LDS
+//   roff  byte offset of the label's row in the chunk's weight resource, plus the feature offset of
+//         lane half `hi` (features dsl + dblk*32 + 8 hi)
+//   idx0  global element index of that first feature: (c0 + label) * D + feature
+constexpr int UPD_PHASES = 20;
+struct UpdState {
+  float dw[16];
+  u32x4 c[2];
+  i32x4_t ow[2];
+  uint32_t pk[4];
+};
+
+template <int WF>
+__device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& acc, const uint16_t* ow0,
+                                          const uint16_t* ow1, __amdgpu_buffer_rsrc_t wres, int roff,
+                                          uint64_t idx0, float lr, uint64_t seed, uint64_t step) {
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  if (p == 0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // (copy to scalars first: bit-casting an ext-vector element reference reads element 0)
+        const float lo_v = acc[8 * u + e], hi_v = acc[8 * u + 4 + e];
+        const auto sw = __builtin_amdgcn_permlane32_swap(f2u(lo_v), f2u(hi_v), false, false);
+        st.dw[8 * u + e] = u2f((uint32_t)sw[0]);
+        st.dw[8 * u + 4 + e] = u2f((uint32_t)sw[1]);
+      }
+      st.c[u] = philox_counter((idx0 + 16 * u) >> 3, step);
+    }
+  } else if (p <= 10) {
+    const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
+    st.c[0] = philox_round(st.c[0], k0, k1);
+    st.c[1] = philox_round(st.c[1], k0, k1);
+  } else if (p == 11) {
+    st.ow[0] = *(const i32x4_t*)ow0;
+    st.ow[1] = *(const i32x4_t*)ow1;
+  } else {
+    const int u = (p - 12) >> 2, pr = (p - 12) & 3;          // weights 2 pr, 2 pr + 1 of block u
+    const u32x4& rnd = st.c[u];
+    const uint32_t wb = (uint32_t)st.ow[u][pr];
+    const float t0 = fmaf(-lr, st.dw[8 * u + 2 * pr], u2f(wb << 16));
+    const float t1 = fmaf(-lr, st.dw[8 * u + 2 * pr + 1], u2f(wb & 0xffff0000u));
+    const int off = roff + 16 * u * ESZ;
+    if constexpr (WF == W_BF16_) {
+      const uint32_t lo = sr_bf16_into(0u, t0, rng_pick_hi(rnd, 2 * pr), false);
+      st.pk[pr] = sr_bf16_into(lo, t1, rng_pick_hi(rnd, 2 * pr + 1), true);
+      if (pr == 3)
+        buffer_store16(i32x4_t{(int)st.pk[0], (int)st.pk[1], (int)st.pk[2], (int)st.pk[3]}, wres, off);
+    } else {
+      // bytes 2 pr, 2 pr + 1 of the 8: dword pr >> 1, byte lanes 2 (pr & 1) and 2 (pr & 1) + 1
+      uint32_t o = (pr & 1) ? st.pk[pr >> 1] : 0u;
+      if (pr & 1) {
+        o = sr_e4m3_into<2>(o, t0, rng_pick_hi(rnd, 2 * pr));
+        o = sr_e4m3_into<3>(o, t1, rng_pick_hi(rnd, 2 * pr + 1));
+      } else {
+        o = sr_e4m3_into<0>(o, t0, rng_pick_hi(rnd, 2 * pr));
+        o = sr_e4m3_into<1>(o, t1, rng_pick_hi(rnd, 2 * pr + 1));
+      }
+      st.pk[pr >> 1] = o;
+      if (pr == 3) buffer_store8(i32x2_t{(int)st.pk[0], (int)st.pk[1]}, wres, off);
+    }
+  }
+}
+
+// Work-group: DS/32 waves, one per SIMD for DS = 128. Wave w owns the 32 features
+// [dsl + 32 w, +32) of the slice and does both backward contractions of every tile for them:
+//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]      two 32-label blocks, K = MB samples  (MB/8 MFMAs)
+//   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]    MB/32 sample blocks, K = 64 labels   (MB/8 MFMAs)
+// with A = stationary X^T fragments in registers (dW), B = G rows by ds_read_b128 (dW), and
+// A = W^T, B = G^T by ds_read_b64_tr_b16 (dX). Per 64-label tile t:
+//   G tile  [64][MB] BF16 (label-major, as the forward kernel writes it), double buffered in two
+//           LDS arrays used alternately by an unrolled pair of tiles; staged through registers
+//           (loaded at the start of the previous tile, written at its end) rather than with
+//           global_load_lds, whose in-flight LDS writes make the compiler drain every LDS read
+//           before each MFMA;
+//   W tile  [64][DS] decoded to BF16 in LDS, three buffers: tile t's stays intact through tile t+1,
+//           whose MFMAs its update overlaps, while tile t+2's is being staged.
+// The tile's MFMAs run in slots (dW and dX alternating), each slot's LDS operands read PFS slots
+// ahead, and the previous tile's update (2 x UPD_PHASES phases of VALU work: RNG, rounding,
+// stores) spread over the slots; a scheduling fence closes every slot so that the compiler keeps
+// this interleaving. dW never leaves the registers; one barrier per tile.
 template <int MB, int WF, int DS>
-__global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
+__global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
                                                        const uint16_t* __restrict__ Xb,
                                                        const uint16_t* __restrict__ G,
                                                        float* __restrict__ part, int NR, int NS, float lr,
                                                        uint64_t seed, uint64_t step) {
-  constexpr int ND = DS / 32;                  // feature blocks
-  constexpr int NWV = 2 * ND, NT = 64 * NWV;   // waves, threads
+  constexpr int NW = DS / 32, NT = 64 * NW;    // waves (feature blocks), threads
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  constexpr int NB = MB / 32;
-  constexpr bool SPLIT_B = NB >= 2;            // dX: the two waves split samples, else split K
-  constexpr int NBW = SPLIT_B ? NB / 2 : NB;   // sample blocks per wave for dX
+  constexpr int NB = MB / 32;                  // sample blocks
+  constexpr int KK = MB / 16;                  // dW K steps per label block
+  constexpr int NDW = 2 * KK;                  // dW MFMAs per tile
+  constexpr int KXN = TJ2 / 16;                // dX K steps
+  constexpr int NDX = KXN * NB;                // dX MFMAs per tile
+  static_assert(NDW == NDX, "slots alternate dW and dX");
+  constexpr int NSLOT = NDW + NDX;
+  constexpr int PFS = 4;                       // operand prefetch distance (slots)
   constexpr int GTE = TJ2 * MB;                // G tile elements
-  constexpr int GCM = MB / 8 - 1;              // G row: chunk mask
-  constexpr int GRI = 512 / MB;                // G rows per 1 KiB global_load_lds instruction
+  constexpr int GCPR = MB / 8;                 // 16-byte chunks per G row
+  constexpr int GPT = TJ2 * GCPR / NT;         // G chunks per thread
   constexpr int WCPR = DS * ESZ / 16;          // 16-byte global W chunks per tile row
   constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
+  constexpr int NOW = KK < 8 ? KK : 8;         // distinct dW operand offsets per lane
+  constexpr int NOB = NB < 4 ? NB : 4;         // distinct dX operand offsets per lane and row
   static_assert(WPT >= 1 && TJ2 == 64, "tile split");
-  __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][GTE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ws[2][TJ2 * DS];
+  __shared__ __attribute__((aligned(1024))) uint16_t Gs0[GTE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Gs1[GTE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ws[3][TJ2 * DS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dblk = wave % ND, half = wave / ND;
+  const int dblk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5, q = lane >> 4, li = lane & 15;
   // work-groups of one label range share its G tiles: keep them on one XCD (dispatch is round-robin)
   const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
@@ -288,223 +373,202 @@ __global__ __launch_bounds__(DS * 4) void k_bwd_update(uint8_t* __restrict__ W, 
   const int nt = (clen + TJ2 - 1) / TJ2;
   const int t0 = (int)((int64_t)nt * r / NR), t1 = (int)((int64_t)nt * (r + 1) / NR);
   const int dsl = s * DS;
-  const int64_t rowbytes = (int64_t)D * ESZ;
+  const int rowbytes = D * ESZ;
+  // the chunk's weight rows: rows past the chunk's end (the ragged last tile) load as zero and
+  // drop their stores
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)rowbytes, clen * rowbytes);
 
   // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples)
-  s16x8_t xT[MB / 16];
+  s16x8_t xT[KK];
   {
     const int d = dsl + dblk * 32 + l32;
 #pragma unroll
-    for (int kk = 0; kk < MB / 16; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) xT[kk][e] = (short)Xb[(kk * 16 + hi * 8 + e) * D + d];
   }
-  f32x16_t accX[NBW];
+  f32x16_t accX[NB];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
+  for (int nb = 0; nb < NB; ++nb) accX[nb] = f32x16_t{};
 
-  // loop-invariant LDS element offsets
-  //   dW operand B: G row j = half*32 + l32, chunk 2 kk + hi  = 2 (kk ^ gW1) + hW
-  const int jW = half * 32 + l32;
-  const int gW = row_swz<MB / 8>(jW);
-  const int offW = jW * MB + 8 * (hi ^ (gW & 1));
-  const int gW1 = gW >> 1;
+  // loop-invariant LDS element offsets (rows of both label blocks share the swizzle: it only
+  // depends on the row's low 4 bits)
+  //   dW operand B: G row jb*32 + l32, chunk 2 kk + hi  ->  16 (kk ^ gW1) + 8 (hi ^ gW0)
+  const int gW = row_swz<MB / 8>(l32);
+  int offW[NOW];
+#pragma unroll
+  for (int k = 0; k < NOW; ++k) offW[k] = l32 * MB + 8 * (hi ^ (gW & 1)) + 16 * (k ^ (gW >> 1));
   //   dX operands (transposing reads): rows jX and jX + 4 of each 16-label K step
   const int jX = 8 * (q >> 1) + (li >> 2);
-  const int sA0 = row_swz<DS / 8>(jX), sA1 = row_swz<DS / 8>(jX + 4);
-  const int sB0 = row_swz<MB / 8>(jX), sB1 = row_swz<MB / 8>(jX + 4);
-  const int kx0 = SPLIT_B ? 0 : half * (TJ2 / 32);
   //     A = W^T: features dblk*32 + 16 (q&1) + 4 (li&3) .. +3
   const int cA = 4 * dblk + 2 * (q & 1) + ((li & 3) >> 1);
-  const int offA0 = (16 * kx0 + jX) * DS + ((cA ^ sA0) << 3) + 4 * (li & 1);
-  const int offA1 = (16 * kx0 + jX + 4) * DS + ((cA ^ sA1) << 3) + 4 * (li & 1);
-  //     B = G^T: samples 32 blk + 16 (q&1) + 4 (li&3) .. +3 of sample block blk
-  int offB0[NBW], offB1[NBW];
+  const int offA0 = jX * DS + ((cA ^ row_swz<DS / 8>(jX)) << 3) + 4 * (li & 1);
+  const int offA1 = (jX + 4) * DS + ((cA ^ row_swz<DS / 8>(jX + 4)) << 3) + 4 * (li & 1);
+  //     B = G^T: samples 32 nb + 16 (q&1) + 4 (li&3) .. +3; swizzled chunk 4 (nb ^ (s>>2)) + (c ^ (s&3))
+  const int cBl = 2 * (q & 1) + ((li & 3) >> 1);
+  int offB[2][NOB];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int blk = (SPLIT_B ? half * NBW : 0) + nb;
-    const int cB = 4 * blk + 2 * (q & 1) + ((li & 3) >> 1);
-    offB0[nb] = (16 * kx0 + jX) * MB + ((cB ^ sB0) << 3) + 4 * (li & 1);
-    offB1[nb] = (16 * kx0 + jX + 4) * MB + ((cB ^ sB1) << 3) + 4 * (li & 1);
+  for (int w = 0; w < 2; ++w) {
+    const int sB = row_swz<MB / 8>(jX + 4 * w);
+#pragma unroll
+    for (int k = 0; k < NOB; ++k)
+      offB[w][k] = (jX + 4 * w) * MB + 32 * (k ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
   }
-  //   update: W row jW, chunks 4 dblk + 2u + hi
-  const int sU = row_swz<DS / 8>(jW);
-  const int offU0 = jW * DS + (((4 * dblk + hi) ^ sU) << 3);
-  const int offU1 = jW * DS + (((4 * dblk + 2 + hi) ^ sU) << 3);
+  //   update: old weights of W row jb*32 + l32, chunks 4 dblk + 2u + hi
+  const int sU = row_swz<DS / 8>(l32);
+  const int offU0 = l32 * DS + (((4 * dblk + hi) ^ sU) << 3);
+  const int offU1 = l32 * DS + (((4 * dblk + 2 + hi) ^ sU) << 3);
+  const int fU = dsl + dblk * 32 + 8 * hi;                     // this lane's first update feature
 
-  auto load_g = [&](int t, int buf) {
-    const uint16_t* gt = G + (int64_t)t * TJ2 * MB;
-    for (int inst = wave; inst < MB / 8; inst += NWV) {
-      const int row = inst * GRI + lane / (MB / 8), pos = lane & GCM;
-      global_load_lds16(gt + row * MB + ((pos ^ row_swz<MB / 8>(row)) << 3), &Gs[buf][inst * 512]);
+  // G tile: thread chunk ci = tid + c * NT is row ci / GCPR, chunk ci % GCPR (coalesced reads)
+  i32x4_t gst[GPT];
+  auto load_g = [&](int t) {
+    const i32x4_t* gt = (const i32x4_t*)(G + (int64_t)t * TJ2 * MB);
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) gst[c] = gt[tid + c * NT];
+  };
+  auto store_g = [&](uint16_t* dst) {
+#pragma unroll
+    for (int c = 0; c < GPT; ++c) {
+      const int ci = tid + c * NT, row = ci / GCPR, ch = ci % GCPR;
+      *(i32x4_t*)(dst + row * MB + ((ch ^ row_swz<MB / 8>(row)) << 3)) = gst[c];
     }
   };
   i32x4_t wst[WPT];
   auto load_w = [&](int t) {
-    const int jb = t * TJ2;
 #pragma unroll
     for (int c = 0; c < WPT; ++c) {
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
-      i32x4_t v = {0, 0, 0, 0};
-      if (jb + jr < clen) v = *(const i32x4_t*)(W + (c0 + jb + jr) * rowbytes + (int64_t)dsl * ESZ + p * 16);
-      wst[c] = v;
+      wst[c] = buffer_load16(wres, (t * TJ2 + jr) * rowbytes + dsl * ESZ + p * 16);
     }
   };
-  auto store_w = [&](int buf) {
+  auto store_w = [&](int wb) {
 #pragma unroll
     for (int c = 0; c < WPT; ++c) {
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
       const int sw = row_swz<DS / 8>(jr);
-      uint16_t* row = &Ws[buf][jr * DS];
+      uint16_t* row = &Ws[wb][jr * DS];
       if constexpr (WF == W_BF16_) {
         *(i32x4_t*)(row + ((p ^ sw) << 3)) = wst[c];
       } else {
-        i32x4_t lo, hi4;
+        uint32_t b[8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t v = (uint32_t)wst[c][w];
-          const uint32_t p0 = e4m3_to_bf16(v & 0xff) | (e4m3_to_bf16((v >> 8) & 0xff) << 16);
-          const uint32_t p1 = e4m3_to_bf16((v >> 16) & 0xff) | (e4m3_to_bf16(v >> 24) << 16);
-          if (w < 2) { lo[2 * w] = (int)p0; lo[2 * w + 1] = (int)p1; }
-          else { hi4[2 * (w - 2)] = (int)p0; hi4[2 * (w - 2) + 1] = (int)p1; }
-        }
-        *(i32x4_t*)(row + (((2 * p) ^ sw) << 3)) = lo;
-        *(i32x4_t*)(row + (((2 * p + 1) ^ sw) << 3)) = hi4;
+        for (int w = 0; w < 4; ++w) e4m3x4_to_bf16x4((uint32_t)wst[c][w], b[2 * w], b[2 * w + 1]);
+        *(i32x4_t*)(row + (((2 * p) ^ sw) << 3)) = i32x4_t{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        *(i32x4_t*)(row + (((2 * p + 1) ^ sw) << 3)) = i32x4_t{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
       }
     }
   };
 
-  if (t0 < t1) {
-    load_g(t0, 0);
-    load_w(t0);
-    store_w(0);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
+  f32x16_t accP[2];                            // previous tile's dW (two label blocks)
+  int tP = 0, wbP = 0;                         // previous tile and its W buffer
+  auto tile = [&](int t, int wb, auto gb, auto upd) {
+    constexpr bool UPD = decltype(upd)::value;
+    constexpr int GB = decltype(gb)::value;    // G buffer of this tile (compile time)
+    const int wbn = wb == 2 ? 0 : wb + 1;      // W buffer of tile t+1
     __syncthreads();                           // tile t resident; iteration t-1 fully done
-    if (t + 1 < t1) { load_g(t + 1, buf ^ 1); load_w(t + 1); }
-    const uint16_t* gs = Gs[buf];
-    const uint16_t* ws = Ws[buf];
-
-    // The two contractions, interleaved so that the independent dX MFMAs fill the dependency gaps
-    // of the dW chain, with every LDS fragment read issued two steps ahead of its MFMA:
-    //   dX^T[d][b] += W^T[d][j] G^T[j][b]    (M = d, N = b, K = j)   NDX MFMAs
-    //   dW^T[d][j]  = X^T[d][b] G[b][j]      (M = d, N = j, K = b)   NDW MFMAs, one chain
-    constexpr int NDW = MB / 16;
-    constexpr int KXN = SPLIT_B ? TJ2 / 16 : TJ2 / 32;     // dX K steps of this wave
-    constexpr int NDX = KXN * NBW;
-    constexpr int NST = NDW > NDX ? NDW : NDX;
-    constexpr int PF = 2;                                  // prefetch distance (steps)
-    auto ldW = [&](int kk) { return *(const s16x8_t*)(gs + offW + 16 * (kk ^ gW1)); };
-    auto ldXa = [&](int kx) {
+    if (t + 1 < t1) { load_g(t + 1); load_w(t + 1); }
+    const uint16_t* gs = GB ? Gs1 : Gs0;
+    const uint16_t* ws = Ws[wb];
+    auto rdW = [&](int m) {                    // dW MFMA m: label block m & 1, K step m >> 1
+      const int jb = m & 1, kk = m >> 1;
+      return *(const s16x8_t*)(gs + offW[kk % NOW] + 16 * (kk - kk % NOW) + jb * 32 * MB);
+    };
+    auto rdXa = [&](int kx) {
       return join(lds_read_tr16(ws + offA0 + kx * 16 * DS), lds_read_tr16(ws + offA1 + kx * 16 * DS));
     };
-    auto ldXb = [&](int x) {
-      const int kx = x / NBW, nb = x % NBW;
-      return join(lds_read_tr16(gs + offB0[nb] + kx * 16 * MB), lds_read_tr16(gs + offB1[nb] + kx * 16 * MB));
+    auto rdXb = [&](int m) {                   // dX MFMA m: K step m / NB, sample block m % NB
+      const int kx = m / NB, nb = m % NB, k = nb % NOB, o = 32 * (nb - k) + kx * 16 * MB;
+      return join(lds_read_tr16(gs + offB[0][k] + o), lds_read_tr16(gs + offB[1][k] + o));
     };
-    s16x8_t fW[NST + PF], fXa[KXN + 1], fXb[NST + PF];
-    f32x16_t accW = f32x16_t{};
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      if (i < NDW) fW[i] = ldW(i);
-      if (i < NDX) { if (i % NBW == 0) fXa[i / NBW] = ldXa(i / NBW); fXb[i] = ldXb(i); }
-    }
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int p = i + PF;
-      if (p < NDW) fW[p] = ldW(p);
-      if (p < NDX) { if (p % NBW == 0) fXa[p / NBW] = ldXa(p / NBW); fXb[p] = ldXb(p); }
-      if (i < NDW) accW = mfma_bf16(xT[i], fW[i], accW);
-      if (i < NDX) accX[i % NBW] = mfma_bf16(fXa[i / NBW], fXb[i], accX[i % NBW]);
-    }
-
-    // the next tile's operands: wait for this thread's loads (issued a whole MFMA phase ago; the
-    // previous tile's weight stores have had as long) and stage the W tile. The stores of this
-    // tile's update then overlap the next tile's MFMAs instead of being waited for here.
+    UpdState st;
+    const uint16_t* wsP = Ws[wbP];
+    s16x8_t opW[NDW], opXb[NDX], opXa[KXN];
+    f32x16_t accW[2] = {f32x16_t{}, f32x16_t{}};
+    // operand reads of slot z (dW for even z, dX for odd z)
+    auto fetch = [&](auto Z) {
+      constexpr int z = decltype(Z)::value, m = z >> 1;
+      if constexpr ((z & 1) == 0) {
+        opW[m] = rdW(m);
+      } else {
+        if constexpr (m % NB == 0) opXa[m / NB] = rdXa(m / NB);
+        opXb[m] = rdXb(m);
+      }
+    };
+    static_for<0, PFS>(fetch);
+    static_for<0, NSLOT>([&](auto Z) {
+      constexpr int z = decltype(Z)::value, m = z >> 1;
+      if constexpr (z + PFS < NSLOT) fetch(std::integral_constant<int, z + PFS>{});
+      if constexpr ((z & 1) == 0) accW[m & 1] = mfma_bf16(xT[m >> 1], opW[m], accW[m & 1]);
+      else accX[m % NB] = mfma_bf16(opXa[m / NB], opXb[m], accX[m % NB]);
+      if constexpr (UPD) {
+        // update phases ph with floor(ph * NSLOT / NPH) == z
+        constexpr int NPH = 2 * UPD_PHASES;
+        static_for<(z * NPH + NSLOT - 1) / NSLOT, ((z + 1) * NPH + NSLOT - 1) / NSLOT>([&](auto PH) {
+          constexpr int ph = decltype(PH)::value, jb = ph / UPD_PHASES;
+          upd_phase<WF>(ph % UPD_PHASES, st, accP[jb], wsP + offU0 + jb * 32 * DS, wsP + offU1 + jb * 32 * DS,
+                        wres, (tP * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
+                        (uint64_t)(c0 + tP * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
+        });
+      }
+      sched_fence();
+    });
+    accP[0] = accW[0];
+    accP[1] = accW[1];
+    tP = t;
+    wbP = wb;
+    // the next tile's operands: wait for this thread's loads (issued a whole MFMA phase ago) and
+    // stage the W tile. The wait is unconditional: a wait on one branch only leaves the loads
+    // pending on the other, and the compiler then waits for the next tile's prefetch before it
+    // may reuse their registers.
+    wait_all();
     if (t + 1 < t1) {
-      __builtin_amdgcn_s_waitcnt(0);
-      store_w(buf ^ 1);
+      store_g(GB ? Gs0 : Gs1);
+      store_w(wbn);
     }
+  };
 
-    // fused SGD + stochastic rounding straight from the accumulators. Lane (l32, hi) holds label
-    // half*32 + l32 and features 8 (i/4) + 4 hi + i%4; swapping register groups 1<->0 and 3<->2
-    // across the two lane halves leaves features [16u + 8hi, +8) for u = 0, 1 in each lane.
-    {
-      const int jr = half * 32 + l32;
-      const int jb = t * TJ2;
-      const bool live = jb + jr < clen;
-      const int64_t jg = c0 + jb + jr;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float dw[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (copy to scalars first: bit-casting an ext-vector element reference reads element 0)
-          const float lo_v = accW[8 * u + e], hi_v = accW[8 * u + 4 + e];
-          const auto sw = __builtin_amdgcn_permlane32_swap(f2u(lo_v), f2u(hi_v), false, false);
-          dw[e] = __builtin_bit_cast(float, (uint32_t)sw[0]);
-          dw[4 + e] = __builtin_bit_cast(float, (uint32_t)sw[1]);
-        }
-        const int dl = dblk * 32 + 16 * u + 8 * hi;            // feature offset within the slice
-        const i32x4_t wv = *(const i32x4_t*)(ws + (u ? offU1 : offU0));
-        const u32x4 rnd = rng_block(seed, step, ((uint64_t)jg * (uint64_t)D + (uint64_t)(dsl + dl)) >> 3);
-        float tv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wb = (uint32_t)wv[e >> 1];
-          const float w = u2f((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
-          tv[e] = fmaf(-lr, dw[e], w);
-        }
-        uint8_t* dst = W + jg * rowbytes + (int64_t)(dsl + dl) * ESZ;
-        if constexpr (WF == W_BF16_) {
-          i32x4_t out;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = sr_bf16_into(0u, tv[2 * w], rng_pick_hi(rnd, 2 * w), false);
-            out[w] = (int)sr_bf16_into(lo, tv[2 * w + 1], rng_pick_hi(rnd, 2 * w + 1), true);
-          }
-          if (live) *(i32x4_t*)dst = out;
-        } else {
-          uint32_t o0 = 0, o1 = 0;
-          o0 = sr_e4m3_into<0>(o0, tv[0], rng_pick_hi(rnd, 0));
-          o0 = sr_e4m3_into<1>(o0, tv[1], rng_pick_hi(rnd, 1));
-          o0 = sr_e4m3_into<2>(o0, tv[2], rng_pick_hi(rnd, 2));
-          o0 = sr_e4m3_into<3>(o0, tv[3], rng_pick_hi(rnd, 3));
-          o1 = sr_e4m3_into<0>(o1, tv[4], rng_pick_hi(rnd, 4));
-          o1 = sr_e4m3_into<1>(o1, tv[5], rng_pick_hi(rnd, 5));
-          o1 = sr_e4m3_into<2>(o1, tv[6], rng_pick_hi(rnd, 6));
-          o1 = sr_e4m3_into<3>(o1, tv[7], rng_pick_hi(rnd, 7));
-          if (live) *(uint2*)dst = make_uint2(o0, o1);
-        }
+  if (t0 < t1) {
+    using G0 = std::integral_constant<int, 0>;
+    using G1 = std::integral_constant<int, 1>;
+    load_g(t0);
+    load_w(t0);
+    wait_all();
+    store_g(Gs0);
+    store_w(0);
+    tile(t0, 0, G0{}, std::false_type{});
+    int wb = 1;
+    for (int t = t0 + 1; t < t1; t += 2) {
+      tile(t, wb, G1{}, std::true_type{});
+      wb = wb == 2 ? 0 : wb + 1;
+      if (t + 1 < t1) {
+        tile(t + 1, wb, G0{}, std::true_type{});
+        wb = wb == 2 ? 0 : wb + 1;
       }
     }
+    UpdState st;
+#pragma unroll
+    for (int ph = 0; ph < 2 * UPD_PHASES; ++ph) {
+      const int jb = ph / UPD_PHASES;
+      upd_phase<WF>(ph % UPD_PHASES, st, accP[jb], Ws[wbP] + offU0 + jb * 32 * DS, Ws[wbP] + offU1 + jb * 32 * DS,
+                    wres, (tP * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
+                    (uint64_t)(c0 + tP * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
+    }
   }
 
-  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic).
-  // With the K split (one sample block) the two waves of a feature block add in turn.
+  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic)
 #pragma unroll
-  for (int pass = 0; pass < (SPLIT_B ? 1 : 2); ++pass) {
-    if (SPLIT_B || half == pass) {
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const int b = (SPLIT_B ? half * NBW + nb : nb) * 32 + l32;
-          const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
-          f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
-          f32x4_t v = *pp;
-          v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
-          v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
-          *pp = v;
-        }
+    for (int ig = 0; ig < 4; ++ig) {
+      const int b = nb * 32 + l32;
+      const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
+      f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
+      f32x4_t v = *pp;
+      v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
+      v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
+      *pp = v;
     }
-    if (!SPLIT_B && pass == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -578,6 +642,10 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   int64_t c = chunk - chunk % TJ1;
   if (c < TJ1) c = TJ1;
   if (c > Lr) c = Lr;
+  // chunk-relative 32-bit byte offsets into the chunk's weight rows (one tile of slack)
+  const int64_t rb = (int64_t)D * (wdtype == W_E4M3_ ? 1 : 2);
+  const int64_t cmax = ((int64_t)0x7fffffff / rb - TJ1) / TJ1 * TJ1;
+  if (c > cmax) c = cmax;
   s.Cc = c;
   s.ntiles = (L + TJ1 - 1) / TJ1;
   // backward work-groups hold a whole CU (LDS) and those of one label range share an XCD: give
@@ -637,10 +705,10 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     const int grid2 = 8 * s.NS * ((NR + 7) / 8);
     kt_begin(KT_BWD, st, clen);
     if (s.DS == 128)
-      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(512), 0, st, W, a.D, c0, clen,
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
                          (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
     else
-      hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(128), 0, st, W, a.D, c0, clen,
                          (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
     LAUNCH_CHECK();
     kt_end(KT_BWD, st);

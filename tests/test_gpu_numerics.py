@@ -58,21 +58,40 @@ def test_e4m3_decode_every_code(elmo, orc):
     assert np.all((got == ref) | both_nan) and np.isnan(got).sum() == 2
 
 
+def test_e4m3_to_bf16_pairs_every_code(elmo, orc):
+    """The paired decode the backward kernel stages its weight tiles with: every code in every byte."""
+    c = np.arange(256, dtype=np.uint32)
+    words = np.concatenate([c, c << 8, c << 16, c << 24, c | (c[::-1] << 8) | (c << 16) | (c[::-1] << 24)])
+    got = elmo.numerics_probe(7, _dev(words.astype(np.uint32).view(np.int32))).cpu().numpy().view(np.uint32)
+    codes = np.stack([(words >> (8 * k)) & 0xFF for k in range(4)], axis=1).astype(np.uint8)
+    val = orc.e4m3_value(codes.ravel()).astype(np.float32)
+    ref16 = torch.from_numpy(val).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).reshape(-1, 4)
+    g16 = np.stack([got[0::2] & 0xFFFF, got[0::2] >> 16, got[1::2] & 0xFFFF, got[1::2] >> 16], axis=1)
+    nan = np.isnan(val.reshape(-1, 4))
+    assert np.array_equal(g16[~nan], ref16[~nan].astype(np.uint32))
+    assert np.all((g16[nan] & 0x7FFF) > 0x7F80)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
 def test_stochastic_rounding_bit_exact(elmo, orc, fmt):
     g = np.random.default_rng(4)
     n = 400000
     t = np.concatenate([(g.standard_normal(n) * 0.05), g.standard_normal(n // 4) * 10.0 ** g.uniform(-9, 2.7, n // 4),
-                        [447.9, 448.0, 500.0, -1e9, 1e-45, -1e-40, 0.0, -0.0, 2.0**-6, 2.0**-9 * 0.5]]).astype(np.float32)
+                        [447.9, 448.0, 500.0, -1e9, 1e-45, -1e-40, 0.0, -0.0, 2.0**-6, 2.0**-9 * 0.5],
+                        [np.inf, -np.inf, np.nan, -np.nan, 3e38, -3e38]]).astype(np.float32)
     r = g.integers(0, 65536, t.size).astype(np.uint32)
     r[:1000] = 0; r[1000:2000] = 65535
     op = 3 if fmt == "bf16" else 4
     got = elmo.numerics_probe(op, _dev(t), _dev(r)).cpu().numpy()
     if fmt == "bf16":
         got = got.view(np.uint16); ref = orc.sr_bf16(t, r)
+        nan_g = (got & 0x7FFF) > 0x7F80; nan_r = (ref & 0x7FFF) > 0x7F80
     else:
         ref = orc.sr_e4m3(t, r)
-    assert np.array_equal(got, ref)
+        nan_g = (got & 0x7F) == 0x7F; nan_r = (ref & 0x7F) == 0x7F
+    # a NaN input gives a NaN code (its sign and payload are not specified); everything else is exact
+    assert np.array_equal(nan_g, nan_r) and nan_r.sum() == 2
+    assert np.array_equal(got[~nan_r], ref[~nan_r])
 
 
 @pytest.mark.parametrize("seed,step,idx0", [(0, 0, 0), (12345, 7, 3), (2**63 + 5, 2**40 + 1, 6_600_000_000 - 77)])
