@@ -420,31 +420,30 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
   const int offU1 = l32 * DS + (((4 * dblk + 2 + hi) ^ sU) << 3);
   const int fU = dsl + dblk * 32 + 8 * hi;                     // this lane's first update feature
 
-  // G tile: thread chunk ci = tid + c * NT is row ci / GCPR, chunk ci % GCPR (coalesced reads)
-  i32x4_t gst[GPT];
-  auto load_g = [&](int t) {
-    const i32x4_t* gt = (const i32x4_t*)(G + (int64_t)t * TJ2 * MB);
-#pragma unroll
-    for (int c = 0; c < GPT; ++c) gst[c] = gt[tid + c * NT];
-  };
-  auto store_g = [&](uint16_t* dst) {
-#pragma unroll
-    for (int c = 0; c < GPT; ++c) {
-      const int ci = tid + c * NT, row = ci / GCPR, ch = ci % GCPR;
-      *(i32x4_t*)(dst + row * MB + ((ch ^ row_swz<MB / 8>(row)) << 3)) = gst[c];
-    }
-  };
-  i32x4_t wst[WPT];
-  auto load_w = [&](int t) {
-#pragma unroll
-    for (int c = 0; c < WPT; ++c) {
+  // Staging of the next tile through registers, one 16-byte chunk per item: items 0 .. GPT-1 are
+  // G chunks (thread chunk ci = tid + c * NT is row ci / GCPR, chunk ci % GCPR: coalesced reads),
+  // then WPT weight chunks (row ci / WCPR, 16-byte part ci % WCPR). The loads are spread over the
+  // first half of a tile's MFMA slots and the LDS writes over the second half, so that neither a
+  // burst of loads stalls the wave at the memory queue nor the wait for them sits between tiles.
+  constexpr int NLD = GPT + WPT;
+  i32x4_t gst[GPT], wst[WPT];
+  auto load_item = [&](auto K, int tn) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < GPT) {
+      gst[k] = ((const i32x4_t*)(G + (int64_t)tn * TJ2 * MB))[tid + k * NT];
+    } else {
+      constexpr int c = k - GPT;
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
-      wst[c] = buffer_load16(wres, (t * TJ2 + jr) * rowbytes + dsl * ESZ + p * 16);
+      wst[c] = buffer_load16(wres, (tn * TJ2 + jr) * rowbytes + dsl * ESZ + p * 16);
     }
   };
-  auto store_w = [&](int wb) {
-#pragma unroll
-    for (int c = 0; c < WPT; ++c) {
+  auto store_item = [&](auto K, uint16_t* gdst, int wb) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < GPT) {
+      const int ci = tid + k * NT, row = ci / GCPR, ch = ci % GCPR;
+      *(i32x4_t*)(gdst + row * MB + ((ch ^ row_swz<MB / 8>(row)) << 3)) = gst[k];
+    } else {
+      constexpr int c = k - GPT;
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
       const int sw = row_swz<DS / 8>(jr);
       uint16_t* row = &Ws[wb][jr * DS];
@@ -466,8 +465,10 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     constexpr bool UPD = decltype(upd)::value;
     constexpr int GB = decltype(gb)::value;    // G buffer of this tile (compile time)
     const int wbn = wb == 2 ? 0 : wb + 1;      // W buffer of tile t+1
+    // the next tile (on the range's last tile, a repeat of a valid tile: the staging is then unused)
+    const int tn = t + 1 < nt ? t + 1 : nt - 1;
+    uint16_t* gnext = GB ? Gs0 : Gs1;
     __syncthreads();                           // tile t resident; iteration t-1 fully done
-    if (t + 1 < t1) { load_g(t + 1); load_w(t + 1); }
     const uint16_t* gs = GB ? Gs1 : Gs0;
     const uint16_t* ws = Ws[wb];
     auto rdW = [&](int m) {                    // dW MFMA m: label block m & 1, K step m >> 1
@@ -499,6 +500,11 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     static_for<0, NSLOT>([&](auto Z) {
       constexpr int z = decltype(Z)::value, m = z >> 1;
       if constexpr (z + PFS < NSLOT) fetch(std::integral_constant<int, z + PFS>{});
+      constexpr int HALF = NSLOT / 2;
+      static_for<0, NLD>([&](auto K) {
+        if constexpr (decltype(K)::value * HALF / NLD == z) load_item(K, tn);
+        if constexpr (HALF + decltype(K)::value * HALF / NLD == z) store_item(K, gnext, wbn);
+      });
       if constexpr ((z & 1) == 0) accW[m & 1] = mfma_bf16(xT[m >> 1], opW[m], accW[m & 1]);
       else accX[m % NB] = mfma_bf16(opXa[m / NB], opXb[m], accX[m % NB]);
       if constexpr (UPD) {
@@ -517,25 +523,13 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     accP[1] = accW[1];
     tP = t;
     wbP = wb;
-    // the next tile's operands: wait for this thread's loads (issued a whole MFMA phase ago) and
-    // stage the W tile. The wait is unconditional: a wait on one branch only leaves the loads
-    // pending on the other, and the compiler then waits for the next tile's prefetch before it
-    // may reuse their registers.
-    wait_all();
-    if (t + 1 < t1) {
-      store_g(GB ? Gs0 : Gs1);
-      store_w(wbn);
-    }
   };
 
   if (t0 < t1) {
     using G0 = std::integral_constant<int, 0>;
     using G1 = std::integral_constant<int, 1>;
-    load_g(t0);
-    load_w(t0);
-    wait_all();
-    store_g(Gs0);
-    store_w(0);
+    static_for<0, NLD>([&](auto K) { load_item(K, t0); });
+    static_for<0, NLD>([&](auto K) { store_item(K, Gs0, 0); });
     tile(t0, 0, G0{}, std::false_type{});
     int wb = 1;
     for (int t = t0 + 1; t < t1; t += 2) {
