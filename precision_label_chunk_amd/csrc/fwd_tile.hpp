@@ -2,101 +2,121 @@
 // training step's forward kernel and the top-k scoring kernel:
 //   acc[b][j] = sum_k Xf[b][k] * W[j][k]
 // with Xf the zero-padded feature rows (BF16, or E4M3 for E4M3 weights) and W the tile's weight
-// rows (rows at or beyond `nvalid` read as zero). Operands are staged through LDS in 128-byte K
-// slices, double buffered, with the next slice's global loads in flight during this slice's MFMAs.
+// rows (rows at or beyond `nvalid` read as zero). Operands are staged through LDS in K slices of
+// KS bytes of every row (two LDS stages). Each slice's global loads are issued two slices ahead,
+// spread over the MFMA slots of the slice before the one whose end writes them to LDS, so that
+// neither a burst of loads stalls the wave at the memory queue nor the loads' latency sits
+// between slices; MFMA operands are read from LDS one slot ahead of their use.
 #pragma once
+#include <type_traits>
+
 #include "mfma.hpp"
 #include "step_kernels.hpp"
 
 namespace elmo {
 
-constexpr int fwd_smem_bytes(int MB) { return 2 * (MB + TJ1) * P1; }
+constexpr int fwd_pitch(int KS) { return KS + 16; }     // LDS row pitch: conflict-free 16-row reads
+constexpr int fwd_smem_bytes(int MB, int KS) { return 2 * (MB + TJ1) * fwd_pitch(KS); }
 
 // RW x CW is this wave's sub-tile (RW samples, CW labels); the work-group is (MB/RW) x (TJ1/CW) waves
-template <int MB, int WF, int RW, int CW>
+template <int MB, int WF, int RW, int CW, int KS>
 __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint8_t* smem,
                                          const uint8_t* __restrict__ Wt, int nvalid,
                                          const uint8_t* __restrict__ Xf, int64_t rowbytes, int tid, int wb,
                                          int wj) {
   constexpr int MI = RW / 32, NI = CW / 32;
-  constexpr int SLICE = (MB + TJ1) * P1;
-  constexpr int CPT = (MB + TJ1) * (KSB / 16) / 256;
-  static_assert((MB + TJ1) * (KSB / 16) % 256 == 0, "slice split");
+  constexpr int PT = fwd_pitch(KS);
+  constexpr int SLICE = (MB + TJ1) * PT;
+  constexpr int PPR = KS / 16;                           // 16-byte parts per row and slice
+  constexpr int NCH = (MB + TJ1) * PPR;                  // chunks per slice
+  constexpr int CPT = (NCH + 255) / 256;                 // chunks per thread
+  constexpr int KSTEP = WF == W_BF16_ ? 32 : 64;         // K bytes per MFMA
+  constexpr int NKK = KS / KSTEP;                        // MFMA K steps per slice
+  constexpr int NSL = NKK * MI * NI;                     // MFMA slots per slice
+  static_assert(KS % KSTEP == 0, "slice holds whole MFMA K steps");
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int nks = (int)((rowbytes + KSB - 1) / KSB);
+  const int nks = (int)((rowbytes + KS - 1) / KS);
 
-  i32x4_t stg[CPT];
-  auto gload = [&](int ks) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * 256, row = ci >> 3, part = ci & 7;
-      const int64_t boff = (int64_t)ks * KSB + part * 16;
-      i32x4_t v = {0, 0, 0, 0};
-      if (boff < rowbytes) {
-        if (row < MB) v = *(const i32x4_t*)(Xf + row * rowbytes + boff);
-        else if (row - MB < nvalid) v = *(const i32x4_t*)(Wt + (int64_t)(row - MB) * rowbytes + boff);
-      }
-      stg[c] = v;
+  // chunk c of this thread: ci = tid + 256 c, row ci / PPR (X rows, then W rows), part ci % PPR
+  i32x4_t stg[2][CPT];
+  auto gload = [&](auto S, auto K, int ks) {
+    constexpr int c = decltype(K)::value;
+    const int ci = tid + 256 * c, row = ci / PPR, part = ci % PPR;
+    const int64_t boff = (int64_t)ks * KS + part * 16;
+    i32x4_t v = {0, 0, 0, 0};
+    if ((c + 1 < CPT || ci < NCH) && ks < nks && boff < rowbytes) {
+      if (row < MB) v = *(const i32x4_t*)(Xf + row * rowbytes + boff);
+      else if (row - MB < nvalid) v = *(const i32x4_t*)(Wt + (int64_t)(row - MB) * rowbytes + boff);
     }
+    stg[decltype(S)::value][c] = v;
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * 256, row = ci >> 3, part = ci & 7;
-      *(i32x4_t*)(smem + buf * SLICE + row * P1 + part * 16) = stg[c];
-    }
+  auto lstore = [&](auto S, int buf) {
+    static_for<0, CPT>([&](auto K) {
+      constexpr int c = decltype(K)::value;
+      const int ci = tid + 256 * c;
+      if (c + 1 < CPT || ci < NCH)
+        *(i32x4_t*)(smem + buf * SLICE + (ci / PPR) * PT + (ci % PPR) * 16) = stg[decltype(S)::value][c];
+    });
   };
 
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+  static_for<0, MI * NI>([&](auto I) { acc[decltype(I)::value / NI][decltype(I)::value % NI] = f32x16_t{}; });
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
-    const uint8_t* Xs = smem + buf * SLICE;
-    const uint8_t* Ws = Xs + MB * P1;
+  using Frag = typename std::conditional<WF == W_BF16_, s16x8_t, i32x8_t>::type;
+  auto rdfrag = [&](const uint8_t* base, int row, int kk) -> Frag {
+    const uint8_t* p = base + row * PT + kk * KSTEP + hi * (KSTEP / 2);
     if constexpr (WF == W_BF16_) {
-#pragma unroll
-      for (int kk = 0; kk < KSB / 32; ++kk) {
-        s16x8_t a[MI], b[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) a[mi] = *(const s16x8_t*)(Xs + (wb * RW + mi * 32 + l32) * P1 + kk * 32 + hi * 16);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) b[ni] = *(const s16x8_t*)(Ws + (wj * CW + ni * 32 + l32) * P1 + kk * 32 + hi * 16);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_bf16(a[mi], b[ni], acc[mi][ni]);
-      }
+      return *(const s16x8_t*)p;
     } else {
-#pragma unroll
-      for (int kk = 0; kk < KSB / 64; ++kk) {
-        i32x8_t a[MI], b[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const uint8_t* p = Xs + (wb * RW + mi * 32 + l32) * P1 + kk * 64 + hi * 32;
-          const i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
-          a[mi] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const uint8_t* p = Ws + (wj * CW + ni * 32 + l32) * P1 + kk * 64 + hi * 32;
-          const i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
-          b[ni] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_e4m3(a[mi], b[ni], acc[mi][ni]);
-      }
+      const i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
+      return i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
-    if (ks + 1 < nks) lstore(buf ^ 1);
+  };
+
+  // slice ks from LDS stage ks & 1 (parity S = ks & 1 at compile time): its MFMAs, with the loads of
+  // slice ks + 2 (into staging set S) spread over its slots, then slice ks + 1 (staging set S ^ 1,
+  // loaded during slice ks - 1) written to the other LDS stage
+  auto slice = [&](auto S, int ks) {
+    constexpr int SP = decltype(S)::value;
+    const uint8_t* Xs = smem + SP * SLICE;
+    const uint8_t* Ws = Xs + MB * PT;
+    Frag fa[NKK][MI], fb[NKK][NI];
+    auto fetch = [&](auto Z) {                           // operands first used at slot Z + 1 (or Z = 0)
+      constexpr int z = decltype(Z)::value;
+      static_for<0, NKK * MI>([&](auto I) {
+        constexpr int kk = decltype(I)::value / MI, mi = decltype(I)::value % MI;
+        constexpr int f = (kk * MI + mi) * NI - 1;
+        if constexpr ((f < 0 ? 0 : f) == z) fa[kk][mi] = rdfrag(Xs, wb * RW + mi * 32 + l32, kk);
+      });
+      static_for<0, NKK * NI>([&](auto I) {
+        constexpr int kk = decltype(I)::value / NI, ni = decltype(I)::value % NI;
+        constexpr int f = kk * MI * NI + ni - 1;
+        if constexpr ((f < 0 ? 0 : f) == z) fb[kk][ni] = rdfrag(Ws, wj * CW + ni * 32 + l32, kk);
+      });
+    };
+    static_for<0, NSL>([&](auto Z) {
+      constexpr int z = decltype(Z)::value;
+      constexpr int kk = z / (MI * NI), mi = (z / NI) % MI, ni = z % NI;
+      fetch(Z);
+      static_for<0, CPT>([&](auto K) {
+        if constexpr (decltype(K)::value * NSL / CPT == z) gload(S, K, ks + 2);
+      });
+      if constexpr (WF == W_BF16_) acc[mi][ni] = mfma_bf16(fa[kk][mi], fb[kk][ni], acc[mi][ni]);
+      else acc[mi][ni] = mfma_e4m3(fa[kk][mi], fb[kk][ni], acc[mi][ni]);
+      sched_fence();
+    });
+    if (ks + 1 < nks) lstore(std::integral_constant<int, SP ^ 1>{}, SP ^ 1);
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  static_for<0, CPT>([&](auto K) { gload(S0{}, K, 0); });
+  static_for<0, CPT>([&](auto K) { gload(S1{}, K, 1); });
+  lstore(S0{}, 0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ks += 2) {
+    slice(S0{}, ks);
+    if (ks + 1 < nks) slice(S1{}, ks + 1);
   }
 }
 

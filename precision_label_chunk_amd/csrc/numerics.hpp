@@ -144,23 +144,30 @@ __device__ __forceinline__ uint32_t rng_pick_hi(const u32x4& r, int e) {
 // rounding does not reach the result, v_exp_f32, one correction of the exponent's low part, then
 // v_rcp_f32 refined by one Newton step: about 2 FP32 ulp overall, close to expf + IEEE division.
 // Where the reciprocal leaves the normal range (|z| > 80) the exact-division form is used.
-__device__ __forceinline__ float bce_grad(float z, bool y) {
+// the fast form, valid for |z| <= 80
+__device__ __forceinline__ float bce_grad_fast(float z, bool y) {
   const float a = y ? z : -z;
-  float r;
-  if (__builtin_expect(__builtin_fabsf(a) > 80.0f, 0)) {
-    r = 1.0f / (1.0f + expf(a));
-  } else {
-    constexpr float L2E_HI = 1.44269502162933349609375f;       // FP32(log2 e)
-    constexpr float L2E_LO = 1.925962989e-08f;                 // log2 e - L2E_HI
-    const float p = a * L2E_HI;
-    const float pl = fmaf(a, L2E_HI, -p) + a * L2E_LO;         // p + pl = a log2 e
-    float e = __builtin_amdgcn_exp2f(p);
-    e = fmaf(e, pl * 0.693147180559945309f, e);                // e * 2^pl
-    const float d = 1.0f + e;
-    r = __builtin_amdgcn_rcpf(d);
-    r = fmaf(fmaf(-d, r, 1.0f), r, r);
-  }
+  constexpr float L2E_HI = 1.44269502162933349609375f;         // FP32(log2 e)
+  constexpr float L2E_LO = 1.925962989e-08f;                   // log2 e - L2E_HI
+  const float p = a * L2E_HI;
+  const float pl = fmaf(a, L2E_HI, -p) + a * L2E_LO;           // p + pl = a log2 e
+  float e = __builtin_amdgcn_exp2f(p);
+  e = fmaf(e, pl * 0.693147180559945309f, e);                  // e * 2^pl
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = fmaf(fmaf(-d, r, 1.0f), r, r);
   return y ? -r : r;
+}
+
+// the exact-division form, for |z| > 80
+__device__ __forceinline__ float bce_grad_slow(float z, bool y) {
+  const float r = 1.0f / (1.0f + expf(y ? z : -z));
+  return y ? -r : r;
+}
+
+__device__ __forceinline__ float bce_grad(float z, bool y) {
+  if (__builtin_expect(__builtin_fabsf(z) > 80.0f, 0)) return bce_grad_slow(z, y);
+  return bce_grad_fast(z, y);
 }
 
 // summed-loss term: max(z, 0) - y z + log1p(e^-|z|)

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* __restrict__ l
 // forward + gradient: Z = X~ W_c^T, G = BF16(sigmoid(Z) - Y)
 // ------------------------------------------------------------------------------------------------
 template <int MB, int WF, bool LOSS, bool ZOUT>
-__global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
+__global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
                                                int D, int64_t c0, int clen,
                                                const uint32_t* __restrict__ tile_off,
                                                const uint32_t* __restrict__ bucket, int64_t bucket_cap,
@@ -147,7 +147,8 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
   constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
   constexpr int MI = RW / 32, NI = CW / 32;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB)];
+  constexpr int KS = 64;                       // K slice: small enough for two work-groups per CU
+  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
   __shared__ uint32_t ybits[TJ1 * (MB / 32)];    // positives, label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[4];
 
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void k_fwd_g(const uint8_t* __restrict__ W, co
   }
 
   f32x16_t acc[MI][NI];
-  fwd_tile<MB, WF, RW, CW>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj);
+  fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj);
 
   // epilogue: gradient straight from the accumulators. A lane holds one label and 4 groups of 4
   // consecutive samples of each 32 x 32 block; packing pairs to BF16 and swapping groups 1 <-> 0 and
@@ -645,7 +646,8 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   // backward work-groups hold a whole CU (LDS) and those of one label range share an XCD: give
   // each of the 8 XCDs at most as many work-groups as it has CUs, so the launch is one round
   int64_t nt2 = (c + TJ2 - 1) / TJ2;
-  int per_xcd = (device_cus() / 8) / s.NS;
+  s.cus = device_cus();
+  int per_xcd = (s.cus / 8) / s.NS;
   if (per_xcd < 1) per_xcd = 1;
   const int cap = 8 * per_xcd;
   s.NR = (int)(nt2 < cap ? nt2 : cap);

@@ -14,11 +14,10 @@ constexpr uint32_t ELMO_FLAG_LABEL_RANGE_ = 1u, ELMO_FLAG_ROW_PTR_ = 2u;
 
 constexpr int TJ1 = 128;       // labels per forward tile (and label-bucket granularity)
 constexpr int TJ2 = 64;        // labels per backward tile
-constexpr int KSB = 128;       // bytes of each operand row staged per K slice in the forward kernel
-constexpr int P1 = KSB + 16;   // LDS row pitch of the staged slices
 
 struct StepLayout {
   int MB, DS, NS, NR;
+  int cus;                              // compute units of the device
   int64_t Cc, ntiles;
   size_t flags, tile_cnt, tile_off, bucket, xb, xq, g, part, loss, total;
 };

@@ -48,8 +48,9 @@ __global__ __launch_bounds__(256) void k_topk_scan(const uint8_t* __restrict__ W
   constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int SP = TJ1 + 4;           // score tile pitch (floats)
-  static_assert(MB * SP * 4 <= fwd_smem_bytes(MB), "score staging fits in the operand buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB)];
+  constexpr int KS = 128;
+  static_assert(MB * SP * 4 <= fwd_smem_bytes(MB, KS), "score staging fits in the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wb = wave >> 1, wj = wave & 1, l32 = lane & 31, hi = lane >> 5;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void k_topk_scan(const uint8_t* __restrict__ W
     const int64_t j0 = t * TJ1;
     const int nvalid = (int)((L - j0) < TJ1 ? (L - j0) : TJ1);
     f32x16_t acc[MI][NI];
-    fwd_tile<MB, WF, RW, CW>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj);
+    fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
