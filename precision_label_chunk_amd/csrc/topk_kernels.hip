@@ -42,15 +42,15 @@ __device__ __forceinline__ void list_init(float (&ls)[KK], int (&lj)[KK]) {
 }
 
 template <int WF, int KK>
-__global__ __launch_bounds__(256) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
+__global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
                                                    const uint8_t* __restrict__ Xf, int nbn, int NRg,
                                                    float* __restrict__ cs, int* __restrict__ ci) {
   constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int SP = TJ1 + 4;           // score tile pitch (floats)
-  constexpr int KS = 128;
-  static_assert(MB * SP * 4 <= fwd_smem_bytes(MB, KS), "score staging fits in the operand buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
+  constexpr int KS = 64;
+  constexpr int SMEM = MB * SP * 4 > fwd_smem_bytes(MB, KS) ? MB * SP * 4 : fwd_smem_bytes(MB, KS);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];   // operand stages, then the score tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wb = wave >> 1, wj = wave & 1, l32 = lane & 31, hi = lane >> 5;
