@@ -69,12 +69,15 @@ def lib():
                                  ctypes.c_int, P, ctypes.c_int]
         L.orc_update_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
                                       ctypes.c_float, u64, u64, P, ctypes.c_int, P, ctypes.c_int]
+        L.orc_update_rows_from_g.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P,
+                                             ctypes.c_float, u64, u64, P, ctypes.c_int, P, ctypes.c_int]
         L.orc_dx_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P, P,
                                   ctypes.c_int, P, ctypes.c_int]
         L.orc_grad_exact.argtypes = [i64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P]
         L.orc_topk.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                P, P, ctypes.c_int]
-        for name in ("orc_step", "orc_update_from_g", "orc_logits", "orc_update_rows", "orc_dx_rows", "orc_grad_exact",
+        for name in ("orc_step", "orc_update_from_g", "orc_logits", "orc_update_rows", "orc_update_rows_from_g",
+                     "orc_dx_rows", "orc_grad_exact",
                      "orc_topk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -190,6 +193,17 @@ def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0):
     _chk(lib().orc_update_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
                                float(lr), seed, step_, _p(js), js.size, _p(out), nthreads),
          "update_rows")
+    return out
+
+
+def update_rows_from_g(wfmt, W, X, G, lr, seed, step_, js, nthreads=0):
+    """Updated codes of weight rows js given the gradient codes G [B][len(js)] of those labels."""
+    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    js = _c(js, np.int64); G = _c(G, np.uint16)
+    assert G.shape == (B, js.size)
+    out = np.empty((js.size, D), wdtype_np(wfmt))
+    _chk(lib().orc_update_rows_from_g(wfmt, _p(W), L, D, _p(X), B, _p(G), float(lr), seed, step_, _p(js), js.size,
+                                      _p(out), nthreads), "update_rows_from_g")
     return out
 
 

@@ -384,6 +384,19 @@ int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int
   return ORC_OK;
 }
 
+/* Row j's update given its gradient values g[b] (BF16 values): dW_jk = FP32(sum_b g_b x_bk), summed
+ * in binary64 over b ascending; t = fmaf(-lr, dW, w); SR with the draw of element j*D + k; output
+ * row i of Wrows. */
+static void update_row(int wfmt, const void* W, int64_t j, int D, const double* xb, const double* g, int B,
+                       float lr, uint64_t seed, uint64_t step, void* Wrows, int i) {
+  for (int k = 0; k < D; k++) {
+    double s = 0.0;
+    for (int b = 0; b < B; b++) s += g[b] * xb[(int64_t)b * D + k];
+    store_update(wfmt, Wrows, (int64_t)i * D + k, wval(wfmt, W, j, D, k), (float)s, lr, seed, step,
+                 (uint64_t)(j * (int64_t)D + k));
+  }
+}
+
 int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                     const int32_t* row_ptr, const int32_t* ids, float lr, uint64_t seed,
                     uint64_t step, const int64_t* js, int nj, void* Wrows, int nthreads) {
@@ -403,15 +416,31 @@ int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X
     double* g = (double*)malloc(sizeof(double) * (size_t)B);
     for (int b = 0; b < B; b++)
       g[b] = orc_bf16_value(orc_grad_code(logit(wfmt, W, j, D, xt + (int64_t)b * D), has_label(&ls, b, j)));
-    for (int k = 0; k < D; k++) {
-      double s = 0.0;
-      for (int b = 0; b < B; b++) s += g[b] * xb[(int64_t)b * D + k];
-      store_update(wfmt, Wrows, (int64_t)i * D + k, wval(wfmt, W, j, D, k), (float)s, lr, seed, step,
-                   (uint64_t)(j * (int64_t)D + k));
-    }
+    update_row(wfmt, W, j, D, xb, g, B, lr, seed, step, Wrows, i);
     free(g);
   }
   free(xt); free(xb); labelsets_free(&ls);
+  return ORC_OK;
+}
+
+int orc_update_rows_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
+                           const uint16_t* G, float lr, uint64_t seed, uint64_t step, const int64_t* js,
+                           int nj, void* Wrows, int nthreads) {
+  int rc = check_common(wfmt, W, L, D, X, B);
+  if (rc) return rc;
+  if (!G || !js || !Wrows || nj < 0) return ORC_EINVAL;
+  for (int i = 0; i < nj; i++) if (js[i] < 0 || js[i] >= L) return ORC_EINVAL;
+  set_threads(nthreads);
+  double* xb = backward_x(X, B, D);
+  if (!xb) return ORC_ENOMEM;
+  #pragma omp parallel for schedule(static)
+  for (int i = 0; i < nj; i++) {
+    double* g = (double*)malloc(sizeof(double) * (size_t)B);
+    for (int b = 0; b < B; b++) g[b] = orc_bf16_value(G[(int64_t)b * nj + i]);
+    update_row(wfmt, W, js[i], D, xb, g, B, lr, seed, step, Wrows, i);
+    free(g);
+  }
+  free(xb);
   return ORC_OK;
 }
 

@@ -76,6 +76,10 @@ int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int
 int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                     const int32_t* row_ptr, const int32_t* ids, float lr, uint64_t seed,
                     uint64_t step, const int64_t* js, int nj, void* Wrows, int nthreads);
+/* orc_update_rows with given gradient codes: G [B][nj] BF16 codes of labels js (teacher forcing). */
+int orc_update_rows_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
+                           const uint16_t* G, float lr, uint64_t seed, uint64_t step, const int64_t* js,
+                           int nj, void* Wrows, int nthreads);
 int orc_dx_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                 const int32_t* row_ptr, const int32_t* ids, const int32_t* bs, int nb,
                 float* dXrows, int nthreads);

@@ -207,6 +207,18 @@ def test_update_from_g_is_the_weight_half_of_the_step(orc, wfmt):
     assert np.array_equal(orc.update_from_g(wfmt, W, bt.X, G, wl.lr, 8, 2), Wn)
 
 
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_update_rows_from_g_is_the_sampled_weight_half(orc, wfmt):
+    wl, W, bt = _small_case(wfmt, B=9, D=64, L=260)
+    Wn, _, _, _, G = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, wl.lr, 6, 4, want_g=True)
+    js = np.array([0, 3, 128, 259], np.int64)
+    assert np.array_equal(orc.update_rows_from_g(wfmt, W, bt.X, G[:, js], wl.lr, 6, 4, js), Wn[js])
+    # other codes give the row update of those codes (global RNG index of each row kept)
+    G2 = G.copy(); G2[:, js] ^= 1
+    assert np.array_equal(orc.update_rows_from_g(wfmt, W, bt.X, G2[:, js], wl.lr, 6, 4, js),
+                          orc.update_from_g(wfmt, W, bt.X, G2, wl.lr, 6, 4)[js])
+
+
 def test_saturated_dyadic_step_is_exact(orc):
     """X, W in {+-2^-3} with a dominant first column make |z| >= 116, so the FP32 sigmoid is exactly
     0 or 1 and every intermediate is exact; the result is predicted without the oracle."""
