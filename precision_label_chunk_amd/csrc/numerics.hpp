@@ -102,9 +102,17 @@ __device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k)
 
 // one Philox4x32 round with round key (k0, k1) (wave-uniform); round i of the 10 uses the key
 // (seed_lo + i * 0x9E3779B9, seed_hi + i * 0xBB67AE85)
+// a * m as a 64-bit product in one full-rate instruction (v_mad_u64_u32; the compiler otherwise
+// splits it into v_mul_lo_u32 and v_mul_hi_u32); m is wave-uniform
+__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t m) {
+  uint64_t r, carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "s"(m));
+  return r;
+}
+
 __device__ __forceinline__ u32x4 philox_round(u32x4 c, uint32_t k0, uint32_t k1) {
-  const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
-  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+  const uint64_t p0 = mul_wide(c.x, 0xD2511F53u);
+  const uint64_t p1 = mul_wide(c.z, 0xCD9E8D57u);
   return u32x4{xor3_key((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
                xor3_key((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0};
 }

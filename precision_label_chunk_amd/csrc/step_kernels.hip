@@ -34,65 +34,122 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
-// one block per sample: validate its CSR row and count its labels per 128-label tile
-__global__ void k_label_count(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
-                              int B, int64_t nnz, int64_t L, uint32_t* __restrict__ tile_cnt,
-                              uint32_t* __restrict__ flags) {
-  const int b = blockIdx.x;
-  int64_t r0 = row_ptr[b], r1 = row_ptr[b + 1];
-  if (threadIdx.x == 0) {
-    bool bad = r0 < 0 || r1 < r0 || r1 > nnz || (b == 0 && r0 != 0) || (b == B - 1 && r1 != nnz);
+// Label bucketing by 128-label tile: counts, exclusive offsets, then the bucket entries
+// (sample << 16 | label within the tile). A work-group handles LSPB samples, one wave per sample at
+// a time; counts of the first LHOT tiles (where a skewed label law concentrates its mass) are first
+// gathered in LDS and added to the global counters once per work-group, so a popular tile costs one
+// global atomic per work-group instead of one per occurrence.
+constexpr int LSPB = 16, LHOT = 4096;
+
+// validate sample b's CSR row (flags) and return its clamped entry range
+__device__ __forceinline__ void label_row(const int32_t* __restrict__ row_ptr, int b, int B, int64_t nnz,
+                                          uint32_t* __restrict__ flags, bool check, int64_t& r0, int64_t& r1) {
+  r0 = row_ptr[b]; r1 = row_ptr[b + 1];
+  if (check) {
+    const bool bad = r0 < 0 || r1 < r0 || r1 > nnz || (b == 0 && r0 != 0) || (b == B - 1 && r1 != nnz);
     if (bad) atomicOr(flags, ELMO_FLAG_ROW_PTR_);
   }
   r0 = r0 < 0 ? 0 : (r0 > nnz ? nnz : r0);
   r1 = r1 < r0 ? r0 : (r1 > nnz ? nnz : r1);
-  for (int64_t i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
-    int32_t id = ids[i];
-    if (id < 0 || id >= L) { atomicOr(flags, ELMO_FLAG_LABEL_RANGE_); continue; }
-    atomicAdd(&tile_cnt[id / TJ1], 1u);
-  }
 }
 
-// exclusive scan of the per-tile counts (one block of 1024 threads); cnt becomes the scatter cursor
+__global__ __launch_bounds__(256) void k_label_count(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
+                                                     int B, int64_t nnz, int64_t L, int64_t ntiles,
+                                                     uint32_t* __restrict__ tile_cnt, uint32_t* __restrict__ flags) {
+  __shared__ uint32_t h[LHOT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = tid; t < LHOT; t += 256) h[t] = 0u;
+  __syncthreads();
+  const int b0 = blockIdx.x * LSPB, b1 = b0 + LSPB < B ? b0 + LSPB : B;
+  for (int b = b0 + wave; b < b1; b += 4) {
+    int64_t r0, r1;
+    label_row(row_ptr, b, B, nnz, flags, lane == 0, r0, r1);
+    for (int64_t i = r0 + lane; i < r1; i += 64) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= L) { atomicOr(flags, ELMO_FLAG_LABEL_RANGE_); continue; }
+      const int t = id / TJ1;
+      if (t < LHOT) atomicAdd(&h[t], 1u);
+      else atomicAdd(&tile_cnt[t], 1u);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < LHOT && t < ntiles; t += 256)
+    if (h[t]) atomicAdd(&tile_cnt[t], h[t]);
+}
+
+// exclusive scan of the per-tile counts (one work-group of 1024 threads, 4096-entry segments with a
+// running carry); cnt becomes the scatter cursor and off[ntiles] the total
 __global__ __launch_bounds__(1024) void k_label_scan(uint32_t* __restrict__ cnt, uint32_t* __restrict__ off,
                                                      int64_t ntiles) {
-  __shared__ uint32_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t seg = (ntiles + 1023) / 1024;
-  const int64_t a = tid * seg, e = (a + seg < ntiles) ? a + seg : ntiles;
-  uint32_t s = 0;
-  for (int64_t i = a; i < e; ++i) s += cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {      // inclusive Hillis-Steele scan
-    uint32_t v = tid >= o ? part[tid - o] : 0u;
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t carry = 0;
+  for (int64_t base = 0; base < ntiles; base += 4096) {
+    const int64_t i0 = base + 4 * (int64_t)tid;
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = i0 + k < ntiles ? cnt[i0 + k] : 0u;
+    const uint32_t tsum = v[0] + v[1] + v[2] + v[3];
+    // inclusive scan of the thread sums within the wave, then across the 16 waves
+    uint32_t x = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    part[tid] += v;
+    if (tid == 0) {
+      uint32_t run = carry;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) { const uint32_t t = wsum[w]; wsum[w] = run; run += t; }
+      carry_s = run;
+    }
+    __syncthreads();
+    uint32_t run = wsum[wave] + x - tsum;         // exclusive prefix of this thread's first entry
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k < ntiles) { off[i0 + k] = run; cnt[i0 + k] = run; }
+      run += v[k];
+    }
+    carry = carry_s;
     __syncthreads();
   }
-  uint32_t run = tid ? part[tid - 1] : 0u;
-  for (int64_t i = a; i < e; ++i) {
-    uint32_t c = cnt[i];
-    off[i] = run;
-    cnt[i] = run;
-    run += c;
-  }
-  if (tid == 1023) off[ntiles] = part[1023];
+  if (tid == 0) off[ntiles] = carry;
 }
 
 // bucket capacity is nnz: with a malformed row_ptr (overlapping rows) entries beyond it are dropped
-__global__ void k_label_scatter(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
-                                int64_t nnz, int64_t L, uint32_t* __restrict__ cursor,
-                                uint32_t* __restrict__ bucket) {
-  const int b = blockIdx.x;
-  int64_t r0 = row_ptr[b], r1 = row_ptr[b + 1];
-  r0 = r0 < 0 ? 0 : (r0 > nnz ? nnz : r0);
-  r1 = r1 < r0 ? r0 : (r1 > nnz ? nnz : r1);
-  for (int64_t i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
-    int32_t id = ids[i];
-    if (id < 0 || id >= L) continue;
-    uint32_t pos = atomicAdd(&cursor[id / TJ1], 1u);
-    if (pos < (uint64_t)nnz) bucket[pos] = ((uint32_t)b << 16) | (uint32_t)(id % TJ1);
+__global__ __launch_bounds__(256) void k_label_scatter(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ ids,
+                                                       int B, int64_t nnz, int64_t L, int64_t ntiles,
+                                                       uint32_t* __restrict__ cursor, uint32_t* __restrict__ bucket) {
+  __shared__ uint32_t h[LHOT];                    // counts of this work-group's entries, then its cursors
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = tid; t < LHOT; t += 256) h[t] = 0u;
+  __syncthreads();
+  const int b0 = blockIdx.x * LSPB, b1 = b0 + LSPB < B ? b0 + LSPB : B;
+  for (int b = b0 + wave; b < b1; b += 4) {
+    int64_t r0, r1;
+    label_row(row_ptr, b, B, nnz, nullptr, false, r0, r1);
+    for (int64_t i = r0 + lane; i < r1; i += 64) {
+      const int32_t id = ids[i];
+      if (id >= 0 && id < L && id / TJ1 < LHOT) atomicAdd(&h[id / TJ1], 1u);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < LHOT && t < ntiles; t += 256)    // reserve this work-group's range per tile
+    if (h[t]) h[t] = atomicAdd(&cursor[t], h[t]);
+  __syncthreads();
+  for (int b = b0 + wave; b < b1; b += 4) {
+    int64_t r0, r1;
+    label_row(row_ptr, b, B, nnz, nullptr, false, r0, r1);
+    for (int64_t i = r0 + lane; i < r1; i += 64) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= L) continue;
+      const int t = id / TJ1;
+      const uint32_t pos = t < LHOT ? atomicAdd(&h[t], 1u) : atomicAdd(&cursor[t], 1u);
+      if (pos < (uint64_t)nnz) bucket[pos] = ((uint32_t)b << 16) | (uint32_t)(id % TJ1);
+    }
   }
 }
 
@@ -341,7 +398,7 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
                                                        const uint16_t* __restrict__ Xb,
                                                        const uint16_t* __restrict__ G,
                                                        float* __restrict__ part, int NR, int NS, float lr,
-                                                       uint64_t seed, uint64_t step) {
+                                                       uint64_t seed, uint64_t step, int first) {
   constexpr int NW = DS / 32, NT = 64 * NW;    // waves (feature blocks), threads
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int NB = MB / 32;                  // sample blocks
@@ -551,7 +608,8 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     }
   }
 
-  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic)
+  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic); the
+  // step's first chunk writes its slot instead (every slot has a range there)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -559,9 +617,11 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
       const int b = nb * 32 + l32;
       const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
       f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
-      f32x4_t v = *pp;
-      v[0] += accX[nb][4 * ig]; v[1] += accX[nb][4 * ig + 1];
-      v[2] += accX[nb][4 * ig + 2]; v[3] += accX[nb][4 * ig + 3];
+      f32x4_t v = {accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
+      if (!first) {
+        const f32x4_t o = *pp;
+        v[0] = o[0] + v[0]; v[1] = o[1] + v[1]; v[2] = o[2] + v[2]; v[3] = o[3] + v[3];
+      }
       *pp = v;
     }
 }
@@ -699,13 +759,14 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     const int nt2 = (clen + TJ2 - 1) / TJ2;
     const int NR = nt2 < s.NR ? nt2 : s.NR;
     const int grid2 = 8 * s.NS * ((NR + 7) / 8);
+    const int first = c0 == a.l0 && NR == s.NR;    // writes every partial slot: no zero fill needed
     kt_begin(KT_BWD, st, clen);
     if (s.DS == 128)
       hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
+                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
     else
       hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(128), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step);
+                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
     LAUNCH_CHECK();
     kt_end(KT_BWD, st);
   }
@@ -722,19 +783,25 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, cnt, s.ntiles + 1, 0u);
   LAUNCH_CHECK();
   if (!a.forward_only()) {
-    hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, st, (uint32_t*)(ws + s.part),
-                       (int64_t)s.NR * s.MB * a.D, 0u);
-    LAUNCH_CHECK();
+    // the first chunk stores all partial slots unless it has fewer label ranges than there are slots
+    const int64_t clen0 = (a.l1 - a.l0) < s.Cc ? (a.l1 - a.l0) : s.Cc;
+    if ((clen0 + TJ2 - 1) / TJ2 < s.NR) {
+      hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, st, (uint32_t*)(ws + s.part),
+                         (int64_t)s.NR * s.MB * a.D, 0u);
+      LAUNCH_CHECK();
+    }
   }
+  const int lblocks = (a.B + LSPB - 1) / LSPB;
   if (a.B > 0 && a.row_ptr) {
-    hipLaunchKernelGGL(k_label_count, dim3(a.B), dim3(64), 0, st, a.row_ptr, a.ids, a.B, a.nnz, a.L, cnt, flags);
+    hipLaunchKernelGGL(k_label_count, dim3(lblocks), dim3(256), 0, st, a.row_ptr, a.ids, a.B, a.nnz, a.L, s.ntiles,
+                       cnt, flags);
     LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(k_label_scan, dim3(1), dim3(1024), 0, st, cnt, off, s.ntiles);
   LAUNCH_CHECK();
   if (a.B > 0 && a.row_ptr && a.nnz > 0) {
-    hipLaunchKernelGGL(k_label_scatter, dim3(a.B), dim3(64), 0, st, a.row_ptr, a.ids, a.nnz, a.L, cnt,
-                       (uint32_t*)(ws + s.bucket));
+    hipLaunchKernelGGL(k_label_scatter, dim3(lblocks), dim3(256), 0, st, a.row_ptr, a.ids, a.B, a.nnz, a.L,
+                       s.ntiles, cnt, (uint32_t*)(ws + s.bucket));
     LAUNCH_CHECK();
   }
   {
