@@ -92,29 +92,33 @@ __device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) { return sr_e
 // ---- Philox4x32-10 ------------------------------------------------------------------------------
 struct u32x4 { uint32_t x, y, z, w; };
 
-// a ^ b ^ k in one instruction (gfx950's three-input bitwise op, truth table 0x96 = parity); the
-// key k is wave-uniform
+// a ^ b ^ k in one instruction (gfx950's three-input bitwise op, truth table 0x96 = parity)
 __device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+  return (uint32_t)__builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
 // one Philox4x32 round with round key (k0, k1) (wave-uniform); round i of the 10 uses the key
 // (seed_lo + i * 0x9E3779B9, seed_hi + i * 0xBB67AE85)
-// a * m as a 64-bit product in one full-rate instruction (v_mad_u64_u32; the compiler otherwise
-// splits it into v_mul_lo_u32 and v_mul_hi_u32); m is wave-uniform
-__device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t m) {
-  uint64_t r, carry;
-  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "s"(m));
-  return r;
-}
-
 __device__ __forceinline__ u32x4 philox_round(u32x4 c, uint32_t k0, uint32_t k1) {
-  const uint64_t p0 = mul_wide(c.x, 0xD2511F53u);
-  const uint64_t p1 = mul_wide(c.z, 0xCD9E8D57u);
+  const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u, p1 = (uint64_t)c.z * 0xCD9E8D57u;
   return u32x4{xor3_key((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
                xor3_key((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0};
+}
+
+// the same round applied to two counters. Inside a large kernel the compiler splits each 32 x 32
+// -> 64-bit product into v_mul_lo_u32 + v_mul_hi_u32; the four products are written here as
+// v_mad_u64_u32 in one block (their carry-out is unused and shares one SGPR pair, as in the
+// compiler's own code for such products), so that no hazard padding separates them.
+__device__ __forceinline__ void philox_round2(u32x4& a, u32x4& b, uint32_t k0, uint32_t k1) {
+  uint64_t pa0, pa1, pb0, pb1, cy;
+  asm("v_mad_u64_u32 %0, %4, %5, %9, 0\n\t"
+      "v_mad_u64_u32 %1, %4, %6, %10, 0\n\t"
+      "v_mad_u64_u32 %2, %4, %7, %9, 0\n\t"
+      "v_mad_u64_u32 %3, %4, %8, %10, 0"
+      : "=&v"(pa0), "=&v"(pa1), "=&v"(pb0), "=&v"(pb1), "=&s"(cy)
+      : "v"(a.x), "v"(a.z), "v"(b.x), "v"(b.z), "s"(0xD2511F53u), "s"(0xCD9E8D57u));
+  a = u32x4{xor3_key((uint32_t)(pa1 >> 32), a.y, k0), (uint32_t)pa1, xor3_key((uint32_t)(pa0 >> 32), a.w, k1), (uint32_t)pa0};
+  b = u32x4{xor3_key((uint32_t)(pb1 >> 32), b.y, k0), (uint32_t)pb1, xor3_key((uint32_t)(pb0 >> 32), b.w, k1), (uint32_t)pb0};
 }
 __device__ __forceinline__ uint32_t philox_key0(uint64_t seed, int i) { return (uint32_t)seed + (uint32_t)i * 0x9E3779B9u; }
 __device__ __forceinline__ uint32_t philox_key1(uint64_t seed, int i) { return (uint32_t)(seed >> 32) + (uint32_t)i * 0xBB67AE85u; }

@@ -343,8 +343,7 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
     }
   } else if (p <= 10) {
     const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
-    st.c[0] = philox_round(st.c[0], k0, k1);
-    st.c[1] = philox_round(st.c[1], k0, k1);
+    philox_round2(st.c[0], st.c[1], k0, k1);
   } else if (p == 11) {
     st.ow[0] = *(const i32x4_t*)ow0;
     st.ow[1] = *(const i32x4_t*)ow1;
