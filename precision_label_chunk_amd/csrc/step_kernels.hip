@@ -155,12 +155,15 @@ __global__ __launch_bounds__(256) void k_label_scatter(const int32_t* __restrict
 
 // zero-padded BF16 copy of X ([MB][D]) and, in FP8 mode, its E4M3-RNE cast for the forward MFMA
 __global__ void k_prep_x(const uint16_t* __restrict__ X, int B, int D, int MB, uint16_t* __restrict__ Xb,
-                         uint8_t* __restrict__ Xq) {
+                         uint8_t* __restrict__ Xq, uint16_t* __restrict__ XbT) {
   const int64_t n = (int64_t)MB * D;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     uint32_t v = (i / D) < B ? X[i] : 0u;
     Xb[i] = (uint16_t)v;
     if (Xq) Xq[i] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(v));
+    // the feature-major copy XbT[d][b] (element i of it: d = i / MB, b = i % MB)
+    const int64_t d = i / MB, b = i % MB;
+    XbT[i] = b < B ? X[b * D + d] : (uint16_t)0;
   }
 }
 
@@ -308,51 +311,51 @@ __device__ __forceinline__ int row_swz(int j) {
 // register i; swapping register groups 1<->0 and 3<->2 across the two lane halves leaves features
 // [16u + 8hi, +8) for u = 0, 1 in each lane, which it updates with one Philox block each:
 // t = fmaf(-lr, dW, w), hardware stochastic rounding, one 16- or 8-byte store per 8 weights.
-// The work is cut into UPD_PHASES phases so that it can be spread between the MFMAs of the next
-// tile: 0 swaps and RNG counters, 1..10 the Philox rounds, 11 old-weight reads, 12..19 two weights
-// each (rounding and packing; the last of each 8 also stores them).
+// The work is cut into UPD_PHASES phases so that it can be spread between MFMAs: 0 the RNG
+// counters, 1..10 the Philox rounds (these RNG_PHASES need no dW), 11 the swaps, 12 old-weight
+// reads, 13..20 two weights each (rounding and packing; the last of each 8 also stores them).
 //   ow0/1 the old weights of those features (8 BF16 each, u = 0 / 1) in LDS
 //   roff  byte offset of the label's row in the chunk's weight resource, plus the feature offset of
 //         lane half `hi` (features dsl + dblk*32 + 8 hi)
 //   idx0  global element index of that first feature: (c0 + label) * D + feature
-constexpr int UPD_PHASES = 20;
+constexpr int UPD_PHASES = 21, RNG_PHASES = 11;
 struct UpdState {
-  float dw[16];
   u32x4 c[2];
   i32x4_t ow[2];
   uint32_t pk[4];
 };
 
 template <int WF>
-__device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& acc, const uint16_t* ow0,
+__device__ __forceinline__ void upd_phase(int p, UpdState& st, f32x16_t& acc, const uint16_t* ow0,
                                           const uint16_t* ow1, __amdgpu_buffer_rsrc_t wres, int roff,
                                           uint64_t idx0, float lr, uint64_t seed, uint64_t step) {
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   if (p == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u) st.c[u] = philox_counter((idx0 + 16 * u) >> 3, step);
+  } else if (p <= 10) {
+    const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
+    philox_round2(st.c[0], st.c[1], k0, k1);
+  } else if (p == 11) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // (copy to scalars first: bit-casting an ext-vector element reference reads element 0)
         const float lo_v = acc[8 * u + e], hi_v = acc[8 * u + 4 + e];
         const auto sw = __builtin_amdgcn_permlane32_swap(f2u(lo_v), f2u(hi_v), false, false);
-        st.dw[8 * u + e] = u2f((uint32_t)sw[0]);
-        st.dw[8 * u + 4 + e] = u2f((uint32_t)sw[1]);
+        acc[8 * u + e] = u2f((uint32_t)sw[0]);
+        acc[8 * u + 4 + e] = u2f((uint32_t)sw[1]);
       }
-      st.c[u] = philox_counter((idx0 + 16 * u) >> 3, step);
-    }
-  } else if (p <= 10) {
-    const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
-    philox_round2(st.c[0], st.c[1], k0, k1);
-  } else if (p == 11) {
+  } else if (p == 12) {
     st.ow[0] = *(const i32x4_t*)ow0;
     st.ow[1] = *(const i32x4_t*)ow1;
   } else {
-    const int u = (p - 12) >> 2, pr = (p - 12) & 3;          // weights 2 pr, 2 pr + 1 of block u
+    const int u = (p - 13) >> 2, pr = (p - 13) & 3;          // weights 2 pr, 2 pr + 1 of block u
     const u32x4& rnd = st.c[u];
     const uint32_t wb = (uint32_t)st.ow[u][pr];
-    const float t0 = fmaf(-lr, st.dw[8 * u + 2 * pr], u2f(wb << 16));
-    const float t1 = fmaf(-lr, st.dw[8 * u + 2 * pr + 1], u2f(wb & 0xffff0000u));
+    const float t0 = fmaf(-lr, acc[8 * u + 2 * pr], u2f(wb << 16));
+    const float t1 = fmaf(-lr, acc[8 * u + 2 * pr + 1], u2f(wb & 0xffff0000u));
     const int off = roff + 16 * u * ESZ;
     if constexpr (WF == W_BF16_) {
       const uint32_t lo = sr_bf16_into(0u, t0, rng_pick_hi(rnd, 2 * pr), false);
@@ -375,10 +378,13 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
   }
 }
 
-// Work-group: DS/32 waves, one per SIMD for DS = 128. Wave w owns the 32 features
-// [dsl + 32 w, +32) of the slice and does both backward contractions of every tile for them:
-//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]      two 32-label blocks, K = MB samples  (MB/8 MFMAs)
-//   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]    MB/32 sample blocks, K = 64 labels   (MB/8 MFMAs)
+// Work-group: NH * DS/32 waves. The NH waves of feature block fb own the 32 features
+// [dsl + 32 fb, +32) of the slice and share the two backward contractions of every tile; with
+// NH = 2 (two waves per SIMD for DS = 128, so that one wave's update arithmetic fills the other's
+// MFMA and LDS waits) wave half h computes dW of label block h over all samples and dX of sample
+// half h over all the tile's labels:
+//   dW^T[d][j]  = sum_b X^T[d][b] G[b][j]      2/NH 32-label blocks, K = MB samples  (MB/8/NH MFMAs)
+//   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]    MB/32/NH sample blocks, K = 64 labels (MB/8/NH MFMAs)
 // with A = stationary X^T fragments in registers (dW), B = G rows by ds_read_b128 (dW), and
 // A = W^T, B = G^T by ds_read_b64_tr_b16 (dX). Per 64-label tile t:
 //   G tile  [64][MB] BF16 (label-major, as the forward kernel writes it), double buffered in two
@@ -389,39 +395,46 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
 //   W tile  [64][DS] decoded to BF16 in LDS, three buffers: tile t's stays intact through tile t+1,
 //           whose MFMAs its update overlaps, while tile t+2's is being staged.
 // The tile's MFMAs run in slots (dW and dX alternating), each slot's LDS operands read PFS slots
-// ahead, and the previous tile's update (2 x UPD_PHASES phases of VALU work: RNG, rounding,
-// stores) spread over the slots; a scheduling fence closes every slot so that the compiler keeps
-// this interleaving. dW never leaves the registers; one barrier per tile.
-template <int MB, int WF, int DS>
-__global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
-                                                       const uint16_t* __restrict__ Xb,
-                                                       const uint16_t* __restrict__ G,
-                                                       float* __restrict__ part, int NR, int NS, float lr,
-                                                       uint64_t seed, uint64_t step, int first) {
-  constexpr int NW = DS / 32, NT = 64 * NW;    // waves (feature blocks), threads
+// ahead, and the update of the wave's label blocks of the previous tile (UPD_PHASES phases of VALU
+// work per block: RNG, rounding, stores) spread over the slots; a scheduling fence closes every
+// slot so that the compiler keeps this interleaving. dW never leaves the registers; one barrier
+// per tile.
+template <int MB, int WF, int DS, int NH>
+__global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict__ W, int D, int64_t c0, int clen,
+                                                            const uint16_t* __restrict__ XbT,
+                                                            const uint16_t* __restrict__ G,
+                                                            float* __restrict__ part, int NR, int NS, float lr,
+                                                            uint64_t seed, uint64_t step, int first) {
+  constexpr int NFB = DS / 32;                 // feature blocks
+  constexpr int NW = NFB * NH, NT = 64 * NW;   // waves, threads
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int NB = MB / 32;                  // sample blocks
+  constexpr int NJB = 2 / NH;                  // label blocks per wave (dW, update)
+  constexpr int NBW = NB / NH;                 // sample blocks per wave (dX)
   constexpr int KK = MB / 16;                  // dW K steps per label block
-  constexpr int NDW = 2 * KK;                  // dW MFMAs per tile
+  constexpr int NDW = NJB * KK;                // dW MFMAs per tile
   constexpr int KXN = TJ2 / 16;                // dX K steps
-  constexpr int NDX = KXN * NB;                // dX MFMAs per tile
-  static_assert(NDW == NDX, "slots alternate dW and dX");
+  constexpr int NDX = KXN * NBW;               // dX MFMAs per tile
+  static_assert(NH == 1 || NH == 2, "one or two waves per feature block");
+  static_assert(NBW >= 1 && NDW == NDX, "slots alternate dW and dX");
   constexpr int NSLOT = NDW + NDX;
-  constexpr int PFS = 4;                       // operand prefetch distance (slots)
+  constexpr int PFS = NH == 2 ? 2 : 4;         // operand prefetch distance (slots)
+  constexpr int STAGE_MODE = 2;
   constexpr int GTE = TJ2 * MB;                // G tile elements
   constexpr int GCPR = MB / 8;                 // 16-byte chunks per G row
   constexpr int GPT = TJ2 * GCPR / NT;         // G chunks per thread
   constexpr int WCPR = DS * ESZ / 16;          // 16-byte global W chunks per tile row
   constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
   constexpr int NOW = KK < 8 ? KK : 8;         // distinct dW operand offsets per lane
-  constexpr int NOB = NB < 4 ? NB : 4;         // distinct dX operand offsets per lane and row
-  static_assert(WPT >= 1 && TJ2 == 64, "tile split");
+  constexpr int NOB = NBW < 4 ? NBW : 4;       // distinct dX operand offsets per lane and row
+  static_assert(GPT >= 1 && WPT >= 1 && TJ2 == 64, "tile split");
   __shared__ __attribute__((aligned(1024))) uint16_t Gs0[GTE];
   __shared__ __attribute__((aligned(1024))) uint16_t Gs1[GTE];
   __shared__ __attribute__((aligned(1024))) uint16_t Ws[3][TJ2 * DS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int dblk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dblk = wave % NFB, h = wave / NFB;  // feature block, wave half
   const int l32 = lane & 31, hi = lane >> 5, q = lane >> 4, li = lane & 15;
   // work-groups of one label range share its G tiles: keep them on one XCD (dispatch is round-robin)
   const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
@@ -434,19 +447,20 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
   // the chunk's weight rows: rows past the chunk's end (the ragged last tile) load as zero and
   // drop their stores
   const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)rowbytes, clen * rowbytes);
+  const int jb0 = NH == 2 ? h : 0;             // first label block of this wave
+  const int nb0 = h * NBW;                     // first sample block of this wave
 
-  // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples)
+  // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples), from the
+  // feature-major copy XbT[d][b]
   s16x8_t xT[KK];
   {
     const int d = dsl + dblk * 32 + l32;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xT[kk][e] = (short)Xb[(kk * 16 + hi * 8 + e) * D + d];
+    for (int kk = 0; kk < KK; ++kk) xT[kk] = *(const s16x8_t*)(XbT + (int64_t)d * MB + kk * 16 + hi * 8);
   }
-  f32x16_t accX[NB];
+  f32x16_t accX[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) accX[nb] = f32x16_t{};
+  for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
 
   // loop-invariant LDS element offsets (rows of both label blocks share the swizzle: it only
   // depends on the row's low 4 bits)
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
   const int gW = row_swz<MB / 8>(l32);
   int offW[NOW];
 #pragma unroll
-  for (int k = 0; k < NOW; ++k) offW[k] = l32 * MB + 8 * (hi ^ (gW & 1)) + 16 * (k ^ (gW >> 1));
+  for (int k = 0; k < NOW; ++k) offW[k] = (jb0 * 32 + l32) * MB + 8 * (hi ^ (gW & 1)) + 16 * (k ^ (gW >> 1));
   //   dX operands (transposing reads): rows jX and jX + 4 of each 16-label K step
   const int jX = 8 * (q >> 1) + (li >> 2);
   //     A = W^T: features dblk*32 + 16 (q&1) + 4 (li&3) .. +3
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     const int sB = row_swz<MB / 8>(jX + 4 * w);
 #pragma unroll
     for (int k = 0; k < NOB; ++k)
-      offB[w][k] = (jX + 4 * w) * MB + 32 * (k ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
+      offB[w][k] = (jX + 4 * w) * MB + 32 * ((nb0 + k) ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
   }
   //   update: old weights of W row jb*32 + l32, chunks 4 dblk + 2u + hi
   const int sU = row_swz<DS / 8>(l32);
@@ -516,9 +530,21 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     }
   };
 
-  f32x16_t accP[2];                            // previous tile's dW (two label blocks)
+  f32x16_t accP[NJB];                          // previous tile's dW (this wave's label blocks)
   int tP = 0, wbP = 0;                         // previous tile and its W buffer
-  auto tile = [&](int t, int wb, auto gb, auto upd) {
+  // update phase PH of the wave's label blocks of tile tU (old weights in W buffer wsU, dW in accP)
+  auto upd_args = [&](auto PH, UpdState& st, const uint16_t* wsU, int tU) {
+    constexpr int ph = decltype(PH)::value, jl = ph / UPD_PHASES;
+    const int jb = jb0 + jl;
+    upd_phase<WF>(ph % UPD_PHASES, st, accP[jl], wsU + offU0 + jb * 32 * DS, wsU + offU1 + jb * 32 * DS, wres,
+                  (tU * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
+                  (uint64_t)(c0 + tU * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
+  };
+  auto update = [&](int tU, int wbU) {         // the whole update of tile tU, in sequence
+    UpdState st;
+    static_for<0, NJB * UPD_PHASES>([&](auto PH) { upd_args(PH, st, Ws[wbU], tU); });
+  };
+  auto tile = [&](int t, int wb, auto gb, auto upd, auto pre, auto post) {
     constexpr bool UPD = decltype(upd)::value;
     constexpr int GB = decltype(gb)::value;    // G buffer of this tile (compile time)
     const int wbn = wb == 2 ? 0 : wb + 1;      // W buffer of tile t+1
@@ -526,30 +552,34 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     const int tn = t + 1 < nt ? t + 1 : nt - 1;
     uint16_t* gnext = GB ? Gs0 : Gs1;
     __syncthreads();                           // tile t resident; iteration t-1 fully done
+    if constexpr (NH == 2 && STAGE_MODE != 0) static_for<0, NLD>([&](auto K) { load_item(K, tn); });
+    pre(t);
     const uint16_t* gs = GB ? Gs1 : Gs0;
     const uint16_t* ws = Ws[wb];
-    auto rdW = [&](int m) {                    // dW MFMA m: label block m & 1, K step m >> 1
-      const int jb = m & 1, kk = m >> 1;
-      return *(const s16x8_t*)(gs + offW[kk % NOW] + 16 * (kk - kk % NOW) + jb * 32 * MB);
+    auto rdW = [&](int m) {                    // dW MFMA m: label block m % NJB, K step m / NJB
+      const int jl = m % NJB, kk = m / NJB;
+      return *(const s16x8_t*)(gs + offW[kk % NOW] + 16 * (kk - kk % NOW) + jl * 32 * MB);
     };
     auto rdXa = [&](int kx) {
       return join(lds_read_tr16(ws + offA0 + kx * 16 * DS), lds_read_tr16(ws + offA1 + kx * 16 * DS));
     };
-    auto rdXb = [&](int m) {                   // dX MFMA m: K step m / NB, sample block m % NB
-      const int kx = m / NB, nb = m % NB, k = nb % NOB, o = 32 * (nb - k) + kx * 16 * MB;
+    auto rdXb = [&](int m) {                   // dX MFMA m: K step m / NBW, sample block nb0 + m % NBW
+      const int kx = m / NBW, nb = m % NBW, k = nb % NOB, o = 32 * (nb - k) + kx * 16 * MB;
       return join(lds_read_tr16(gs + offB[0][k] + o), lds_read_tr16(gs + offB[1][k] + o));
     };
     UpdState st;
     const uint16_t* wsP = Ws[wbP];
     s16x8_t opW[NDW], opXb[NDX], opXa[KXN];
-    f32x16_t accW[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t accW[NJB];
+#pragma unroll
+    for (int jl = 0; jl < NJB; ++jl) accW[jl] = f32x16_t{};
     // operand reads of slot z (dW for even z, dX for odd z)
     auto fetch = [&](auto Z) {
       constexpr int z = decltype(Z)::value, m = z >> 1;
       if constexpr ((z & 1) == 0) {
         opW[m] = rdW(m);
       } else {
-        if constexpr (m % NB == 0) opXa[m / NB] = rdXa(m / NB);
+        if constexpr (m % NBW == 0) opXa[m / NBW] = rdXa(m / NBW);
         opXb[m] = rdXb(m);
       }
     };
@@ -558,26 +588,30 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
       constexpr int z = decltype(Z)::value, m = z >> 1;
       if constexpr (z + PFS < NSLOT) fetch(std::integral_constant<int, z + PFS>{});
       constexpr int HALF = NSLOT / 2;
-      static_for<0, NLD>([&](auto K) {
-        if constexpr (decltype(K)::value * HALF / NLD == z) load_item(K, tn);
-        if constexpr (HALF + decltype(K)::value * HALF / NLD == z) store_item(K, gnext, wbn);
-      });
-      if constexpr ((z & 1) == 0) accW[m & 1] = mfma_bf16(xT[m >> 1], opW[m], accW[m & 1]);
-      else accX[m % NB] = mfma_bf16(opXa[m / NB], opXb[m], accX[m % NB]);
+      if constexpr (NH == 1 || STAGE_MODE == 0)
+        static_for<0, NLD>([&](auto K) {
+          if constexpr (decltype(K)::value * HALF / NLD == z) load_item(K, tn);
+          if constexpr (HALF + decltype(K)::value * HALF / NLD == z) store_item(K, gnext, wbn);
+        });
+      else if constexpr (STAGE_MODE >= 2)      // LDS writes spread over the slots from S0 on
+        static_for<0, NLD>([&](auto K) {
+          constexpr int S0 = STAGE_MODE == 2 ? NSLOT - NSLOT / 3 : HALF;
+          if constexpr (S0 + decltype(K)::value * (NSLOT - S0) / NLD == z) store_item(K, gnext, wbn);
+        });
+      if constexpr ((z & 1) == 0) accW[m % NJB] = mfma_bf16(xT[m / NJB], opW[m], accW[m % NJB]);
+      else accX[m % NBW] = mfma_bf16(opXa[m / NBW], opXb[m], accX[m % NBW]);
       if constexpr (UPD) {
         // update phases ph with floor(ph * NSLOT / NPH) == z
-        constexpr int NPH = 2 * UPD_PHASES;
-        static_for<(z * NPH + NSLOT - 1) / NSLOT, ((z + 1) * NPH + NSLOT - 1) / NSLOT>([&](auto PH) {
-          constexpr int ph = decltype(PH)::value, jb = ph / UPD_PHASES;
-          upd_phase<WF>(ph % UPD_PHASES, st, accP[jb], wsP + offU0 + jb * 32 * DS, wsP + offU1 + jb * 32 * DS,
-                        wres, (tP * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
-                        (uint64_t)(c0 + tP * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
-        });
+        constexpr int NPH = NJB * UPD_PHASES;
+        static_for<(z * NPH + NSLOT - 1) / NSLOT, ((z + 1) * NPH + NSLOT - 1) / NSLOT>(
+            [&](auto PH) { upd_args(PH, st, wsP, tP); });
       }
       sched_fence();
     });
-    accP[0] = accW[0];
-    accP[1] = accW[1];
+#pragma unroll
+    for (int jl = 0; jl < NJB; ++jl) accP[jl] = accW[jl];
+    post(t, wb);
+    if constexpr (NH == 2 && STAGE_MODE == 1) static_for<0, NLD>([&](auto K) { store_item(K, gnext, wbn); });
     tP = t;
     wbP = wb;
   };
@@ -587,33 +621,50 @@ __global__ __launch_bounds__(DS * 2) void k_bwd_update(uint8_t* __restrict__ W, 
     using G1 = std::integral_constant<int, 1>;
     static_for<0, NLD>([&](auto K) { load_item(K, t0); });
     static_for<0, NLD>([&](auto K) { store_item(K, Gs0, 0); });
-    tile(t0, 0, G0{}, std::false_type{});
-    int wb = 1;
-    for (int t = t0 + 1; t < t1; t += 2) {
-      tile(t, wb, G1{}, std::true_type{});
-      wb = wb == 2 ? 0 : wb + 1;
-      if (t + 1 < t1) {
-        tile(t + 1, wb, G0{}, std::true_type{});
+    if constexpr (NH == 1) {
+      // one wave per SIMD: the previous tile's update is spread between this tile's MFMAs
+      auto none = [](int) {};
+      auto none2 = [](int, int) {};
+      tile(t0, 0, G0{}, std::false_type{}, none, none2);
+      int wb = 1;
+      for (int t = t0 + 1; t < t1; t += 2) {
+        tile(t, wb, G1{}, std::true_type{}, none, none2);
         wb = wb == 2 ? 0 : wb + 1;
+        if (t + 1 < t1) {
+          tile(t + 1, wb, G0{}, std::true_type{}, none, none2);
+          wb = wb == 2 ? 0 : wb + 1;
+        }
       }
-    }
-    UpdState st;
-#pragma unroll
-    for (int ph = 0; ph < 2 * UPD_PHASES; ++ph) {
-      const int jb = ph / UPD_PHASES;
-      upd_phase<WF>(ph % UPD_PHASES, st, accP[jb], Ws[wbP] + offU0 + jb * 32 * DS, Ws[wbP] + offU1 + jb * 32 * DS,
-                    wres, (tP * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
-                    (uint64_t)(c0 + tP * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
+      update(tP, wbP);
+    } else {
+      // two waves per SIMD (halves h = 0, 1 of a feature block) in complementary phases: half 0
+      // updates its label block right after a tile's MFMAs, half 1 before the next tile's MFMAs, so
+      // that on each SIMD the MFMAs of one wave overlap the update arithmetic of the other. The next
+      // tile's staging loads are issued right after the barrier and written to LDS after the wave's
+      // update (half 0) or late in its MFMA phase (half 1), so that an update phase and most of an
+      // MFMA phase cover their latency.
+      auto pre = [&](int t) { if (h == 1 && t > t0) update(t - 1, wbP); };
+      auto post = [&](int t, int wbc) { if (h == 0) update(t, wbc); };
+      int wb = 0;
+      for (int t = t0; t < t1; t += 2) {
+        tile(t, wb, G0{}, std::false_type{}, pre, post);
+        wb = wb == 2 ? 0 : wb + 1;
+        if (t + 1 < t1) {
+          tile(t + 1, wb, G1{}, std::false_type{}, pre, post);
+          wb = wb == 2 ? 0 : wb + 1;
+        }
+      }
+      if (h == 1) update(tP, wbP);
     }
   }
 
   // this range's dX contribution, accumulated in place (fixed slot per range: deterministic); the
   // step's first chunk writes its slot instead (every slot has a range there)
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const int b = nb * 32 + l32;
+      const int b = (nb0 + nb) * 32 + l32;
       const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
       f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
       f32x4_t v = {accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
@@ -718,6 +769,7 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   s.bucket = off;   off = align_up(off + 4 * (size_t)(max_nnz > 0 ? max_nnz : 1), A);
   s.xb = off;       off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.xq = off;       off = align_up(off + (wdtype == W_E4M3_ ? (size_t)s.MB * D : 0), A);
+  s.xbt = off;      off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
   s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
   s.loss = off;     off = align_up(off + 4 * (size_t)s.ntiles, A);
@@ -760,12 +812,14 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     const int grid2 = 8 * s.NS * ((NR + 7) / 8);
     const int first = c0 == a.l0 && NR == s.NR;    // writes every partial slot: no zero fill needed
     kt_begin(KT_BWD, st, clen);
+    // two waves per feature block where the batch has at least two sample blocks
+    constexpr int NH = MB >= 64 ? 2 : 1;
     if (s.DS == 128)
-      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128>), dim3(grid2), dim3(256), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 128, NH>), dim3(grid2), dim3(256 * NH), 0, st, W, a.D, c0, clen,
+                         (const uint16_t*)(ws + s.xbt), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
     else
-      hipLaunchKernelGGL((k_bwd_update<MB, WF, 64>), dim3(grid2), dim3(128), 0, st, W, a.D, c0, clen,
-                         (const uint16_t*)(ws + s.xb), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
+      hipLaunchKernelGGL((k_bwd_update<MB, WF, 64, NH>), dim3(grid2), dim3(128 * NH), 0, st, W, a.D, c0, clen,
+                         (const uint16_t*)(ws + s.xbt), Gc, part, NR, s.NS, a.lr, a.seed, a.step, first);
     LAUNCH_CHECK();
     kt_end(KT_BWD, st);
   }
@@ -807,7 +861,8 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     const int64_t n = (int64_t)s.MB * a.D;
     const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
     hipLaunchKernelGGL(k_prep_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)a.X, a.B, a.D, s.MB,
-                       (uint16_t*)(ws + s.xb), a.wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr);
+                       (uint16_t*)(ws + s.xb), a.wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr,
+                       (uint16_t*)(ws + s.xbt));
     LAUNCH_CHECK();
   }
   int rc;

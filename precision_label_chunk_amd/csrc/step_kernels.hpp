@@ -19,7 +19,7 @@ struct StepLayout {
   int MB, DS, NS, NR;
   int cus;                              // compute units of the device
   int64_t Cc, ntiles;
-  size_t flags, tile_cnt, tile_off, bucket, xb, xq, g, part, loss, total;
+  size_t flags, tile_cnt, tile_off, bucket, xb, xq, xbt, g, part, loss, total;
 };
 
 struct StepArgs {
