@@ -249,13 +249,32 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
       const int bb = wb * RW + mi * 32;
       const uint32_t yw = ybits[jl * (MB / 32) + (bb >> 5)];
       float gv[16];
+      // the exact form is needed only for |z| > 80: one wave-uniform test per block keeps the
+      // common case free of branches
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) big |= __builtin_fabsf(acc[mi][ni][i]) > 80.0f;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+          gv[i] = jvalid && (bb + bl < B) ? bce_grad(acc[mi][ni][i], (yw >> bl) & 1u) : 0.0f;
+        }
+      } else {
+        // (computed for every element, padding included, and selected: no branch per element)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+          const float g = bce_grad_fast(acc[mi][ni][i], (yw >> bl) & 1u);
+          gv[i] = jvalid && (bb + bl < B) ? g : 0.0f;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
         const bool valid = jvalid && (bb + bl < B);
         const bool y = (yw >> bl) & 1u;
         const float z = acc[mi][ni][i];
-        gv[i] = valid ? bce_grad(z, y) : 0.0f;
         if constexpr (LOSS) if (valid) lsum += bce_loss(z, y);
         if constexpr (ZOUT) {
           const int64_t lab = c0 + jbase + jl;
