@@ -37,16 +37,30 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int nks = (int)((rowbytes + KS - 1) / KS);
 
-  // chunk c of this thread: ci = tid + 256 c, row ci / PPR (X rows, then W rows), part ci % PPR
+  // chunk c of this thread: ci = tid + 256 c, row ci / PPR (X rows, then W rows), part ci % PPR.
+  // Buffer loads: W rows at or past nvalid fall outside their resource and read as zero, and so
+  // does a part past the end of a row (its offset is pushed out of range); whether chunk c is an X
+  // or a W chunk is known at compile time when the X chunks fill whole multiples of 256.
+  constexpr int NCHX = MB * PPR;                          // X chunks per slice
+  constexpr int OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xf, (int64_t)MB * rowbytes);
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(Wt, (int64_t)(nvalid < TJ1 ? nvalid : TJ1) * rowbytes);
   i32x4_t stg[2][CPT];
   auto gload = [&](auto S, auto K, int ks) {
     constexpr int c = decltype(K)::value;
     const int ci = tid + 256 * c, row = ci / PPR, part = ci % PPR;
-    const int64_t boff = (int64_t)ks * KS + part * 16;
+    const int kb = ks * KS;                               // wave-uniform
+    const bool inrow = kb + part * 16 < rowbytes;
     i32x4_t v = {0, 0, 0, 0};
-    if ((c + 1 < CPT || ci < NCH) && ks < nks && boff < rowbytes) {
-      if (row < MB) v = *(const i32x4_t*)(Xf + row * rowbytes + boff);
-      else if (row - MB < nvalid) v = *(const i32x4_t*)(Wt + (int64_t)(row - MB) * rowbytes + boff);
+    if constexpr (256 * (c + 1) <= NCHX) {
+      v = buffer_load16(xres, inrow ? row * (int)rowbytes + part * 16 : OOB, kb);
+    } else if constexpr (256 * c >= NCHX) {
+      v = buffer_load16(wres, inrow ? (row - MB) * (int)rowbytes + part * 16 : OOB, kb);
+    } else {
+      const bool isx = row < MB;
+      const i32x4_t vx = buffer_load16(xres, inrow && isx ? row * (int)rowbytes + part * 16 : OOB, kb);
+      const i32x4_t vw = buffer_load16(wres, inrow && !isx ? (row - MB) * (int)rowbytes + part * 16 : OOB, kb);
+      v = i32x4_t{vx[0] | vw[0], vx[1] | vw[1], vx[2] | vw[2], vx[3] | vw[3]};
     }
     stg[decltype(S)::value][c] = v;
   };

@@ -56,6 +56,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ i32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// with a wave-uniform byte offset added (the instruction's scalar offset)
+__device__ __forceinline__ i32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+}
 __device__ __forceinline__ void buffer_store16(i32x4_t v, __amdgpu_buffer_rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
