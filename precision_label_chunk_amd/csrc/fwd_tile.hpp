@@ -19,11 +19,11 @@ constexpr int fwd_pitch(int KS) { return KS + 16; }     // LDS row pitch: confli
 constexpr int fwd_smem_bytes(int MB, int KS) { return 2 * (MB + TJ1) * fwd_pitch(KS); }
 
 // RW x CW is this wave's sub-tile (RW samples, CW labels); the work-group is (MB/RW) x (TJ1/CW) waves
-template <int MB, int WF, int RW, int CW, int KS>
+template <int MB, int WF, int RW, int CW, int KS, typename Mid>
 __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint8_t* smem,
                                          const uint8_t* __restrict__ Wt, int nvalid,
                                          const uint8_t* __restrict__ Xf, int64_t rowbytes, int tid, int wb,
-                                         int wj) {
+                                         int wj, Mid&& mid) {
   constexpr int MI = RW / 32, NI = CW / 32;
   constexpr int PT = fwd_pitch(KS);
   constexpr int SLICE = (MB + TJ1) * PT;
@@ -64,14 +64,13 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
     }
     stg[decltype(S)::value][c] = v;
   };
-  auto lstore = [&](auto S, int buf) {
-    static_for<0, CPT>([&](auto K) {
-      constexpr int c = decltype(K)::value;
-      const int ci = tid + 256 * c;
-      if (c + 1 < CPT || ci < NCH)
-        *(i32x4_t*)(smem + buf * SLICE + (ci / PPR) * PT + (ci % PPR) * 16) = stg[decltype(S)::value][c];
-    });
+  auto lstore1 = [&](auto S, auto K, int buf) {
+    constexpr int c = decltype(K)::value;
+    const int ci = tid + 256 * c;
+    if (c + 1 < CPT || ci < NCH)
+      *(i32x4_t*)(smem + buf * SLICE + (ci / PPR) * PT + (ci % PPR) * 16) = stg[decltype(S)::value][c];
   };
+  auto lstore = [&](auto S, int buf) { static_for<0, CPT>([&](auto K) { lstore1(S, K, buf); }); };
 
   static_for<0, MI * NI>([&](auto I) { acc[decltype(I)::value / NI][decltype(I)::value % NI] = f32x16_t{}; });
 
@@ -87,8 +86,9 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
   };
 
   // slice ks from LDS stage ks & 1 (parity S = ks & 1 at compile time): its MFMAs, with the loads of
-  // slice ks + 2 (into staging set S) spread over its slots, then slice ks + 1 (staging set S ^ 1,
-  // loaded during slice ks - 1) written to the other LDS stage
+  // slice ks + 2 (into staging set S) and the LDS writes of slice ks + 1 (staging set S ^ 1, loaded
+  // during slice ks - 1, into the other stage, which every wave finished reading before the last
+  // barrier) spread over its slots
   auto slice = [&](auto S, int ks) {
     constexpr int SP = decltype(S)::value;
     const uint8_t* Xs = smem + SP * SLICE;
@@ -112,13 +112,15 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
       constexpr int kk = z / (MI * NI), mi = (z / NI) % MI, ni = z % NI;
       fetch(Z);
       static_for<0, CPT>([&](auto K) {
-        if constexpr (decltype(K)::value * NSL / CPT == z) gload(S, K, ks + 2);
+        if constexpr (decltype(K)::value * NSL / CPT == z) {
+          gload(S, K, ks + 2);
+          if (ks + 1 < nks) lstore1(std::integral_constant<int, SP ^ 1>{}, K, SP ^ 1);
+        }
       });
       if constexpr (WF == W_BF16_) acc[mi][ni] = mfma_bf16(fa[kk][mi], fb[kk][ni], acc[mi][ni]);
       else acc[mi][ni] = mfma_e4m3(fa[kk][mi], fb[kk][ni], acc[mi][ni]);
       sched_fence();
     });
-    if (ks + 1 < nks) lstore(std::integral_constant<int, SP ^ 1>{}, SP ^ 1);
     __syncthreads();
   };
 
@@ -126,6 +128,7 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
   using S1 = std::integral_constant<int, 1>;
   static_for<0, CPT>([&](auto K) { gload(S0{}, K, 0); });
   static_for<0, CPT>([&](auto K) { gload(S1{}, K, 1); });
+  mid();
   lstore(S0{}, 0);
   __syncthreads();
   for (int ks = 0; ks < nks; ks += 2) {

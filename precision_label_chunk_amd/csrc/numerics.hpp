@@ -154,7 +154,8 @@ __device__ __forceinline__ uint32_t rng_pick_hi(const u32x4& r, int e) {
 // g = sigmoid(z) - y = s / (1 + e^a) with a = -z, s = 1 (y = 0) or a = z, s = -1 (y = 1): the
 // cancellation-free forms. e^a = 2^(a log2 e) with the product carried to ~48 bits so that its
 // rounding does not reach the result, v_exp_f32, one correction of the exponent's low part, then
-// v_rcp_f32 refined by one Newton step: about 2 FP32 ulp overall, close to expf + IEEE division.
+// v_rcp_f32: about 3 FP32 ulp overall, some 2^-15 of a BF16 unit, so the BF16 gradient code
+// differs from the correctly rounded one only for values that close to a rounding boundary.
 // Where the reciprocal leaves the normal range (|z| > 80) the exact-division form is used.
 // the fast form, valid for |z| <= 80
 __device__ __forceinline__ float bce_grad_fast(float z, bool y) {
@@ -165,9 +166,7 @@ __device__ __forceinline__ float bce_grad_fast(float z, bool y) {
   const float pl = fmaf(a, L2E_HI, -p) + a * L2E_LO;           // p + pl = a log2 e
   float e = __builtin_amdgcn_exp2f(p);
   e = fmaf(e, pl * 0.693147180559945309f, e);                  // e * 2^pl
-  const float d = 1.0f + e;
-  float r = __builtin_amdgcn_rcpf(d);
-  r = fmaf(fmaf(-d, r, 1.0f), r, r);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
   return y ? -r : r;
 }
 

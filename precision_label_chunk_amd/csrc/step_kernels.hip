@@ -220,9 +220,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
   const int jbase = tile * TJ1;                // first label of the tile, relative to c0
   const int64_t rowbytes = (int64_t)D * ESZ;
 
-  for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
-  __syncthreads();
-  {
+  f32x16_t acc[MI][NI];
+  // the tile's positives into ybits while the first K slices load
+  auto scan = [&]() {
+    for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
+    __syncthreads();
     const uint64_t e0 = tile_off[tg];
     const uint64_t e1 = tile_off[tg + 1] < (uint64_t)bucket_cap ? tile_off[tg + 1] : (uint64_t)bucket_cap;
     for (uint64_t e = e0 + tid; e < e1; e += 256) {
@@ -230,10 +232,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
       uint32_t b = v >> 16, jl = v & (TJ1 - 1);
       if (b < (uint32_t)MB) atomicOr(&ybits[jl * (MB / 32) + (b >> 5)], 1u << (b & 31));
     }
-  }
-
-  f32x16_t acc[MI][NI];
-  fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj);
+  };
+  fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj, scan);
 
   // epilogue: gradient straight from the accumulators. A lane holds one label and 4 groups of 4
   // consecutive samples of each 32 x 32 block; packing pairs to BF16 and swapping groups 1 <-> 0 and
