@@ -709,8 +709,10 @@ KTState& kt() { static KTState s; return s; }
 hipEvent_t kt_event() {
   KTState& s = kt();
   if (!s.pool.empty()) { hipEvent_t e = s.pool.back(); s.pool.pop_back(); return e; }
+  // timing only: no system-scope fence (cache writeback and invalidation) when the event is recorded,
+  // which would otherwise add its cost between the launches it brackets
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 }  // namespace
