@@ -67,6 +67,9 @@ typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 __device__ __forceinline__ void buffer_store8(i32x2_t v, __amdgpu_buffer_rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
 
 // instruction-scheduling group (LLVM AMDGPU IGroupLP): N instructions of class MASK (0x2 VALU,
 // 0x8 MFMA, 0x100 LDS read, 0x200 LDS write, 0x20 VMEM read, 0x40 VMEM write), in program order of

@@ -134,14 +134,24 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint64_t seed) {
   return c;
 }
 
-// the 8 random 16-bit values of element block g = idx >> 3, packed two per word (seed wave-uniform)
+// The 8 random 16-bit values of element block g, packed two per word (seed wave-uniform). Within
+// each aligned group of 32 element indices, the 8 indices with equal bits 4 and 2 form block
+// g = 4 (idx >> 5) + 2 bit4 + bit2, in position order p = 4 bit3 + (idx & 3); position p takes
+// 16-bit half p & 1 of word p >> 1. (This is exactly the set of one 32 x 32 MFMA accumulator
+// lane's 8 features of one label and register group pair, so the update needs no lane exchange.)
 __device__ __forceinline__ u32x4 rng_block(uint64_t seed, uint64_t step, uint64_t g) {
   return philox4x32_10(philox_counter(g, step), seed);
 }
 
-__device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = idx & 7
+__device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = position p
   uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// the 16 random bits of element idx
+__device__ __forceinline__ uint32_t rng_r16(uint64_t seed, uint64_t step, uint64_t idx) {
+  const uint64_t g = 4 * (idx >> 5) + 2 * ((idx >> 4) & 1) + ((idx >> 2) & 1);
+  return rng_pick(rng_block(seed, step, g), (int)(4 * ((idx >> 3) & 1) + (idx & 3)));
 }
 
 // the same 16 bits placed in bits 31..16 (the form the SR instructions take)

@@ -16,7 +16,7 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
       case 4: ((uint8_t*)out)[i] = (uint8_t)sr_e4m3(((const float*)in0)[i], ((const uint32_t*)in1)[i] & 0xffffu); break;
       case 5: {
         const uint64_t idx = idx0 + (uint64_t)i;
-        ((uint32_t*)out)[i] = rng_pick(rng_block(seed, step, idx >> 3), (int)(idx & 7));
+        ((uint32_t*)out)[i] = rng_r16(seed, step, idx);
         break;
       }
       case 6: {

@@ -194,6 +194,48 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* __restrict__ l
 // ------------------------------------------------------------------------------------------------
 // forward + gradient: Z = X~ W_c^T, G = BF16(sigmoid(Z) - Y)
 // ------------------------------------------------------------------------------------------------
+// Gradient of one 32 x 32 accumulator block: lane (l32, hi) holds label l32 of the block and
+// samples bb + 8 (i/4) + 4 hi + i%4 in register i; yw holds the positives of samples bb .. bb+31 of
+// that label. Padding (samples >= B, labels past the chunk) gets 0. The exact form is needed only
+// for |z| > 80: one wave-uniform test per block keeps the common case free of branches.
+__device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, bool jvalid, int bb, int B, int hi,
+                                               float (&gv)[16]) {
+  bool big = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) big |= __builtin_fabsf(a[i]) > 80.0f;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+      gv[i] = jvalid && (bb + bl < B) ? bce_grad(a[i], (yw >> bl) & 1u) : 0.0f;
+    }
+  } else {
+    // (computed for every element, padding included, and selected: no branch per element)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+      const float g = bce_grad_fast(a[i], (yw >> bl) & 1u);
+      gv[i] = jvalid && (bb + bl < B) ? g : 0.0f;
+    }
+  }
+}
+
+// Packing pairs to BF16 and swapping register groups 1 <-> 0 and 3 <-> 2 across the lane halves
+// leaves 8 consecutive samples per lane and group pair, written with one 16-byte store each into
+// the label's row `grow` of the label-major chunk buffer G[label][sample].
+__device__ __forceinline__ void fwd_store_block(const float (&gv)[16], uint16_t* grow, int bb, int hi) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
+    const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+    *(i32x4_t*)(grow + bb + 16 * u + 8 * hi) = out;
+  }
+}
+
 template <int MB, int WF, bool LOSS, bool ZOUT>
 __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
                                                int D, int64_t c0, int clen,
@@ -235,10 +277,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
   };
   fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj, scan);
 
-  // epilogue: gradient straight from the accumulators. A lane holds one label and 4 groups of 4
-  // consecutive samples of each 32 x 32 block; packing pairs to BF16 and swapping groups 1 <-> 0 and
-  // 3 <-> 2 across the lane halves leaves 8 consecutive samples per lane and group pair, written
-  // with one 16-byte store into the label-major chunk buffer G[label][sample].
+  // epilogue: gradient straight from the accumulators, block by block
   float lsum = 0.0f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -249,26 +288,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
       const int bb = wb * RW + mi * 32;
       const uint32_t yw = ybits[jl * (MB / 32) + (bb >> 5)];
       float gv[16];
-      // the exact form is needed only for |z| > 80: one wave-uniform test per block keeps the
-      // common case free of branches
-      bool big = false;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) big |= __builtin_fabsf(acc[mi][ni][i]) > 80.0f;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
-          gv[i] = jvalid && (bb + bl < B) ? bce_grad(acc[mi][ni][i], (yw >> bl) & 1u) : 0.0f;
-        }
-      } else {
-        // (computed for every element, padding included, and selected: no branch per element)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
-          const float g = bce_grad_fast(acc[mi][ni][i], (yw >> bl) & 1u);
-          gv[i] = jvalid && (bb + bl < B) ? g : 0.0f;
-        }
-      }
+      fwd_grad_block(acc[mi][ni], yw, jvalid, bb, B, hi, gv);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -285,19 +305,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
           }
         }
       }
-      if constexpr (!ZOUT) {
-        uint32_t pk[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
-        uint16_t* grow = G + (int64_t)(jbase + jl) * gpitch;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
-          const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-          *(i32x4_t*)(grow + bb + 16 * u + 8 * hi) = out;
-        }
-      }
+      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)(jbase + jl) * gpitch, bb, hi);
     }
   if constexpr (LOSS) {
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
@@ -326,64 +334,59 @@ __device__ __forceinline__ int row_swz(int j) {
 }
 
 // The fused SGD step with stochastic rounding for one wave's 32 labels x 32 features, straight
-// from its dW accumulators. Lane (l32, hi) holds label l32 and features 8 (i/4) + 4 hi + i%4 in
-// register i; swapping register groups 1<->0 and 3<->2 across the two lane halves leaves features
-// [16u + 8hi, +8) for u = 0, 1 in each lane, which it updates with one Philox block each:
-// t = fmaf(-lr, dW, w), hardware stochastic rounding, one 16- or 8-byte store per 8 weights.
-// The work is cut into UPD_PHASES phases so that it can be spread between MFMAs: 0 the RNG
-// counters, 1..10 the Philox rounds (these RNG_PHASES need no dW), 11 the swaps, 12 old-weight
-// reads, 13..20 two weights each (rounding and packing; the last of each 8 also stores them).
-//   ow0/1 the old weights of those features (8 BF16 each, u = 0 / 1) in LDS
-//   roff  byte offset of the label's row in the chunk's weight resource, plus the feature offset of
-//         lane half `hi` (features dsl + dblk*32 + 8 hi)
-//   idx0  global element index of that first feature: (c0 + label) * D + feature
+// from its dW accumulators. Lane (l32, hi) holds label l32 and, in register 8u + p (u = 0, 1,
+// p = 0..7), feature 16u + 8 (p >> 2) + 4 hi + (p & 3) of the 32: for each u the 8 elements of one
+// RNG block (block 4 grp + 2u + hi, positions p in order, grp the index of the row's 32-element
+// group), which the lane updates with one Philox block: t = fmaf(-lr, dW, w), hardware stochastic
+// rounding. Swapping the packed results of block 1 of lane half 0 with those of block 0 of lane
+// half 1 leaves each lane the 16 consecutive features 16 hi .. 16 hi + 15 of its label, stored in
+// 16-byte pieces. The work is cut into UPD_PHASES phases so that it can be spread between MFMAs:
+// 0 the RNG counters, 1..10 the Philox rounds (these RNG_PHASES need no dW), 11 old-weight reads,
+// 12..19 two weights each (rounding and packing), 20 the exchange and the stores.
+//   ow    the label's W row in the LDS tile (BF16); owa/owb[u] element offsets of the runs
+//         16u + 4 hi and 16u + 8 + 4 hi of the wave's features in it
+//   roff  byte offset of the label's row in the chunk's weight resource plus that of the wave's
+//         first feature
+//   grp   (global element index of the wave's first feature in the label's row) >> 5
 constexpr int UPD_PHASES = 21, RNG_PHASES = 11;
 struct UpdState {
   u32x4 c[2];
   i32x4_t ow[2];
-  uint32_t pk[4];
+  uint32_t pk[8];                              // packed results: 4 words per block (BF16), 2 (E4M3)
 };
 
 template <int WF>
-__device__ __forceinline__ void upd_phase(int p, UpdState& st, f32x16_t& acc, const uint16_t* ow0,
-                                          const uint16_t* ow1, __amdgpu_buffer_rsrc_t wres, int roff,
-                                          uint64_t idx0, float lr, uint64_t seed, uint64_t step) {
+__device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& acc, const uint16_t* ow,
+                                          const int (&owa)[2], const int (&owb)[2], __amdgpu_buffer_rsrc_t wres,
+                                          int roff, uint64_t grp, int hi, float lr, uint64_t seed, uint64_t step) {
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   if (p == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) st.c[u] = philox_counter((idx0 + 16 * u) >> 3, step);
+    for (int u = 0; u < 2; ++u) st.c[u] = philox_counter(4 * grp + 2 * u + hi, step);
   } else if (p <= 10) {
     const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
     philox_round2(st.c[0], st.c[1], k0, k1);
   } else if (p == 11) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // (copy to scalars first: bit-casting an ext-vector element reference reads element 0)
-        const float lo_v = acc[8 * u + e], hi_v = acc[8 * u + 4 + e];
-        const auto sw = __builtin_amdgcn_permlane32_swap(f2u(lo_v), f2u(hi_v), false, false);
-        acc[8 * u + e] = u2f((uint32_t)sw[0]);
-        acc[8 * u + 4 + e] = u2f((uint32_t)sw[1]);
-      }
-  } else if (p == 12) {
-    st.ow[0] = *(const i32x4_t*)ow0;
-    st.ow[1] = *(const i32x4_t*)ow1;
-  } else {
-    const int u = (p - 13) >> 2, pr = (p - 13) & 3;          // weights 2 pr, 2 pr + 1 of block u
+    for (int u = 0; u < 2; ++u) {
+      const i32x2_t a = *(const i32x2_t*)(ow + owa[u]), b = *(const i32x2_t*)(ow + owb[u]);
+      st.ow[u] = i32x4_t{a[0], a[1], b[0], b[1]};
+    }
+  } else if (p < 20) {
+    const int u = (p - 12) >> 2, pr = (p - 12) & 3;          // positions 2 pr, 2 pr + 1 of block u
     const u32x4& rnd = st.c[u];
     const uint32_t wb = (uint32_t)st.ow[u][pr];
     const float t0 = fmaf(-lr, acc[8 * u + 2 * pr], u2f(wb << 16));
     const float t1 = fmaf(-lr, acc[8 * u + 2 * pr + 1], u2f(wb & 0xffff0000u));
-    const int off = roff + 16 * u * ESZ;
     if constexpr (WF == W_BF16_) {
-      const uint32_t lo = sr_bf16_into(0u, t0, rng_pick_hi(rnd, 2 * pr), false);
-      st.pk[pr] = sr_bf16_into(lo, t1, rng_pick_hi(rnd, 2 * pr + 1), true);
-      if (pr == 3)
-        buffer_store16(i32x4_t{(int)st.pk[0], (int)st.pk[1], (int)st.pk[2], (int)st.pk[3]}, wres, off);
+      // (the BF16 rounding uses bits 31..16 of its random operand only: the odd position takes its
+      // word as it is)
+      const uint32_t w = (pr >> 1) == 0 ? ((pr & 1) ? rnd.y : rnd.x) : ((pr & 1) ? rnd.w : rnd.z);
+      const uint32_t lo = sr_bf16_into(0u, t0, w << 16, false);
+      st.pk[4 * u + pr] = sr_bf16_into(lo, t1, w, true);
     } else {
-      // bytes 2 pr, 2 pr + 1 of the 8: dword pr >> 1, byte lanes 2 (pr & 1) and 2 (pr & 1) + 1
-      uint32_t o = (pr & 1) ? st.pk[pr >> 1] : 0u;
+      // bytes 2 (pr & 1), 2 (pr & 1) + 1 of the word of run pr >> 1
+      uint32_t o = (pr & 1) ? st.pk[2 * u + (pr >> 1)] : 0u;
       if (pr & 1) {
         o = sr_e4m3_into<2>(o, t0, rng_pick_hi(rnd, 2 * pr));
         o = sr_e4m3_into<3>(o, t1, rng_pick_hi(rnd, 2 * pr + 1));
@@ -391,8 +394,25 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, f32x16_t& acc, co
         o = sr_e4m3_into<0>(o, t0, rng_pick_hi(rnd, 2 * pr));
         o = sr_e4m3_into<1>(o, t1, rng_pick_hi(rnd, 2 * pr + 1));
       }
-      st.pk[pr >> 1] = o;
-      if (pr == 3) buffer_store8(i32x2_t{(int)st.pk[0], (int)st.pk[1]}, wres, off);
+      st.pk[2 * u + (pr >> 1)] = o;
+    }
+  } else {
+    // word k of block 0 (lane half 1) <-> word k of block 1 (lane half 0): then words x (own) and
+    // y (received) of each run are features 16 hi + 8 run + 0..3 and + 4..7
+    constexpr int NW = WF == W_BF16_ ? 4 : 2;
+    uint32_t x[NW], y[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(st.pk[k], st.pk[NW + k], false, false);
+      x[k] = (uint32_t)sw[0];
+      y[k] = (uint32_t)sw[1];
+    }
+    const int off = roff + 16 * hi * ESZ;
+    if constexpr (WF == W_BF16_) {
+      buffer_store16(i32x4_t{(int)x[0], (int)x[1], (int)y[0], (int)y[1]}, wres, off);
+      buffer_store16(i32x4_t{(int)x[2], (int)x[3], (int)y[2], (int)y[3]}, wres, off + 16);
+    } else {
+      buffer_store16(i32x4_t{(int)x[0], (int)y[0], (int)x[1], (int)y[1]}, wres, off);
     }
   }
 }
@@ -504,11 +524,16 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     for (int k = 0; k < NOB; ++k)
       offB[w][k] = (jX + 4 * w) * MB + 32 * ((nb0 + k) ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
   }
-  //   update: old weights of W row jb*32 + l32, chunks 4 dblk + 2u + hi
+  //   update: old weights of W row jb*32 + l32, features dblk*32 + 16u + 4hi (chunk 4 dblk + 2u) and
+  //   + 8 (chunk 4 dblk + 2u + 1), 4 each at element 4 hi of the chunk
   const int sU = row_swz<DS / 8>(l32);
-  const int offU0 = l32 * DS + (((4 * dblk + hi) ^ sU) << 3);
-  const int offU1 = l32 * DS + (((4 * dblk + 2 + hi) ^ sU) << 3);
-  const int fU = dsl + dblk * 32 + 8 * hi;                     // this lane's first update feature
+  int offUA[2], offUB[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    offUA[u] = l32 * DS + (((4 * dblk + 2 * u) ^ sU) << 3) + 4 * hi;
+    offUB[u] = l32 * DS + (((4 * dblk + 2 * u + 1) ^ sU) << 3) + 4 * hi;
+  }
+  const int fU = dsl + dblk * 32;                              // the wave's first feature
 
   // Staging of the next tile through registers, one 16-byte chunk per item: items 0 .. GPT-1 are
   // G chunks (thread chunk ci = tid + c * NT is row ci / GCPR, chunk ci % GCPR: coalesced reads),
@@ -555,9 +580,9 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   auto upd_args = [&](auto PH, UpdState& st, const uint16_t* wsU, int tU) {
     constexpr int ph = decltype(PH)::value, jl = ph / UPD_PHASES;
     const int jb = jb0 + jl;
-    upd_phase<WF>(ph % UPD_PHASES, st, accP[jl], wsU + offU0 + jb * 32 * DS, wsU + offU1 + jb * 32 * DS, wres,
+    upd_phase<WF>(ph % UPD_PHASES, st, accP[jl], wsU + jb * 32 * DS, offUA, offUB, wres,
                   (tU * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
-                  (uint64_t)(c0 + tU * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU, lr, seed, step);
+                  ((uint64_t)(c0 + tU * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU) >> 5, hi, lr, seed, step);
   };
   auto update = [&](int tU, int wbU) {         // the whole update of tile tU, in sequence
     UpdState st;

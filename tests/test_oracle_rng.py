@@ -67,12 +67,25 @@ def test_philox_zero_block_known_value(orc, rocrand_kat):
     assert orc.philox4x32(np.zeros(4, np.uint32), np.zeros(2, np.uint32), 10)[0] == 0x6627E8D5
 
 
+def _block_elements(g):
+    # the 8 element indices of block g, in position order p = 0..7: group g >> 2 of 32 indices,
+    # index bits 4 and 2 from g & 3, bit 3 and bits 1..0 from p
+    base, q = 32 * (g >> 2), g & 3
+    return [base + 16 * (q >> 1) + 4 * (q & 1) + 8 * (p >> 2) + (p & 3) for p in range(8)]
+
+
 def test_r16_slices_the_block(orc, rocrand_kat):
-    # element idx uses 16-bit half (idx & 1) of word ((idx >> 1) & 3) of block idx >> 3
+    # element at position p of block g uses 16-bit half (p & 1) of word p >> 1 of that block
     for (s, step, g), ref in zip(TRIPLES, rocrand_kat):
-        r = orc.r16(s, step, 8 * g, 8)
-        halves = np.array([(int(ref[i // 2]) >> (16 * (i % 2))) & 0xFFFF for i in range(8)], np.uint32)
-        assert np.array_equal(r, halves)
+        halves = [(int(ref[p // 2]) >> (16 * (p % 2))) & 0xFFFF for p in range(8)]
+        for p, idx in enumerate(_block_elements(g)):
+            assert int(orc.r16(s, step, idx, 1)[0]) == halves[p], (s, step, g, p)
+
+
+def test_r16_blocks_partition_the_indices():
+    # every index of a 32-group belongs to exactly one of its 4 blocks
+    seen = sorted(i for q in range(4) for i in _block_elements(4 * 5 + q))
+    assert seen == list(range(32 * 5, 32 * 6))
 
 
 def test_r16_statistics(orc):
