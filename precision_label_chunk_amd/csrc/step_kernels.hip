@@ -475,9 +475,12 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dblk = wave % NFB, h = wave / NFB;  // feature block, wave half
   const int l32 = lane & 31, hi = lane >> 5, q = lane >> 4, li = lane & 15;
-  // work-groups of one label range share its G tiles: keep them on one XCD (dispatch is round-robin)
+  // work-groups of one label range share its G tiles: dispatch is round-robin over the 8 XCDs, so
+  // number the (range, slice) pairs XCD-major, consecutive on each XCD; at most one range per XCD
+  // boundary is split between two L2s
   const int g = blockIdx.x, xcd = g & 7, kq = g >> 3;
-  const int r = (kq / NS) * 8 + xcd, s = kq % NS;
+  const int lin = xcd * (int)(gridDim.x >> 3) + kq;
+  const int r = lin / NS, s = lin % NS;
   if (r >= NR) return;
   const int nt = (clen + TJ2 - 1) / TJ2;
   const int t0 = (int)((int64_t)nt * r / NR), t1 = (int)((int64_t)nt * (r + 1) / NR);
@@ -497,9 +500,19 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) xT[kk] = *(const s16x8_t*)(XbT + (int64_t)d * MB + kk * 16 + hi * 8);
   }
+  // dX^T accumulators, starting from this range's running partial sum (fixed slot per range:
+  // deterministic; zero in the step's first chunk, where every slot has a range), which is read
+  // here, under the first tile's staging, and stored back at the end
   f32x16_t accX[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) accX[nb] = f32x16_t{};
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int b = (nb0 + nb) * 32 + l32;
+      const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
+      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
+      accX[nb][4 * ig] = o[0]; accX[nb][4 * ig + 1] = o[1]; accX[nb][4 * ig + 2] = o[2]; accX[nb][4 * ig + 3] = o[3];
+    }
 
   // loop-invariant LDS element offsets (rows of both label blocks share the swizzle: it only
   // depends on the row's low 4 bits)
@@ -702,21 +715,15 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     }
   }
 
-  // this range's dX contribution, accumulated in place (fixed slot per range: deterministic); the
-  // step's first chunk writes its slot instead (every slot has a range there)
+  // the range's running dX partial back to its slot
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
       const int b = (nb0 + nb) * 32 + l32;
       const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
-      f32x4_t* pp = (f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
-      f32x4_t v = {accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
-      if (!first) {
-        const f32x4_t o = *pp;
-        v[0] = o[0] + v[0]; v[1] = o[1] + v[1]; v[2] = o[2] + v[2]; v[3] = o[3] + v[3];
-      }
-      *pp = v;
+      *(f32x4_t*)(part + ((int64_t)r * MB + b) * D + d) =
+          f32x4_t{accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
     }
 }
 
@@ -799,13 +806,12 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   if (c > cmax) c = cmax;
   s.Cc = c;
   s.ntiles = (L + TJ1 - 1) / TJ1;
-  // backward work-groups hold a whole CU (LDS) and those of one label range share an XCD: give
-  // each of the 8 XCDs at most as many work-groups as it has CUs, so the launch is one round
+  // backward work-groups hold a whole CU (LDS and registers): at most as many (range, slice)
+  // work-groups as CUs, so the launch is one round; they are laid out XCD-major (see the kernel)
   int64_t nt2 = (c + TJ2 - 1) / TJ2;
   s.cus = device_cus();
-  int per_xcd = (s.cus / 8) / s.NS;
-  if (per_xcd < 1) per_xcd = 1;
-  const int cap = 8 * per_xcd;
+  int cap = s.cus / s.NS;
+  if (cap < 1) cap = 1;
   s.NR = (int)(nt2 < cap ? nt2 : cap);
   size_t off = 0;
   const size_t A = 256;
@@ -855,7 +861,7 @@ static int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipSt
     kt_end(KT_FWD, st);
     const int nt2 = (clen + TJ2 - 1) / TJ2;
     const int NR = nt2 < s.NR ? nt2 : s.NR;
-    const int grid2 = 8 * s.NS * ((NR + 7) / 8);
+    const int grid2 = 8 * ((NR * s.NS + 7) / 8);
     const int first = c0 == a.l0 && NR == s.NR;    // writes every partial slot: no zero fill needed
     kt_begin(KT_BWD, st, clen);
     // two waves per feature block where the batch has at least two sample blocks
