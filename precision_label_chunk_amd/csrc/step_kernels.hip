@@ -167,13 +167,23 @@ __global__ void k_prep_x(const uint16_t* __restrict__ X, int B, int D, int MB, u
   }
 }
 
-// dX[b][d] = sum over label ranges r (fixed order) of the FP32 partials
+// dX[b][d] = sum over label ranges r (fixed order) of the FP32 partials. A range's partial holds
+// the backward's 32 x 32 dX^T accumulator blocks: element p = (((fb * NB + sb) * 4 + ig) * 64 +
+// lane) * 4 + e (feature block fb, sample block sb) is register i = 4 ig + e of that lane, feature
+// 32 fb + 8 ig + 4 (lane / 32) + e of sample 32 sb + lane % 32.
 __global__ void k_dx_reduce(const float* __restrict__ part, int NR, int MB, int D, int B, float* __restrict__ dX) {
-  const int64_t n = (int64_t)B * D;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t n = (int64_t)MB * D;
+  const int NB = MB / 32;
+  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < n; p += (int64_t)gridDim.x * blockDim.x) {
+    const int e = (int)(p & 3), lane = (int)((p >> 2) & 63), ig = (int)((p >> 8) & 3);
+    const int64_t blk = p >> 10;
+    const int sb = (int)(blk % NB), fb = (int)(blk / NB);
+    const int b = 32 * sb + (lane & 31);
+    if (b >= B) continue;
+    const int d = 32 * fb + 8 * ig + 4 * (lane >> 5) + e;
     float s = 0.0f;
-    for (int r = 0; r < NR; ++r) s += part[(int64_t)r * MB * D + i];
-    dX[i] = s;
+    for (int r = 0; r < NR; ++r) s += part[(int64_t)r * n + p];
+    dX[(int64_t)b * D + d] = s;
   }
 }
 
@@ -500,17 +510,18 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) xT[kk] = *(const s16x8_t*)(XbT + (int64_t)d * MB + kk * 16 + hi * 8);
   }
-  // dX^T accumulators, starting from this range's running partial sum (fixed slot per range:
-  // deterministic; zero in the step's first chunk, where every slot has a range), which is read
-  // here, under the first tile's staging, and stored back at the end
+  // dX^T accumulators, starting from this range's running partial sum (a fixed slot per range:
+  // deterministic; zero in the step's first chunk, where every slot has a range), read here under
+  // the first tile's staging and stored back at the end. The partial keeps the accumulators' own
+  // layout, lane l's registers 4 ig .. 4 ig + 3 of sample block sb at ((sb * 4 + ig) * 64 + l) * 4
+  // within the wave's feature block, so that every access is 1 KiB contiguous.
+  float* slot = part + ((int64_t)r * (D / 32) + (dsl / 32 + dblk)) * (MB * 32) + 4 * lane;
   f32x16_t accX[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const int b = (nb0 + nb) * 32 + l32;
-      const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
-      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)(part + ((int64_t)r * MB + b) * D + d);
+      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)(slot + ((nb0 + nb) * 4 + ig) * 256);
       accX[nb][4 * ig] = o[0]; accX[nb][4 * ig + 1] = o[1]; accX[nb][4 * ig + 2] = o[2]; accX[nb][4 * ig + 3] = o[3];
     }
 
@@ -720,9 +731,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const int b = (nb0 + nb) * 32 + l32;
-      const int d = dsl + dblk * 32 + 8 * ig + 4 * hi;
-      *(f32x4_t*)(part + ((int64_t)r * MB + b) * D + d) =
+      *(f32x4_t*)(slot + ((nb0 + nb) * 4 + ig) * 256) =
           f32x4_t{accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
     }
 }
@@ -928,7 +937,7 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   }
   if (rc != ELMO_OK_ || a.forward_only()) return rc;
   {
-    const int64_t n = (int64_t)a.B * a.D;
+    const int64_t n = (int64_t)s.MB * a.D;
     const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
     hipLaunchKernelGGL(k_dx_reduce, dim3(blocks), dim3(256), 0, st, (const float*)(ws + s.part), s.NR, s.MB,
                        a.D, a.B, a.dX);
