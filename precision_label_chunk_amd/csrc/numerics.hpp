@@ -29,9 +29,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// two values packed low / high
+// two values packed low / high, each rounded as above (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
 }
 
 // ---- OCP E4M3 (E4M3FN) --------------------------------------------------------------------------
@@ -167,18 +169,25 @@ __device__ __forceinline__ uint32_t rng_pick_hi(const u32x4& r, int e) {
 // v_rcp_f32: about 3 FP32 ulp overall, some 2^-15 of a BF16 unit, so the BF16 gradient code
 // differs from the correctly rounded one only for values that close to a rounding boundary.
 // Where the reciprocal leaves the normal range (|z| > 80) the exact-division form is used.
-// the fast form, valid for |z| <= 80
-__device__ __forceinline__ float bce_grad_fast(float z, bool y) {
-  const float a = y ? z : -z;
+// the fast form, valid for |z| <= 80, with the label as a sign mask: bit 31 of ys set for y = 1
+// (the sign flips of a and of the result are then one bit operation each)
+__device__ __forceinline__ float bce_grad_fast_m(float z, uint32_t ys) {
   constexpr float L2E_HI = 1.44269502162933349609375f;         // FP32(log2 e)
-  constexpr float L2E_LO = 1.925962989e-08f;                   // log2 e - L2E_HI
+  constexpr float LN2 = 0.693147180559945309f;
+  constexpr float L2E_LO_LN2 = 1.33498838e-08f;                // (log2 e - L2E_HI) ln 2
+  // bitop3 truth tables index (src0, src1, src2) as bits (2, 1, 0): 0xD2 = s0 ^ (~s1 & s2),
+  // 0x78 = s0 ^ (s1 & s2)
+  const float a = u2f(__builtin_amdgcn_bitop3_b32(f2u(z), ys, 0x80000000u, 0xD2));   // -z (y = 0), z (y = 1)
   const float p = a * L2E_HI;
-  const float pl = fmaf(a, L2E_HI, -p) + a * L2E_LO;           // p + pl = a log2 e
+  const float t = fmaf(a, L2E_HI, -p);                         // exact: a L2E_HI - p
+  const float c = fmaf(t, LN2, a * L2E_LO_LN2);                // (a log2 e - p) ln 2
   float e = __builtin_amdgcn_exp2f(p);
-  e = fmaf(e, pl * 0.693147180559945309f, e);                  // e * 2^pl
+  e = fmaf(e, c, e);                                           // e^a = 2^p e^c
   const float r = __builtin_amdgcn_rcpf(1.0f + e);
-  return y ? -r : r;
+  return u2f(__builtin_amdgcn_bitop3_b32(f2u(r), ys, 0x80000000u, 0x78));          // r (y = 0), -r (y = 1)
 }
+
+__device__ __forceinline__ float bce_grad_fast(float z, bool y) { return bce_grad_fast_m(z, y ? 0x80000000u : 0u); }
 
 // the exact-division form, for |z| > 80
 __device__ __forceinline__ float bce_grad_slow(float z, bool y) {

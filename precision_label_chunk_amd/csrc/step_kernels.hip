@@ -207,25 +207,24 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* __restrict__ l
 // Gradient of one 32 x 32 accumulator block: lane (l32, hi) holds label l32 of the block and
 // samples bb + 8 (i/4) + 4 hi + i%4 in register i; yw holds the positives of samples bb .. bb+31 of
 // that label. Padding (samples >= B, labels past the chunk) gets 0. The exact form is needed only
-// for |z| > 80: one wave-uniform test per block keeps the common case free of branches.
+// for |z| > 80: one wave-uniform test per block (every |z| <= 80, every sample and label valid)
+// keeps the common case free of branches and selects.
 __device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, bool jvalid, int bb, int B, int hi,
                                                float (&gv)[16]) {
-  bool big = false;
+  float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) big |= __builtin_fabsf(a[i]) > 80.0f;
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, __builtin_fabsf(a[i]));
+  const bool common = m <= 80.0f && jvalid && bb + 32 <= B;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!common) == 0, 1)) {
+    // every element in range and valid: no select; label bit bl of yw moved to bit 31
+    const uint32_t yh = yw >> (4 * hi);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gv[i] = bce_grad_fast_m(a[i], yh << (31 - (8 * (i >> 2) + (i & 3))));
+  } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
       gv[i] = jvalid && (bb + bl < B) ? bce_grad(a[i], (yw >> bl) & 1u) : 0.0f;
-    }
-  } else {
-    // (computed for every element, padding included, and selected: no branch per element)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
-      const float g = bce_grad_fast(a[i], (yw >> bl) & 1u);
-      gv[i] = jvalid && (bb + bl < B) ? g : 0.0f;
     }
   }
 }
