@@ -5,6 +5,10 @@
 // 128 x 128 score tiles on the matrix cores (the same forward tile as the training step), stages
 // each tile in LDS and lets two threads per sample keep running top-KK lists in registers (KK is k
 // rounded up to 8 or 32). Lists are ordered by (score desc, label asc) with NaN after numbers.
+// Each list publishes its last entry's score in LDS as a bound: a tile's scores are first tested
+// against the bounds in registers, and only those that may enter a list (usually none, once the
+// lists have filled) go through an LDS queue to their list's thread; a tile with more such
+// candidates than the queue holds takes the full path (the whole score tile through LDS).
 // A second kernel merges the per-range lists of each sample.
 #include <float.h>
 
@@ -16,6 +20,7 @@
 namespace elmo {
 
 constexpr int TN = 128;                 // samples per work-group
+constexpr int QCAP = 256;               // candidate queue entries per tile
 
 __device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb) {
   const bool na = sa != sa, nb = sb != sb;
@@ -51,6 +56,12 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
   constexpr int KS = 64;
   constexpr int SMEM = MB * SP * 4 > fwd_smem_bytes(MB, KS) ? MB * SP * 4 : fwd_smem_bytes(MB, KS);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];   // operand stages, then the score tile
+  // bound[h][n]: score of the last entry of sample n's list for label half h (NaN while not full)
+  __shared__ __attribute__((aligned(16))) float bound[2][MB];
+  __shared__ uint32_t qkey[QCAP];       // candidates: sample | half << 7 | label in tile << 8
+  __shared__ float qscore[QCAP];
+  __shared__ uint32_t qcount;
+  __shared__ uint32_t wcand[4];         // per wave: it had candidates this tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wb = wave >> 1, wj = wave & 1, l32 = lane & 31, hi = lane >> 5;
@@ -66,30 +77,112 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
   list_init<KK>(ls, lj);
   const int srow = tid >> 1, half = tid & 1;
   float* sc = (float*)smem;
+  bound[half][srow] = __builtin_nanf("");
+  if (tid == 0) qcount = 0u;            // (the first tile's barriers order these before use)
 
   for (int64_t t = t0; t < t1; ++t) {
     const int64_t j0 = t * TJ1;
     const int nvalid = (int)((L - j0) < TJ1 ? (L - j0) : TJ1);
     f32x16_t acc[MI][NI];
     fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj, [] {});
+
+    if constexpr (KK <= 8) {
+      // candidates: a score may enter its list only if the list's bound is NaN or not above it
+      // (a bound from an earlier tile is a lower one, so it never drops a candidate). Wave (wb, wj)
+      // holds samples wb * RW .. + RW - 1 and label half wj (CW = 64) of the tile.
+      uint32_t cm[MI * NI];               // candidate bits, register i of block (mi, ni)
+      int cnt = 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        const int nb = wb * RW + mi * 32 + 4 * hi;
+        f32x4_t bq[4];
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
+        for (int q = 0; q < 4; ++q) bq[q] = *(const f32x4_t*)&bound[wj][nb + 8 * q];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int n = wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const int jl = wj * CW + ni * 32 + l32;
-          sc[n * SP + jl] = acc[mi][ni][i];
+        for (int ni = 0; ni < NI; ++ni) {
+          const bool jin = wj * CW + ni * 32 + l32 < nvalid;
+          uint32_t m = 0u;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float b = bq[i >> 2][i & 3], z = acc[mi][ni][i];
+            m |= (uint32_t)(jin && (b != b || z >= b)) << i;
+          }
+          cm[mi * NI + ni] = m;
+          cnt += __builtin_popcount(m);
         }
-    __syncthreads();
-    const int jend = nvalid < (half + 1) * 64 ? nvalid : (half + 1) * 64;
-    for (int jl = half * 64; jl < jend; ++jl) {
-      const float s = sc[srow * SP + jl];
-      const int j = (int)(j0 + jl);
-      if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+      }
+      // a wave with candidates queues them (as far as the queue goes) and writes its scores to
+      // the score tile, for the full path
+      const bool wany = __builtin_amdgcn_ballot_w64(cnt > 0) != 0;
+      if (wany) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              sc[(wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3)) * SP + wj * CW + ni * 32 + l32] = acc[mi][ni][i];
+        // the lane's candidates, read back from its own score tile entries
+        uint32_t k = cnt > 0 ? atomicAdd(&qcount, (uint32_t)cnt) : 0u;
+#pragma unroll
+        for (int b = 0; b < MI * NI; ++b) {
+          uint32_t m = cm[b];
+          while (m != 0u) {
+            const int i = __builtin_ctz(m);
+            m &= m - 1u;
+            const int n = wb * RW + (b / NI) * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const int jl = wj * CW + (b % NI) * 32 + l32;
+            if (k < (uint32_t)QCAP) {
+              qkey[k] = (uint32_t)n | ((uint32_t)wj << 7) | ((uint32_t)jl << 8);
+              qscore[k] = sc[n * SP + jl];
+            }
+            ++k;
+          }
+        }
+      }
+      if (lane == 0) wcand[wave] = wany ? 1u : 0u;
+      __syncthreads();
+      const uint32_t nq = qcount;
+      if (nq <= (uint32_t)QCAP) {
+        // few candidates: each list's thread takes its own from the queue
+        const uint32_t key = (uint32_t)srow | ((uint32_t)half << 7);
+        for (uint32_t e = 0; e < nq; ++e) {
+          const uint32_t v = qkey[e];
+          if ((v & 0xffu) == key) {
+            const float s = qscore[e];
+            const int j = (int)(j0 + (v >> 8));
+            if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+          }
+        }
+      } else if (wcand[(srow / RW) * 2 + half]) {
+        // the row half from the score tile (written by the one wave that holds it)
+        const int jend = nvalid < (half + 1) * 64 ? nvalid : (half + 1) * 64;
+        for (int jl = half * 64; jl < jend; ++jl) {
+          const float s = sc[srow * SP + jl];
+          const int j = (int)(j0 + jl);
+          if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+        }
+      }
+    } else {
+      // (longer lists: registers are short for the candidate test; always the full path)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sc[(wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3)) * SP + wj * CW + ni * 32 + l32] = acc[mi][ni][i];
+      __syncthreads();
+      const int jend = nvalid < (half + 1) * 64 ? nvalid : (half + 1) * 64;
+      for (int jl = half * 64; jl < jend; ++jl) {
+        const float s = sc[srow * SP + jl];
+        const int j = (int)(j0 + jl);
+        if (ranks_before(s, j, ls[KK - 1], lj[KK - 1])) list_insert<KK>(ls, lj, s, j);
+      }
     }
-    __syncthreads();                    // scores consumed before the next tile's staging
+    bound[half][srow] = ls[KK - 1];
+    __syncthreads();                    // scores and queue consumed before the next tile's staging
+    if (tid == 0) qcount = 0u;
   }
 
   // merge the two half lists of each sample through LDS, then write this range's candidates

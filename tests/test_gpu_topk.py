@@ -88,3 +88,28 @@ def test_topk_nan_scores_rank_last(elmo, orc):
     idx, sc = elmo.topk(to_dev_codes(W0), _xdev(X), 4)
     idx_r, sc_r = orc.topk(wk.W_BF16, W0, X, 4)
     assert np.array_equal(idx.cpu().numpy(), idx_r)
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_topk_many_tiles_per_range(elmo, orc, wfmt):
+    """4096 queries over 60k labels: each work-group scans some 30 label tiles, so the lists fill
+    and later tiles take the bounded-candidate path (lists of up to 8). Its top-8 must equal, bit for
+    bit, the first 8 of the top-32 (lists of 32 always take the full score-tile path), and sampled
+    queries must match the oracle. Duplicated weight rows across tiles force exact ties."""
+    N, D, L = 4096, 64, 60000
+    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
+    W0 = wk.make_weights(wl).copy()
+    for a, b in [(5, 40000), (12345, 129), (59999, 0), (777, 778)]:
+        W0[b] = W0[a]
+    X = wk.make_eval_x(wl, N)
+    Wd, Xd = to_dev_codes(W0), _xdev(X)
+    print(f"  topk N={N} D={D} L={L} wfmt={wfmt}", flush=True)
+    i8, s8 = elmo.topk(Wd, Xd, 8)
+    i32, s32 = elmo.topk(Wd, Xd, 32)
+    i8, s8, i32, s32 = i8.cpu().numpy(), s8.cpu().numpy(), i32.cpu().numpy(), s32.cpu().numpy()
+    assert np.array_equal(i32[:, :8], i8)
+    assert np.array_equal(s32[:, :8].view(np.uint32), s8.view(np.uint32))
+    qs = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4094, 4095], np.random.default_rng(9).integers(0, N, 25)]))
+    idx_r, sc_r = orc.topk(wfmt, W0, X[qs], 8)
+    Zfull = orc.logits(wfmt, W0, X[qs], np.arange(L))
+    _check(i8[qs], s8[qs], idx_r, sc_r, Zfull, RTOL[wfmt])
