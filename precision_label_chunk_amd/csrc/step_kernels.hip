@@ -514,13 +514,22 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   // the first tile's staging and stored back at the end. The partial keeps the accumulators' own
   // layout, lane l's registers 4 ig .. 4 ig + 3 of sample block sb at ((sb * 4 + ig) * 64 + l) * 4
   // within the wave's feature block, so that every access is 1 KiB contiguous.
-  float* slot = part + ((int64_t)r * (D / 32) + (dsl / 32 + dblk)) * (MB * 32) + 4 * lane;
+  // With four sample blocks per wave and an even number of feature blocks, each wave takes a 2 x 2
+  // square of (feature block, sample block) pairs instead of one feature block's four sample
+  // blocks, so that every A (W^T) and B (G^T) fragment feeds two MFMAs: 4 fragment reads per 4
+  // MFMAs instead of 5. Accumulator a holds feature block xfb(a) of the slice, sample block xsb(a).
+  constexpr bool SQ = NH == 2 && NBW == 4 && NFB % 2 == 0;
+  const int fp = SQ ? wave % (NFB / 2) : 0, sp = SQ ? wave / (NFB / 2) : 0;
+  auto xfb = [&](int a) { return SQ ? 2 * fp + (a >> 1) : dblk; };
+  auto xsb = [&](int a) { return SQ ? 2 * sp + (a & 1) : nb0 + a; };
+  float* slot = part + (int64_t)r * (D / 32) * (MB * 32) + 4 * lane;
+  auto pslot = [&](int a, int ig) { return slot + (dsl / 32 + xfb(a)) * (MB * 32) + (xsb(a) * 4 + ig) * 256; };
   f32x16_t accX[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)(slot + ((nb0 + nb) * 4 + ig) * 256);
+      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)pslot(nb, ig);
       accX[nb][4 * ig] = o[0]; accX[nb][4 * ig + 1] = o[1]; accX[nb][4 * ig + 2] = o[2]; accX[nb][4 * ig + 3] = o[3];
     }
 
@@ -533,19 +542,26 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   for (int k = 0; k < NOW; ++k) offW[k] = (jb0 * 32 + l32) * MB + 8 * (hi ^ (gW & 1)) + 16 * (k ^ (gW >> 1));
   //   dX operands (transposing reads): rows jX and jX + 4 of each 16-label K step
   const int jX = 8 * (q >> 1) + (li >> 2);
-  //     A = W^T: features dblk*32 + 16 (q&1) + 4 (li&3) .. +3
-  const int cA = 4 * dblk + 2 * (q & 1) + ((li & 3) >> 1);
-  const int offA0 = jX * DS + ((cA ^ row_swz<DS / 8>(jX)) << 3) + 4 * (li & 1);
-  const int offA1 = (jX + 4) * DS + ((cA ^ row_swz<DS / 8>(jX + 4)) << 3) + 4 * (li & 1);
+  //     A = W^T: features 32 fb + 16 (q&1) + 4 (li&3) .. +3 of feature block fb = xfb(2 fi)
+  constexpr int NAF = SQ ? 2 : 1;
+  int offA0[NAF], offA1[NAF];
+#pragma unroll
+  for (int fi = 0; fi < NAF; ++fi) {
+    const int cA = 4 * xfb(2 * fi) + 2 * (q & 1) + ((li & 3) >> 1);
+    offA0[fi] = jX * DS + ((cA ^ row_swz<DS / 8>(jX)) << 3) + 4 * (li & 1);
+    offA1[fi] = (jX + 4) * DS + ((cA ^ row_swz<DS / 8>(jX + 4)) << 3) + 4 * (li & 1);
+  }
   //     B = G^T: samples 32 nb + 16 (q&1) + 4 (li&3) .. +3; swizzled chunk 4 (nb ^ (s>>2)) + (c ^ (s&3))
+  //     for sample block nb = xsb(k) (k < NOB; further blocks of the same residue mod 4 by offset)
   const int cBl = 2 * (q & 1) + ((li & 3) >> 1);
-  int offB[2][NOB];
+  constexpr int NOBX = SQ ? 2 : NOB;
+  int offB[2][NOBX];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const int sB = row_swz<MB / 8>(jX + 4 * w);
 #pragma unroll
-    for (int k = 0; k < NOB; ++k)
-      offB[w][k] = (jX + 4 * w) * MB + 32 * ((nb0 + k) ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
+    for (int k = 0; k < NOBX; ++k)
+      offB[w][k] = (jX + 4 * w) * MB + 32 * (xsb(k) ^ (sB >> 2)) + ((cBl ^ (sB & 3)) << 3) + 4 * (li & 1);
   }
   //   update: old weights of W row jb*32 + l32, features dblk*32 + 16u + 4hi (chunk 4 dblk + 2u) and
   //   + 8 (chunk 4 dblk + 2u + 1), 4 each at element 4 hi of the chunk
@@ -627,16 +643,19 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
       const int jl = m % NJB, kk = m / NJB;
       return *(const s16x8_t*)(gs + offW[kk % NOW] + 16 * (kk - kk % NOW) + jl * 32 * MB);
     };
-    auto rdXa = [&](int kx) {
-      return join(lds_read_tr16(ws + offA0 + kx * 16 * DS), lds_read_tr16(ws + offA1 + kx * 16 * DS));
+    auto rdXa = [&](int kx, int fi) {          // A of K step kx, feature block xfb(2 fi)
+      return join(lds_read_tr16(ws + offA0[fi] + kx * 16 * DS), lds_read_tr16(ws + offA1[fi] + kx * 16 * DS));
     };
     auto rdXb = [&](int m) {                   // dX MFMA m: K step m / NBW, sample block nb0 + m % NBW
       const int kx = m / NBW, nb = m % NBW, k = nb % NOB, o = 32 * (nb - k) + kx * 16 * MB;
       return join(lds_read_tr16(gs + offB[0][k] + o), lds_read_tr16(gs + offB[1][k] + o));
     };
+    auto rdXb2 = [&](int kx, int si) {         // B of K step kx, sample block xsb(si) (square blocking)
+      return join(lds_read_tr16(gs + offB[0][si] + kx * 16 * MB), lds_read_tr16(gs + offB[1][si] + kx * 16 * MB));
+    };
     UpdState st;
     const uint16_t* wsP = Ws[wbP];
-    s16x8_t opW[NDW], opXb[NDX], opXa[KXN];
+    s16x8_t opW[NDW], opXb[NDX], opXa[KXN], opXa2[KXN][2], opXb2[KXN][2];
     f32x16_t accW[NJB];
 #pragma unroll
     for (int jl = 0; jl < NJB; ++jl) accW[jl] = f32x16_t{};
@@ -645,8 +664,15 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
       constexpr int z = decltype(Z)::value, m = z >> 1;
       if constexpr ((z & 1) == 0) {
         opW[m] = rdW(m);
+      } else if constexpr (SQ) {
+        // accumulator a = m % 4 of K step m / 4: (feature block a >> 1, sample block a & 1); each
+        // fragment is read for the first MFMA that uses it
+        constexpr int kx = m / 4, a = m % 4;
+        if constexpr (a == 0) { opXa2[kx][0] = rdXa(kx, 0); opXb2[kx][0] = rdXb2(kx, 0); }
+        else if constexpr (a == 1) opXb2[kx][1] = rdXb2(kx, 1);
+        else if constexpr (a == 2) opXa2[kx][1] = rdXa(kx, 1);
       } else {
-        if constexpr (m % NBW == 0) opXa[m / NBW] = rdXa(m / NBW);
+        if constexpr (m % NBW == 0) opXa[m / NBW] = rdXa(m / NBW, 0);
         opXb[m] = rdXb(m);
       }
     };
@@ -666,6 +692,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
           if constexpr (S0 + decltype(K)::value * (NSLOT - S0) / NLD == z) store_item(K, gnext, wbn);
         });
       if constexpr ((z & 1) == 0) accW[m % NJB] = mfma_bf16(xT[m / NJB], opW[m], accW[m % NJB]);
+      else if constexpr (SQ) accX[m % 4] = mfma_bf16(opXa2[m / 4][(m % 4) >> 1], opXb2[m / 4][m & 1], accX[m % 4]);
       else accX[m % NBW] = mfma_bf16(opXa[m / NBW], opXb[m], accX[m % NBW]);
       if constexpr (UPD) {
         // update phases ph with floor(ph * NSLOT / NPH) == z
@@ -730,7 +757,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      *(f32x4_t*)(slot + ((nb0 + nb) * 4 + ig) * 256) =
+      *(f32x4_t*)pslot(nb, ig) =
           f32x4_t{accX[nb][4 * ig], accX[nb][4 * ig + 1], accX[nb][4 * ig + 2], accX[nb][4 * ig + 3]};
     }
 }
