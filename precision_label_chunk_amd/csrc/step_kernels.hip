@@ -77,21 +77,30 @@ __global__ __launch_bounds__(256) void k_label_count(const int32_t* __restrict__
     if (h[t]) atomicAdd(&tile_cnt[t], h[t]);
 }
 
-// exclusive scan of the per-tile counts (one work-group of 1024 threads, 4096-entry segments with a
-// running carry); cnt becomes the scatter cursor and off[ntiles] the total
+// exclusive scan of the per-tile counts by one work-group of 1024 threads, in segments of LSEG
+// counts staged in LDS (coalesced loads and stores): thread t scans its run of LSEG/1024
+// consecutive counts, the run sums are scanned across the work-group, a running carry joins the
+// segments; cnt becomes the scatter cursor and off[ntiles] the total. Count i of a segment sits at
+// LDS word i + i / LRUN (a pad word after each run keeps the runs' reads on distinct banks).
+constexpr int LSEG = 32768, LRUN = LSEG / 1024;
 __global__ __launch_bounds__(1024) void k_label_scan(uint32_t* __restrict__ cnt, uint32_t* __restrict__ off,
                                                      int64_t ntiles) {
+  __shared__ uint32_t seg[LSEG + LSEG / LRUN];
   __shared__ uint32_t wsum[16];
-  __shared__ uint32_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t carry = 0;
-  for (int64_t base = 0; base < ntiles; base += 4096) {
-    const int64_t i0 = base + 4 * (int64_t)tid;
-    uint32_t v[4];
+  for (int64_t base = 0; base < ntiles; base += LSEG) {
+    const int64_t n = ntiles - base < LSEG ? ntiles - base : LSEG;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = i0 + k < ntiles ? cnt[i0 + k] : 0u;
-    const uint32_t tsum = v[0] + v[1] + v[2] + v[3];
-    // inclusive scan of the thread sums within the wave, then across the 16 waves
+    for (int k = 0; k < LRUN; ++k) {
+      const int i = tid + 1024 * k;
+      seg[i + i / LRUN] = i < n ? cnt[base + i] : 0u;
+    }
+    __syncthreads();
+    uint32_t tsum = 0;
+#pragma unroll 8
+    for (int k = 0; k < LRUN; ++k) tsum += seg[tid * (LRUN + 1) + k];
+    // inclusive scan of the run sums within the wave, then across the 16 waves
     uint32_t x = tsum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -100,21 +109,27 @@ __global__ __launch_bounds__(1024) void k_label_scan(uint32_t* __restrict__ cnt,
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    if (tid == 0) {
-      uint32_t run = carry;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) { const uint32_t t = wsum[w]; wsum[w] = run; run += t; }
-      carry_s = run;
+    uint32_t wpre = carry, total = carry;
+    for (int w = 0; w < 16; ++w) {
+      const uint32_t t = wsum[w];
+      if (w < wave) wpre += t;
+      total += t;
+    }
+    uint32_t run = wpre + x - tsum;             // exclusive prefix of this thread's run
+#pragma unroll 8
+    for (int k = 0; k < LRUN; ++k) {
+      const uint32_t v = seg[tid * (LRUN + 1) + k];
+      seg[tid * (LRUN + 1) + k] = run;
+      run += v;
     }
     __syncthreads();
-    uint32_t run = wsum[wave] + x - tsum;         // exclusive prefix of this thread's first entry
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (i0 + k < ntiles) { off[i0 + k] = run; cnt[i0 + k] = run; }
-      run += v[k];
+    for (int k = 0; k < LRUN; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < n) { off[base + i] = seg[i + i / LRUN]; cnt[base + i] = seg[i + i / LRUN]; }
     }
-    carry = carry_s;
-    __syncthreads();
+    carry = total;
+    __syncthreads();                            // seg and wsum free for the next segment
   }
   if (tid == 0) off[ntiles] = carry;
 }
@@ -182,6 +197,7 @@ __global__ void k_dx_reduce(const float* __restrict__ part, int NR, int MB, int 
     if (b >= B) continue;
     const int d = 32 * fb + 8 * ig + 4 * (lane >> 5) + e;
     float s = 0.0f;
+#pragma unroll 8
     for (int r = 0; r < NR; ++r) s += part[(int64_t)r * n + p];
     dX[(int64_t)b * D + d] = s;
   }
