@@ -74,6 +74,7 @@ def lib():
         L.orc_dx_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P, P,
                                   ctypes.c_int, P, ctypes.c_int]
         L.orc_grad_exact.argtypes = [i64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P]
+        L.orc_kahan_update.argtypes = [i64, P, P, P, ctypes.c_float]; L.orc_kahan_update.restype = None
         L.orc_topk.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                P, P, ctypes.c_int]
         for name in ("orc_step", "orc_update_from_g", "orc_logits", "orc_update_rows", "orc_update_rows_from_g",
@@ -231,3 +232,13 @@ def topk(wfmt, W, X, k, nthreads=0):
     idx = np.empty((N, k), np.int32); score = np.empty((N, k), np.float32)
     _chk(lib().orc_topk(wfmt, _p(W), L, D, _p(X), N, k, _p(idx), _p(score), nthreads), "topk")
     return idx, score
+
+
+def kahan_update(w, c, g, lr):
+    """One Kahan-compensated BF16 update of parameters w with compensation c (uint16 BF16 codes)
+    by gradient g (float32); returns the new (w, c)."""
+    w = np.array(w, np.uint16, copy=True).ravel(); c = np.array(c, np.uint16, copy=True).ravel()
+    g = _c(np.asarray(g, np.float32).ravel(), np.float32)
+    assert w.size == c.size == g.size
+    lib().orc_kahan_update(w.size, _p(w), _p(c), _p(g), float(lr))
+    return w, c

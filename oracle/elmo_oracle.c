@@ -574,3 +574,25 @@ int orc_topk(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int N
   free(xt);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Kahan-compensated BF16 update (encoder parameters). The pages train the encoder with Kahan
+ * summation and no FP32 master weights (ELMO summary, Approach); they fix neither the precision
+ * of the compensation nor the order of operations. Reading: the compensation is a BF16 buffer
+ * beside the BF16 parameters, and each step is one step of Kahan's compensated summation of the
+ * increments d = -lr g, with w the running sum and c the negated low part it lost:
+ *   y = d - c,  t = w + y (stored as BF16),  c = (t - w) - y (stored as BF16),  w = t,
+ * evaluated in binary32 (t - w of two BF16 values is exact there).
+ * ---------------------------------------------------------------------------------------------- */
+void orc_kahan_update(int64_t n, uint16_t* w, uint16_t* c, const float* g, float lr) {
+  for (int64_t i = 0; i < n; ++i) {
+    const float wv = f32_from_bits((uint32_t)w[i] << 16);
+    const float cv = f32_from_bits((uint32_t)c[i] << 16);
+    const float d = -lr * g[i];
+    const float y = d - cv;
+    const uint16_t t = orc_bf16_rne(wv + y);
+    const float tv = f32_from_bits((uint32_t)t << 16);
+    c[i] = orc_bf16_rne((tv - wv) - y);
+    w[i] = t;
+  }
+}

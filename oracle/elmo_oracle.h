@@ -95,6 +95,12 @@ int orc_grad_exact(int64_t L, int D, int B, const double* W, const double* X, co
 int orc_topk(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int N, int k,
              int32_t* idx, float* score, int nthreads);
 
+/* Kahan-compensated BF16 update of n encoder parameters, in place: parameter w[i] and its
+ * compensation c[i] BF16, gradient g[i] and lr binary32 (reading of "Kahan summation (encoder)",
+ * ELMO summary, Approach). Per element, in binary32, both stores rounded to BF16 by RNE:
+ *   d = -lr g;  y = d - c;  t = bf16(w + y);  c' = bf16((t - w) - y);  w' = t.  */
+void orc_kahan_update(int64_t n, uint16_t* w, uint16_t* c, const float* g, float lr);
+
 #ifdef __cplusplus
 }
 #endif
