@@ -41,10 +41,43 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--topk-n", type=int, default=4096)
+    ap.add_argument("--no-kahan", action="store_true")
+    ap.add_argument("--kahan-params", type=int, default=110_000_000,
+                    help="encoder parameters of the Kahan-compensated BF16 update pass (768-wide, 12 layers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times) and exit: the "
                          "known-size reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def kahan_bench(n, stream):
+    """Kahan-compensated BF16 update of n encoder parameters (BF16 w and c, FP32 g), a separate
+    elementwise pass bound by HBM: 12 algorithmic bytes per parameter (w, c, g read; w, c written),
+    timed over 10 updates with events on the launch stream."""
+    import torch
+
+    import precision_label_chunk_amd as elmo
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    w = (torch.randn(n, device=dev, generator=gen) * 0.02).to(torch.bfloat16).view(torch.int16)
+    c = torch.zeros(n, dtype=torch.int16, device=dev)
+    g = torch.randn(n, device=dev, generator=gen)
+    for _ in range(2):
+        elmo.kahan_update(w, c, g, 1e-3)
+    torch.cuda.synchronize()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        elmo.kahan_update(w, c, g, 1e-3)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 12.0 * n / (ms / 1e3) / 1e9
+    del w, c, g
+    return {"params": n, "ms": round(ms, 4), "alg_gbs": round(gbs, 1), "peak_gbs": PEAK["hbm"] / 1e9,
+            "frac": round(gbs * 1e9 / PEAK["hbm"], 4)}
 
 
 def kernel_source_hash():
@@ -264,6 +297,9 @@ def main():
         out["topk"] = {"N": N, "k": k, "ms": round(tk, 3), "samples_s": round(N / (tk / 1e3), 1),
                        "tflops": round(tf / (tk / 1e3) / 1e12, 2),
                        "frac": round(tf / (tk / 1e3) / fwd_peak, 4)}
+
+    if not args.no_kahan:
+        out["kahan_update"] = kahan_bench(args.kahan_params, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, W, host_batches[0], args.cpu_seconds)

@@ -133,6 +133,18 @@ int elmo_xmc_forward(const void* W, int wdtype, int64_t L, int D, const void* X,
 int elmo_xmc_kernel_timing(int enable);
 int elmo_xmc_kernel_timing_read(double* ms, int64_t* launches, double* labels);
 
+/* Kahan-compensated BF16 update of n encoder parameters, in place (ELMO summary, Approach: the
+ * encoder is trained with Kahan summation and no FP32 master weights; the pages fix neither the
+ * compensation's precision nor the order of operations, this is one step of Kahan's compensated
+ * summation of the increments). w[i]: the parameter, c[i]: its compensation, both BF16 codes;
+ * g[i]: the binary32 gradient. Per element, in binary32 with both stores rounded to nearest-even:
+ *   d = -lr g;  y = d - c;  t = bf16(w + y);  c = bf16((t - w) - y);  w = t.
+ * w, c, g: DEVICE pointers to n elements each, naturally aligned (2, 2, 4 bytes; 16-byte alignment
+ * of all three takes the vector path), owned by the caller; w and c must not overlap each other or
+ * g. n = 0 is a no-op. Returns ELMO_ESHAPE for n < 0, ELMO_EINVAL for a null or misaligned
+ * pointer, ELMO_EHIP on a launch failure; asynchronous on `stream`. */
+int elmo_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float lr, void* stream);
+
 /*
  * Test hook: the device codec, stochastic rounding and RNG applied elementwise to n elements.
  *   op 0  BF16 RNE encode:      in0 float[n]            -> out uint16[n]

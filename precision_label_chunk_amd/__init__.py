@@ -69,6 +69,7 @@ def lib():
         L.elmo_xmc_kernel_timing_read.argtypes = [P, P, P]; L.elmo_xmc_kernel_timing_read.restype = i32
         L.elmo_numerics_probe.argtypes = [i32, P, P, P, i64, u64, u64, P]
         L.elmo_numerics_probe.restype = i32
+        L.elmo_kahan_update.argtypes = [P, P, P, i64, f32, P]; L.elmo_kahan_update.restype = i32
         _lib = L
     return _lib
 
@@ -198,6 +199,18 @@ def kernel_timing_read():
     ms = (ctypes.c_double * 2)(); n = (ctypes.c_int64 * 2)(); lab = (ctypes.c_double * 2)()
     _chk("elmo_xmc_kernel_timing_read", lib().elmo_xmc_kernel_timing_read(ms, n, lab))
     return {"fwd": (ms[0], n[0], lab[0]), "bwd": (ms[1], n[1], lab[1])}
+
+
+def kahan_update(w, c, g, lr):
+    """Kahan-compensated BF16 update of encoder parameters in place: w, c (int16 tensors of BF16
+    codes) and g (float32), same number of elements, on the GPU (see elmo_xmc.h)."""
+    _check_dev(w, c, g)
+    assert w.dtype == torch.int16 and c.dtype == torch.int16 and g.dtype == torch.float32
+    assert w.is_contiguous() and c.is_contiguous() and g.is_contiguous()
+    n = w.numel()
+    assert c.numel() == n and g.numel() == n
+    _chk("elmo_kahan_update", lib().elmo_kahan_update(_ptr(w), _ptr(c), _ptr(g), n, float(lr), _stream()))
+    return w, c
 
 
 def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):

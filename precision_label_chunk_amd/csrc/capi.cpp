@@ -128,6 +128,13 @@ int elmo_xmc_kernel_timing_read(double* ms, int64_t* launches, double* labels) {
   return elmo::kernel_timing_read(ms, launches, labels);
 }
 
+int elmo_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float lr, void* stream) {
+  if (n < 0) return ELMO_ESHAPE;
+  if (n == 0) return ELMO_OK;
+  if (!w || !c || !g || (uintptr_t)w % 2 || (uintptr_t)c % 2 || (uintptr_t)g % 4) return ELMO_EINVAL;
+  return elmo::run_kahan_update(w, c, g, n, lr, (hipStream_t)stream);
+}
+
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                         uint64_t step, void* stream) {
   return elmo::run_numerics_probe(op, in0, in1, out, n, seed, step, (hipStream_t)stream);

@@ -53,6 +53,9 @@ TopkLayout topk_layout(int N, int D, int64_t L, int k, int wdtype);
 int run_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, int k, int32_t* idx,
              float* score, const TopkLayout& s, void* workspace, hipStream_t st);
 
+// Kahan-compensated BF16 update of encoder parameters (elementwise)
+int run_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float lr, hipStream_t st);
+
 // elementwise numerics hook
 int run_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                        uint64_t step, hipStream_t st);

@@ -28,7 +28,8 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["elmo_xmc_step", "elmo_xmc_topk", "elmo_xmc_step_workspace_bytes", "elmo_xmc_topk_workspace_bytes",
-              "elmo_xmc_logits", "elmo_numerics_probe", "elmo_status_str", "elmo_abi_version", "elmo_xmc_step_flags"]:
+              "elmo_xmc_logits", "elmo_numerics_probe", "elmo_status_str", "elmo_abi_version", "elmo_xmc_step_flags",
+              "elmo_kahan_update"]:
         assert n in names
 
 
@@ -80,3 +81,14 @@ def test_topk_rejects_invalid_arguments(L):
 def test_numerics_probe_rejects_bad_op(L):
     assert L.elmo_numerics_probe(9, None, None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
     assert L.elmo_numerics_probe(3, ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
+
+
+def test_kahan_update_rejects_invalid_arguments(L):
+    L.elmo_kahan_update.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_float, ctypes.c_void_p]
+    p = ctypes.c_void_p(4096)
+    assert L.elmo_kahan_update(p, p, p, -1, 0.1, None) == -2
+    assert L.elmo_kahan_update(None, None, None, 0, 0.1, None) == 0          # empty: nothing to do
+    assert L.elmo_kahan_update(None, p, p, 8, 0.1, None) == -1
+    assert L.elmo_kahan_update(p, p, ctypes.c_void_p(4098), 8, 0.1, None) == -1   # misaligned g
+    assert L.elmo_kahan_update(ctypes.c_void_p(4097), p, p, 8, 0.1, None) == -1   # misaligned w
