@@ -4,8 +4,8 @@
 // increments d = -lr g, evaluated in binary32 with the two stores rounded to nearest-even:
 //   y = d - c,  t = bf16(w + y),  c = bf16((t - w) - y),  w = t.
 // The work is elementwise and bound by HBM (12 bytes per parameter: w, c and g read, w and c
-// written): 8 parameters per thread and iteration with 16-byte accesses when the three arrays
-// allow it, a grid-stride loop of a few work-groups per CU.
+// written): 8 parameters per thread with 16-byte non-temporal accesses when the three arrays allow
+// it, up to 256 work-groups per CU (one pass for an encoder-sized array), a scalar tail.
 #include "mfma.hpp"
 #include "numerics.hpp"
 #include "step_kernels.hpp"
@@ -25,8 +25,11 @@ __device__ __forceinline__ void kahan1(uint32_t wb, uint32_t cb, float g, float 
 __global__ __launch_bounds__(256) void k_kahan8(uint16_t* __restrict__ w, uint16_t* __restrict__ c,
                                                 const float* __restrict__ g, int64_t n8, float lr) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    const i32x4_t wv = ((const i32x4_t*)w)[i], cv = ((const i32x4_t*)c)[i];
-    const f32x4_t g0 = ((const f32x4_t*)g)[2 * i], g1 = ((const f32x4_t*)g)[2 * i + 1];
+    // (every byte is touched once: non-temporal accesses keep the stream from displacing the caches)
+    const i32x4_t wv = __builtin_nontemporal_load((const i32x4_t*)w + i);
+    const i32x4_t cv = __builtin_nontemporal_load((const i32x4_t*)c + i);
+    const f32x4_t g0 = __builtin_nontemporal_load((const f32x4_t*)g + 2 * i);
+    const f32x4_t g1 = __builtin_nontemporal_load((const f32x4_t*)g + 2 * i + 1);
     const uint32_t wa[4] = {(uint32_t)wv[0], (uint32_t)wv[1], (uint32_t)wv[2], (uint32_t)wv[3]};
     const uint32_t ca[4] = {(uint32_t)cv[0], (uint32_t)cv[1], (uint32_t)cv[2], (uint32_t)cv[3]};
     const float ga[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
@@ -39,8 +42,8 @@ __global__ __launch_bounds__(256) void k_kahan8(uint16_t* __restrict__ w, uint16
       wo[k] = w0 | (w1 << 16);
       co[k] = c0 | (c1 << 16);
     }
-    ((i32x4_t*)w)[i] = i32x4_t{(int)wo[0], (int)wo[1], (int)wo[2], (int)wo[3]};
-    ((i32x4_t*)c)[i] = i32x4_t{(int)co[0], (int)co[1], (int)co[2], (int)co[3]};
+    __builtin_nontemporal_store(i32x4_t{(int)wo[0], (int)wo[1], (int)wo[2], (int)wo[3]}, (i32x4_t*)w + i);
+    __builtin_nontemporal_store(i32x4_t{(int)co[0], (int)co[1], (int)co[2], (int)co[3]}, (i32x4_t*)c + i);
   }
 }
 
@@ -58,7 +61,7 @@ int run_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float 
   if (n == 0) return ELMO_OK_;
   const bool vec = ((uintptr_t)w % 16 == 0) && ((uintptr_t)c % 16 == 0) && ((uintptr_t)g % 16 == 0);
   const int64_t n8 = vec ? n / 8 : 0;
-  const int cap = 16 * device_cus();
+  const int cap = 256 * device_cus();          // (many short-lived work-groups stream best)
   if (n8 > 0) {
     const int64_t want = (n8 + 255) / 256;
     hipLaunchKernelGGL(k_kahan8, dim3((unsigned)(want < cap ? want : cap)), dim3(256), 0, st, w, c, g, n8, lr);
