@@ -197,6 +197,12 @@ def main():
                      device=dev)
     dX = torch.empty((wl.B, wl.D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    # the step's peak HBM counts what is resident while it runs (the library allocates nothing),
+    # not the transients of generating the weights
+    torch.cuda.reset_peak_memory_stats(dev)
+    hbm_parts = {"weights": W.numel() * W.element_size(), "workspace": ws.numel(),
+                 "batches": sum(t.numel() * t.element_size() for b in batches for t in b),
+                 "dX": dX.numel() * 4}
 
     for s in range(args.warmup):
         X, rp, ids = batches[s]
@@ -278,6 +284,7 @@ def main():
            "alg_hbm_gbs": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
            "hbm_frac": round(alg_bytes / (ms_step / 1e3) / PEAK["hbm"], 4),
            "peak_hbm_bytes": int(peak_hbm),
+           "peak_hbm_breakdown": {k: int(v) for k, v in hbm_parts.items()},
            "weights_bytes": int(L * D * wl.wbytes),
            "roofline": roofline}
 
