@@ -261,6 +261,21 @@ __device__ __forceinline__ void fwd_store_block(const float (&gv)[16], uint16_t*
   }
 }
 
+// The same 16-byte pieces into a wave's LDS staging rows instead (row `lrow`, byte column c0b of
+// the block's first sample): the rows then go out as whole 128-byte segments.
+__device__ __forceinline__ void fwd_stage_block(const float (&gv)[16], uint8_t* lrow, int c0b, int hi) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
+    const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+    *(i32x4_t*)(lrow + c0b + 32 * u + 16 * hi) = out;
+  }
+}
+
 template <int MB, int WF, bool LOSS, bool ZOUT>
 __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
                                                int D, int64_t c0, int clen,
@@ -302,10 +317,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
   };
   fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj, scan);
 
-  // epilogue: gradient straight from the accumulators, block by block
+  // epilogue: gradient straight from the accumulators, block by block. With 128 or 256 samples
+  // each wave's rows of G (CW = 64 labels) are staged in LDS (free after the K loop) 64 samples at
+  // a time, so that every row leaves as one whole 128-byte segment instead of 16-byte pieces of
+  // 32 rows.
+  constexpr bool GST = MB >= 128 && !ZOUT;
+  constexpr int GSP = 144;                     // staging row pitch (bytes): 16 rows per bank cycle
+  uint8_t* gst = smem + wave * (CW * GSP);
   float lsum = 0.0f;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int jl = wj * CW + ni * 32 + l32;
@@ -330,8 +351,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
           }
         }
       }
-      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)(jbase + jl) * gpitch, bb, hi);
+      if constexpr (GST) fwd_stage_block(gv, gst + (ni * 32 + l32) * GSP, (mi & 1) * 64, hi);
+      else if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)(jbase + jl) * gpitch, bb, hi);
     }
+    if constexpr (GST) {
+      if (mi & 1) {                            // 64 samples of the wave's CW rows staged
+        const int sb0 = wb * RW + (mi - 1) * 32;
+#pragma unroll
+        for (int k = 0; k < CW / 8; ++k) {
+          const int row = k * 8 + (lane >> 3);
+          const i32x4_t v = *(const i32x4_t*)(gst + row * GSP + (lane & 7) * 16);
+          *(i32x4_t*)(G + (int64_t)(jbase + wj * CW + row) * gpitch + sb0 + (lane & 7) * 8) = v;
+        }
+      }
+    }
+  }
   if constexpr (LOSS) {
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     if (lane == 0) lred[wave] = lsum;
