@@ -46,6 +46,14 @@ __device__ __forceinline__ void list_init(float (&ls)[KK], int (&lj)[KK]) {
   for (int i = 0; i < KK; ++i) { ls[i] = __builtin_nanf(""); lj[i] = INT32_MAX; }
 }
 
+// register i (dynamic) of a 16-register accumulator block, by a select chain
+__device__ __forceinline__ float reg_pick16(const f32x16_t& a, int i) {
+  float v = a[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) v = i == k ? a[k] : v;
+  return v;
+}
+
 template <int WF, int KK>
 __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
                                                    const uint8_t* __restrict__ Xf, int nbn, int NRg,
@@ -88,8 +96,9 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
 
     if constexpr (KK <= 8) {
       // candidates: a score may enter its list only if the list's bound is NaN or not above it
-      // (a bound from an earlier tile is a lower one, so it never drops a candidate). Wave (wb, wj)
-      // holds samples wb * RW .. + RW - 1 and label half wj (CW = 64) of the tile.
+      // (a bound from an earlier tile is a lower one, so it never drops a candidate); NaN scores
+      // pass the test too and are sorted out by the list. Wave (wb, wj) holds samples
+      // wb * RW .. + RW - 1 and label half wj (CW = 64) of the tile.
       uint32_t cm[MI * NI];               // candidate bits, register i of block (mi, ni)
       int cnt = 0;
 #pragma unroll
@@ -105,47 +114,56 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float b = bq[i >> 2][i & 3], z = acc[mi][ni][i];
-            m |= (uint32_t)(jin && (b != b || z >= b)) << i;
+            m |= (uint32_t)(jin && !(z < b)) << i;     // (also true when b or z is NaN)
           }
           cm[mi * NI + ni] = m;
           cnt += __builtin_popcount(m);
         }
       }
-      // a wave with candidates queues them (as far as the queue goes) and writes its scores to
-      // the score tile, for the full path
+      // a wave with candidates queues them; only when the queue overflows do such waves write
+      // their scores to the score tile, for the full path
       const bool wany = __builtin_amdgcn_ballot_w64(cnt > 0) != 0;
       if (wany) {
+        // the lane's candidates into the queue (as far as it goes), each score taken from the
+        // accumulators by a select over the block's 16 registers
+        uint32_t k = cnt > 0 ? atomicAdd(&qcount, (uint32_t)cnt) : 0u;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              sc[(wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3)) * SP + wj * CW + ni * 32 + l32] = acc[mi][ni][i];
-        // the lane's candidates, read back from its own score tile entries
-        uint32_t k = cnt > 0 ? atomicAdd(&qcount, (uint32_t)cnt) : 0u;
-#pragma unroll
-        for (int b = 0; b < MI * NI; ++b) {
-          uint32_t m = cm[b];
-          while (m != 0u) {
-            const int i = __builtin_ctz(m);
-            m &= m - 1u;
-            const int n = wb * RW + (b / NI) * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const int jl = wj * CW + (b % NI) * 32 + l32;
-            if (k < (uint32_t)QCAP) {
-              qkey[k] = (uint32_t)n | ((uint32_t)wj << 7) | ((uint32_t)jl << 8);
-              qscore[k] = sc[n * SP + jl];
+          for (int ni = 0; ni < NI; ++ni) {
+            uint32_t m = cm[mi * NI + ni];
+            while (m != 0u) {
+              const int i = __builtin_ctz(m);
+              m &= m - 1u;
+              if (k < (uint32_t)QCAP) {
+                const int n = wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+                qkey[k] = (uint32_t)n | ((uint32_t)wj << 7) | ((uint32_t)(wj * CW + ni * 32 + l32) << 8);
+                qscore[k] = reg_pick16(acc[mi][ni], i);
+              }
+              ++k;
             }
-            ++k;
           }
-        }
       }
       if (lane == 0) wcand[wave] = wany ? 1u : 0u;
       __syncthreads();
       const uint32_t nq = qcount;
+      if (nq > (uint32_t)QCAP) {
+        // too many for the queue: the waves with candidates write their scores to the tile
+        if (wany) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                sc[(wb * RW + mi * 32 + 8 * (i >> 2) + 4 * hi + (i & 3)) * SP + wj * CW + ni * 32 + l32] = acc[mi][ni][i];
+        }
+        __syncthreads();
+      }
       if (nq <= (uint32_t)QCAP) {
         // few candidates: each list's thread takes its own from the queue
         const uint32_t key = (uint32_t)srow | ((uint32_t)half << 7);
+#pragma unroll 4
         for (uint32_t e = 0; e < nq; ++e) {
           const uint32_t v = qkey[e];
           if ((v & 0xffu) == key) {
