@@ -289,7 +289,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
   constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
   constexpr int MI = RW / 32, NI = CW / 32;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  constexpr int KS = 64;                       // K slice: small enough for two work-groups per CU
+  // K slice: small enough for two work-groups per CU; 128 bytes (64 BF16 elements, half the
+  // barriers) where the LDS stages of 256 rows still leave room for the second work-group
+  constexpr int KS = (MB <= 128 && WF == W_BF16_) ? 128 : 64;
   __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
   __shared__ uint32_t ybits[TJ1 * (MB / 32)];    // positives, label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[4];
