@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
   constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int SP = TJ1 + 4;           // score tile pitch (floats)
-  constexpr int KS = WF == W_BF16_ ? 128 : 64;   // K slice bytes (two work-groups per CU either way)
+  // K slice bytes (two work-groups per CU either way; 64 for E4M3 lists of 32, whose registers are
+  // short for the larger staging)
+  constexpr int KS = (WF == W_BF16_ || KK <= 8) ? 128 : 64;
   constexpr int SMEM = MB * SP * 4 > fwd_smem_bytes(MB, KS) ? MB * SP * 4 : fwd_smem_bytes(MB, KS);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];   // operand stages, then the score tile
   // bound[h][n]: score of the last entry of sample n's list for label half h (NaN while not full)
