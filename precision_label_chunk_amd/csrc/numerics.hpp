@@ -187,6 +187,16 @@ __device__ __forceinline__ float bce_grad_fast_m(float z, uint32_t ys) {
   return u2f(__builtin_amdgcn_bitop3_b32(f2u(r), ys, 0x80000000u, 0x78));          // r (y = 0), -r (y = 1)
 }
 
+// the small-argument form, for |z| <= 2: 2^(a log2 e) straight from the FP32 product. Its rounding
+// (at most 2^-23 in the exponent argument) and that of log2 e add under 1.5 FP32 ulp, so this form
+// stays within about 4 ulp of sigmoid, with two operations per element fewer than the split form.
+__device__ __forceinline__ float bce_grad_small_m(float z, uint32_t ys) {
+  constexpr float L2E_HI = 1.44269502162933349609375f;         // FP32(log2 e)
+  const float a = u2f(__builtin_amdgcn_bitop3_b32(f2u(z), ys, 0x80000000u, 0xD2));
+  const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * L2E_HI));
+  return u2f(__builtin_amdgcn_bitop3_b32(f2u(r), ys, 0x80000000u, 0x78));
+}
+
 __device__ __forceinline__ float bce_grad_fast(float z, bool y) { return bce_grad_fast_m(z, y ? 0x80000000u : 0u); }
 
 // the exact-division form, for |z| > 80
@@ -197,6 +207,7 @@ __device__ __forceinline__ float bce_grad_slow(float z, bool y) {
 
 __device__ __forceinline__ float bce_grad(float z, bool y) {
   if (__builtin_expect(__builtin_fabsf(z) > 80.0f, 0)) return bce_grad_slow(z, y);
+  if (__builtin_fabsf(z) <= 2.0f) return bce_grad_small_m(z, y ? 0x80000000u : 0u);
   return bce_grad_fast(z, y);
 }
 

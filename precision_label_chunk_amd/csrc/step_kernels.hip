@@ -224,7 +224,8 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* __restrict__ l
 // samples bb + 8 (i/4) + 4 hi + i%4 in register i; yw holds the positives of samples bb .. bb+31 of
 // that label. Padding (samples >= B, labels past the chunk) gets 0. The exact form is needed only
 // for |z| > 80: one wave-uniform test per block (every |z| <= 80, every sample and label valid)
-// keeps the common case free of branches and selects.
+// keeps the common case free of branches and selects, and a second one takes the shorter
+// small-argument form when every |z| of the block is at most 2.
 __device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, bool jvalid, int bb, int B, int hi,
                                                float (&gv)[16]) {
   float m = 0.0f;
@@ -234,8 +235,13 @@ __device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, b
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(!common) == 0, 1)) {
     // every element in range and valid: no select; label bit bl of yw moved to bit 31
     const uint32_t yh = yw >> (4 * hi);
+    if (__builtin_amdgcn_ballot_w64(m > 2.0f) == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) gv[i] = bce_grad_fast_m(a[i], yh << (31 - (8 * (i >> 2) + (i & 3))));
+      for (int i = 0; i < 16; ++i) gv[i] = bce_grad_small_m(a[i], yh << (31 - (8 * (i >> 2) + (i & 3))));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gv[i] = bce_grad_fast_m(a[i], yh << (31 - (8 * (i >> 2) + (i & 3))));
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
