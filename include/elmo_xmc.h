@@ -156,6 +156,10 @@ int elmo_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float
  *   op 6  gradient code:        in0 float z[n], in1 uint32 y[n] -> out uint16[n] (BF16(sigmoid(z) - y))
  *   op 7  E4M3 -> BF16, 4 codes per word as the backward kernel decodes its weight tiles:
  *                               in0 uint32[n] -> out uint32[2n] (BF16 pairs of bytes 0,1 and 2,3)
+ *   op 8  gradient, the forward's small-argument form (meant for |z| <= 2), binary32 before rounding:
+ *                               in0 float z[n], in1 uint32 y[n] -> out float[n]
+ *   op 9  gradient, the forward's split-exponent form (meant for |z| <= 80), binary32 before rounding:
+ *                               in0 float z[n], in1 uint32 y[n] -> out float[n]
  */
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n,
                         uint64_t seed, uint64_t step, void* stream);

@@ -216,7 +216,7 @@ def kahan_update(w, c, g, lr):
 def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):
     """Device codec / SR / RNG / gradient applied elementwise (test hook; see elmo_xmc.h)."""
     out_dtype = {0: torch.int16, 1: torch.uint8, 2: torch.float32, 3: torch.int16, 4: torch.uint8,
-                 5: torch.int32, 6: torch.int16, 7: torch.int32}[op]
+                 5: torch.int32, 6: torch.int16, 7: torch.int32, 8: torch.float32, 9: torch.float32}[op]
     if n is None:
         n = in0.numel()
     dev = in0.device if in0 is not None else torch.device("cuda")

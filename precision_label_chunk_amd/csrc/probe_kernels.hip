@@ -32,6 +32,13 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
         ((uint32_t*)out)[2 * i + 1] = hi;
         break;
       }
+      case 8:
+      case 9: {
+        const float z = ((const float*)in0)[i];
+        const uint32_t ys = ((const uint32_t*)in1)[i] != 0 ? 0x80000000u : 0u;
+        ((float*)out)[i] = op == 8 ? bce_grad_small_m(z, ys) : bce_grad_fast_m(z, ys);
+        break;
+      }
       default: break;
     }
   }
@@ -39,9 +46,9 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
 
 int run_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                        uint64_t step, hipStream_t st) {
-  if (op < 0 || op > 7 || n < 0 || !out) return ELMO_EINVAL_;
+  if (op < 0 || op > 9 || n < 0 || !out) return ELMO_EINVAL_;
   if (op != 5 && !in0) return ELMO_EINVAL_;
-  if ((op == 3 || op == 4 || op == 6) && !in1) return ELMO_EINVAL_;
+  if ((op == 3 || op == 4 || op == 6 || op == 8 || op == 9) && !in1) return ELMO_EINVAL_;
   if (n == 0) return ELMO_OK_;
   uint64_t idx0 = 0;
   if (op == 5) idx0 = in0 ? *(const uint64_t*)in0 : 0;

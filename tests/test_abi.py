@@ -79,7 +79,8 @@ def test_topk_rejects_invalid_arguments(L):
 
 
 def test_numerics_probe_rejects_bad_op(L):
-    assert L.elmo_numerics_probe(9, None, None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
+    assert L.elmo_numerics_probe(10, None, None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
+    assert L.elmo_numerics_probe(8, ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
     assert L.elmo_numerics_probe(3, ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1, 0, 0, None) == -1
 
 

@@ -113,3 +113,22 @@ def test_gradient_code_within_fp32_sigmoid_error(elmo, orc):
     d = np.abs(sg - sr)
     assert d.max() <= 1
     assert (d != 0).mean() <= 1e-3
+
+
+@pytest.mark.parametrize("op,zmax,bound", [(8, 2.0, 4.0), (9, 80.0, 3.0)])
+def test_gradient_forms_within_stated_ulps(elmo, op, zmax, bound):
+    """The forward's two fast gradient forms in binary32 against sigmoid(z) - y in binary64
+    (the cancellation-free -sigmoid(-z) for y = 1), in units of the binary32 spacing at the exact
+    value: the small-argument form over |z| <= 2, the split-exponent form over |z| <= 80."""
+    from scipy.special import expit
+    g = np.random.default_rng(9)
+    z = np.concatenate([g.uniform(-zmax, zmax, 200000), g.standard_normal(50000) * min(zmax, 2.0) / 2,
+                        [0.0, zmax, -zmax, 1e-30, -1e-30]]).astype(np.float32)
+    z = np.clip(z, -zmax, zmax)
+    y = (g.random(z.size) < 0.5).astype(np.uint32)
+    got = elmo.numerics_probe(op, _dev(z), _dev(y)).cpu().numpy().astype(np.float64)
+    zd = z.astype(np.float64)
+    ref = np.where(y == 1, -expit(-zd), expit(zd))
+    ulps = np.abs(got - ref) / np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    print(f"op {op}: max {ulps.max():.3f} ulp, mean {ulps.mean():.3f}")
+    assert np.all(np.isfinite(got)) and ulps.max() <= bound
