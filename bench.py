@@ -165,7 +165,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU (--gpus 1); multi-GPU runs are not part of it",
+        print("bench.py: runs on exactly one GPU (--gpus 1); multi-GPU runs are not implemented",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_bytes:

@@ -37,7 +37,7 @@ typedef enum {
   ELMO_EDTYPE = -3,        /* unknown weight format                                      */
   ELMO_EWORKSPACE = -4,    /* workspace missing or smaller than the *_workspace_bytes   */
   ELMO_EHIP = -5,          /* a HIP runtime call or kernel launch failed                 */
-  ELMO_EUNSUPPORTED = -6   /* valid request that this build does not implement           */
+  ELMO_EUNSUPPORTED = -6   /* valid request that this library does not implement         */
 } elmo_status;
 
 /* Weight storage formats. BF16: uint16 codes. E4M3: OCP FP8 E4M3FN codes (uint8; max 448, no

@@ -34,7 +34,7 @@ const char* elmo_status_str(int status) {
     case ELMO_EDTYPE: return "unknown weight format";
     case ELMO_EWORKSPACE: return "workspace missing or too small";
     case ELMO_EHIP: return "HIP runtime error";
-    case ELMO_EUNSUPPORTED: return "not supported by this build";
+    case ELMO_EUNSUPPORTED: return "not supported by this library";
     default: return "unknown status";
   }
 }
