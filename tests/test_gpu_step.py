@@ -6,7 +6,7 @@ import torch
 
 import workloads as wk
 from tests._helpers import (RTOL, assert_close, assert_grad_codes_match, assert_weights_match, batch_to_dev,
-                            from_dev_codes, to_dev_codes, update_error_bound, weight_report)
+                            code_value, from_dev_codes, rel_err, to_dev_codes, update_error_bound, weight_report)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,11 @@ def check_step(elmo, orc, W0, bt, wfmt, lr, seed, step, Wg, dXg, lossg=None):
     if lossg is not None:
         assert abs(lossg - lossr) <= 1e-4 * abs(lossr)
     print(f"  Z rel {ez:.2e}  G flips {flips:.2e}  W equal {eq:.6f} (free {eq_free:.6f})  dX rel {e:.2e}", flush=True)
+    if wfmt == wk.W_E4M3:
+        # context only: the FP8 logits against logits of the unquantised BF16 features (the effect
+        # of casting X to E4M3, which the 6e-2 tolerance leaves room for)
+        Zu = code_value(bt.X, wk.W_BF16) @ code_value(W0, wfmt).T
+        print(f"  FP8 logits vs unquantised-X logits: max rel {rel_err(Zg, Zu).max():.2e}", flush=True)
 
 
 @pytest.mark.parametrize("B,D,L,chunk,wfmt", CASES)
