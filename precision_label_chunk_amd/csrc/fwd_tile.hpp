@@ -19,7 +19,8 @@ constexpr int fwd_pitch(int KS) { return KS + 16; }     // LDS row pitch: confli
 constexpr int fwd_smem_bytes(int MB, int KS) { return 2 * (MB + TJ1) * fwd_pitch(KS); }
 
 // RW x CW is this wave's sub-tile (RW samples, CW labels); the work-group is (MB/RW) x (TJ1/CW) waves
-template <int MB, int WF, int RW, int CW, int KS, typename Mid>
+// SPREAD: the write-group row spreading below (off only where its few extra registers do not fit)
+template <int MB, int WF, int RW, int CW, int KS, bool SPREAD = true, typename Mid>
 __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint8_t* smem,
                                          const uint8_t* __restrict__ Wt, int nvalid,
                                          const uint8_t* __restrict__ Xf, int64_t rowbytes, int tid, int wb,
@@ -37,18 +38,28 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int nks = (int)((rowbytes + KS - 1) / KS);
 
-  // chunk c of this thread: ci = tid + 256 c, row ci / PPR (X rows, then W rows), part ci % PPR.
+  // chunk c of this thread: ci = tid + 256 c, part ci % PPR of a row (X rows, then W rows). The
+  // 16 chunks of a ds_write_b128 lane group take rows PPR apart (4 rows of 64 bytes, or 2 of 128)
+  // rather than consecutive ones: at the 80- or 144-byte pitch those land on disjoint bank windows,
+  // where consecutive rows would overlap. Within each block of 16 rows, group m = (ci / 16) % PPR
+  // holds rows m, m + PPR, ...; a chunk index past the last row maps past it as well.
   // Buffer loads: W rows at or past nvalid fall outside their resource and read as zero, and so
   // does a part past the end of a row (its offset is pushed out of range); whether chunk c is an X
   // or a W chunk is known at compile time when the X chunks fill whole multiples of 256.
   constexpr int NCHX = MB * PPR;                          // X chunks per slice
   constexpr int OOB = 0x7ffffff0;
+  static_assert(MB % 16 == 0 && (PPR == 4 || PPR == 8), "whole 16-row blocks");
+  auto chunk_row = [](int ci) {
+    if constexpr (!SPREAD) return ci / PPR;
+    const int g = ci >> 4;
+    return 16 * (g / PPR) + g % PPR + PPR * ((ci & 15) / PPR);
+  };
   const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xf, (int64_t)MB * rowbytes);
   const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(Wt, (int64_t)(nvalid < TJ1 ? nvalid : TJ1) * rowbytes);
   i32x4_t stg[2][CPT];
   auto gload = [&](auto S, auto K, int ks) {
     constexpr int c = decltype(K)::value;
-    const int ci = tid + 256 * c, row = ci / PPR, part = ci % PPR;
+    const int ci = tid + 256 * c, row = chunk_row(ci), part = ci % PPR;
     const int kb = ks * KS;                               // wave-uniform
     const bool inrow = kb + part * 16 < rowbytes;
     i32x4_t v = {0, 0, 0, 0};
@@ -68,7 +79,7 @@ __device__ __forceinline__ void fwd_tile(f32x16_t (&acc)[RW / 32][CW / 32], uint
     constexpr int c = decltype(K)::value;
     const int ci = tid + 256 * c;
     if (c + 1 < CPT || ci < NCH)
-      *(i32x4_t*)(smem + buf * SLICE + (ci / PPR) * PT + (ci % PPR) * 16) = stg[decltype(S)::value][c];
+      *(i32x4_t*)(smem + buf * SLICE + chunk_row(ci) * PT + (ci % PPR) * 16) = stg[decltype(S)::value][c];
   };
   auto lstore = [&](auto S, int buf) { static_for<0, CPT>([&](auto K) { lstore1(S, K, buf); }); };
 

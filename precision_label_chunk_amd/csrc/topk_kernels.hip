@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
     const int64_t j0 = t * TJ1;
     const int nvalid = (int)((L - j0) < TJ1 ? (L - j0) : TJ1);
     f32x16_t acc[MI][NI];
-    fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj, [] {});
+    fwd_tile<MB, WF, RW, CW, KS, KK <= 8>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj, [] {});
 
     if constexpr (KK <= 8) {
       // candidates: a score may enter its list only if the list's bound is NaN or not above it
