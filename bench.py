@@ -163,6 +163,32 @@ def cpu_baseline(wl, W_dev, batch, target_s):
             "seconds": round(t, 3), "labels": Ls}
 
 
+def cpu_topk_baseline(wl, W_dev, Xe, k, target_s, nq=256):
+    """The oracle's top-k of nq of the same held-out queries over the first L' labels of the same
+    weights, L' sized for about `target_s` seconds; scaled to queries/s over all L labels."""
+    import numpy as np
+
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    Xs = np.ascontiguousarray(Xe[:nq])
+
+    def run(Ls):
+        W = W_dev[:Ls].cpu().numpy()
+        W = W.view(np.uint16) if W.dtype == np.int16 else W
+        t0 = time.perf_counter()
+        oracle.topk(wl.wfmt, W, Xs, min(k, Ls), nthreads=threads)
+        return time.perf_counter() - t0
+
+    Ls = min(wl.L, 4096)
+    t = run(Ls)
+    Ls2 = int(min(wl.L, max(Ls, Ls * target_s / max(t, 1e-3))))
+    if Ls2 > Ls:
+        Ls, t = Ls2, run(Ls2)
+    return {"value": Xs.shape[0] / (t / Ls * wl.L), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle top-{k} of {Xs.shape[0]} queries over the first {Ls} of {wl.L} labels took "
+                      f"{t:.2f} s; scaled linearly to all labels", "seconds": round(t, 3), "labels": Ls}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -304,7 +330,8 @@ def main():
 
     if not args.no_topk:
         N, k = args.topk_n, (wl.topk or 5)
-        Xe = torch.from_numpy(wk.make_eval_x(wl, N).view(np.int16)).to(dev)
+        Xe_host = wk.make_eval_x(wl, N)
+        Xe = torch.from_numpy(Xe_host.view(np.int16)).to(dev)
         tws = torch.empty((elmo.topk_workspace_bytes(N, D, L, k, wl.wfmt),), dtype=torch.uint8, device=dev)
         elmo.topk(W, Xe, k, workspace=tws)
         torch.cuda.synchronize()
@@ -318,6 +345,8 @@ def main():
         out["topk"] = {"N": N, "k": k, "ms": round(tk, 3), "samples_s": round(N / (tk / 1e3), 1),
                        "tflops": round(tf / (tk / 1e3) / 1e12, 2),
                        "frac": round(tf / (tk / 1e3) / fwd_peak, 4)}
+        if not args.no_cpu_baseline:
+            out["topk"]["cpu_baseline"] = cpu_topk_baseline(wl, W, Xe_host, k, args.cpu_seconds / 3)
 
     if not args.no_kahan:
         out["kahan_update"] = kahan_bench(args.kahan_params, stream)
