@@ -275,6 +275,7 @@ def main():
     h = len(per_step) // 2
     events_median = per_step[h] if len(per_step) % 2 else 0.5 * (per_step[h - 1] + per_step[h])
     peak_hbm = torch.cuda.max_memory_allocated(dev)
+    free_b, total_b = torch.cuda.mem_get_info(dev)   # hipMemGetInfo: the device's own view, for comparison
 
     B, D, L = wl.B, wl.D, wl.L
     flops = 6.0 * B * D * L
@@ -325,6 +326,7 @@ def main():
            "hbm_frac": round(alg_bytes / (ms_step / 1e3) / PEAK["hbm"], 4),
            "peak_hbm_bytes": int(peak_hbm),
            "peak_hbm_breakdown": {k: int(v) for k, v in hbm_parts.items()},
+           "device_used_bytes": int(total_b - free_b),
            "weights_bytes": int(L * D * wl.wbytes),
            "roofline": roofline}
 
