@@ -46,6 +46,17 @@ int padded_batch(int B);
 int device_cus();
 StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64_t max_nnz);
 int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_t st);
+// the per-chunk kernels of a step over labels [a.l0, a.l1) (step_chunks.hip, one object per <MB, WF>)
+template <int MB, int WF>
+int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t st);
+extern template int run_chunks<32, W_BF16_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<64, W_BF16_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<128, W_BF16_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<256, W_BF16_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<32, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<64, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<128, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<256, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 
 // top-k
 struct TopkLayout { int MB, NRg; int64_t ncand; size_t xb, xq, cand_s, cand_i, total; };
