@@ -146,15 +146,13 @@ void orc_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds, ui
 
 /* RNG keying (reading of "counter-based, keyed on seed, step and element index"): key = seed,
  * counter = (g, step) as 64-bit halves, ten rounds; the 128 output bits give 16 bits to each of 8
- * elements. Which 8: within each aligned group of 32 consecutive element indices (rows hold whole
- * groups, D being a multiple of 64), the elements with equal bits 4 and 2 of the index share block
- * g = 4 (idx >> 5) + 2 bit4 + bit2, at position p = 4 bit3 + (idx & 3), which takes 16-bit half
- * (p & 1) of output word p >> 1. (A fixed permutation of the elements within each group: every
- * element still gets its own 16 bits of one block.) */
+ * elements. The 8 consecutive element indices 8g .. 8g + 7 share block g = idx >> 3; the element at
+ * position p = idx & 7 takes 16-bit half (p & 1) of output word p >> 1. The index idx = j*D + k runs
+ * over the whole weight matrix, so the draw of an element does not depend on how the labels are
+ * chunked or tiled. */
 uint32_t orc_r16(uint64_t seed, uint64_t step, uint64_t idx) {
-  uint64_t w = idx & 31;
-  uint64_t g = 4 * (idx >> 5) + 2 * ((w >> 4) & 1) + ((w >> 2) & 1);
-  unsigned p = (unsigned)(4 * ((w >> 3) & 1) + (w & 3));
+  uint64_t g = idx >> 3;
+  unsigned p = (unsigned)(idx & 7);
   uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
   uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
   uint32_t x[4];

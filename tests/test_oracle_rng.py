@@ -68,10 +68,8 @@ def test_philox_zero_block_known_value(orc, rocrand_kat):
 
 
 def _block_elements(g):
-    # the 8 element indices of block g, in position order p = 0..7: group g >> 2 of 32 indices,
-    # index bits 4 and 2 from g & 3, bit 3 and bits 1..0 from p
-    base, q = 32 * (g >> 2), g & 3
-    return [base + 16 * (q >> 1) + 4 * (q & 1) + 8 * (p >> 2) + (p & 3) for p in range(8)]
+    # the 8 element indices of block g, in position order p = 0..7: 8g .. 8g + 7
+    return [8 * g + p for p in range(8)]
 
 
 def test_r16_slices_the_block(orc, rocrand_kat):
@@ -82,10 +80,24 @@ def test_r16_slices_the_block(orc, rocrand_kat):
             assert int(orc.r16(s, step, idx, 1)[0]) == halves[p], (s, step, g, p)
 
 
+def test_r16_array_crosses_blocks(orc, rocrand_kat):
+    # 10 consecutive draws from index 8g - 1: the last position of block g - 1, all of block g (the
+    # rocRAND words), the first position of block g + 1 (from the oracle's generator, pinned above)
+    for (s, step, g), ref in zip(TRIPLES, rocrand_kat):
+        if g == 0 or g + 1 >= 2**64:
+            continue
+        r = [int(v) for v in orc.r16(s, step, 8 * g - 1, 10)]
+        prev = orc.philox4x32(*_ctr_key(s, step, g - 1), 10)
+        nxt = orc.philox4x32(*_ctr_key(s, step, g + 1), 10)
+        assert r[0] == int(prev[3]) >> 16
+        assert r[1:9] == [(int(ref[p // 2]) >> (16 * (p % 2))) & 0xFFFF for p in range(8)]
+        assert r[9] == int(nxt[0]) & 0xFFFF
+
+
 def test_r16_blocks_partition_the_indices():
-    # every index of a 32-group belongs to exactly one of its 4 blocks
-    seen = sorted(i for q in range(4) for i in _block_elements(4 * 5 + q))
-    assert seen == list(range(32 * 5, 32 * 6))
+    # every index belongs to exactly one block, at one position
+    seen = sorted(i for g in range(20, 24) for i in _block_elements(g))
+    assert seen == list(range(160, 192))
 
 
 def test_r16_statistics(orc):
