@@ -42,12 +42,6 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<uint16_t*>(p)));
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i writes lds_base + 16 i (the
-// wave-uniform base goes to M0). Kept out of lambdas: the builtin only exists for the device.
-__device__ __forceinline__ void global_load_lds16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
-}
-
 // Raw buffer access through a resource of `bytes` bytes at `base` (both wave-uniform): loads at or
 // beyond the end return zeros and stores there are dropped by the hardware's range check.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
@@ -64,18 +58,6 @@ __device__ __forceinline__ void buffer_store16(i32x4_t v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
-__device__ __forceinline__ void buffer_store8(i32x2_t v, __amdgpu_buffer_rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-}
-__device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
-}
-
-// instruction-scheduling group (LLVM AMDGPU IGroupLP): N instructions of class MASK (0x2 VALU,
-// 0x8 MFMA, 0x100 LDS read, 0x200 LDS write, 0x20 VMEM read, 0x40 VMEM write), in program order of
-// these calls within the scheduling region
-template <int MASK, int N>
-__device__ __forceinline__ void sched_group() { __builtin_amdgcn_sched_group_barrier(MASK, N, 0); }
 
 // f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile time
 template <int B, int E, typename F>
@@ -88,9 +70,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // no instruction is scheduled across this point
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// wait until all of this wave's memory operations have completed
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ s16x8_t join(s16x4_t lo, s16x4_t hi) {
   return s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

@@ -9,8 +9,9 @@
 //   * SR of an FP32 value t with 16 random bits r: keep the truncated magnitude, add one unit in
 //     the last place iff (dropped fraction, as a 16-bit fixed-point number q) + r >= 2^16;
 //   * r comes from Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3",
-//     SC'11) with key = seed and counter = (element index >> 3, step); element idx = j*D + k uses
-//     16-bit half (idx & 1) of output word (idx >> 1) & 3.
+//     SC'11) with key = seed and counter = (g, step): the element indices 8g .. 8g + 7 share block
+//     g = idx >> 3, and element idx = j*D + k takes 16-bit half (idx & 1) of output word
+//     (idx >> 1) & 3 of its block.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,11 +41,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // gfx950's FP8 conversions use the OCP encoding (0x7E = 448, 0x7F/0xFF NaN, subnormals kept).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
-// E4M3 values have at most 4 significant bits and exponents inside BF16's range: exact
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
-
 // the four E4M3 codes in the bytes of v as BF16 codes: lo = bytes 0 | 1 << 16, hi = bytes 2 | 3 << 16
-// (gfx950's paired FP8 -> BF16 conversion with unit scale; exact, as above)
+// (gfx950's paired FP8 -> BF16 conversion with unit scale; exact: E4M3 values have at most 4
+// significant bits and exponents inside BF16's range)
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t v, uint32_t& lo, uint32_t& hi) {
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v, 1.0f, false));
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v, 1.0f, true));
@@ -136,11 +135,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint64_t seed) {
   return c;
 }
 
-// The 8 random 16-bit values of element block g, packed two per word (seed wave-uniform). Within
-// each aligned group of 32 element indices, the 8 indices with equal bits 4 and 2 form block
-// g = 4 (idx >> 5) + 2 bit4 + bit2, in position order p = 4 bit3 + (idx & 3); position p takes
-// 16-bit half p & 1 of word p >> 1. (This is exactly the set of one 32 x 32 MFMA accumulator
-// lane's 8 features of one label and register group pair, so the update needs no lane exchange.)
+// The 8 random 16-bit values of element block g (the element indices 8g .. 8g + 7), packed two per
+// word: position p = idx & 7 takes 16-bit half p & 1 of word p >> 1 (seed wave-uniform).
 __device__ __forceinline__ u32x4 rng_block(uint64_t seed, uint64_t step, uint64_t g) {
   return philox4x32_10(philox_counter(g, step), seed);
 }
@@ -152,8 +148,7 @@ __device__ __forceinline__ uint32_t rng_pick(const u32x4& r, int e) {   // e = p
 
 // the 16 random bits of element idx
 __device__ __forceinline__ uint32_t rng_r16(uint64_t seed, uint64_t step, uint64_t idx) {
-  const uint64_t g = 4 * (idx >> 5) + 2 * ((idx >> 4) & 1) + ((idx >> 2) & 1);
-  return rng_pick(rng_block(seed, step, g), (int)(4 * ((idx >> 3) & 1) + (idx & 3)));
+  return rng_pick(rng_block(seed, step, idx >> 3), (int)(idx & 7));
 }
 
 // the same 16 bits placed in bits 31..16 (the form the SR instructions take)

@@ -214,14 +214,19 @@ __device__ __forceinline__ int row_swz(int j) {
 
 // The fused SGD step with stochastic rounding for one wave's 32 labels x 32 features, straight
 // from its dW accumulators. Lane (l32, hi) holds label l32 and, in register 8u + p (u = 0, 1,
-// p = 0..7), feature 16u + 8 (p >> 2) + 4 hi + (p & 3) of the 32: for each u the 8 elements of one
-// RNG block (block 4 grp + 2u + hi, positions p in order, grp the index of the row's 32-element
-// group), which the lane updates with one Philox block: t = fmaf(-lr, dW, w), hardware stochastic
-// rounding. Swapping the packed results of block 1 of lane half 0 with those of block 0 of lane
-// half 1 leaves each lane the 16 consecutive features 16 hi .. 16 hi + 15 of its label, stored in
-// 16-byte pieces. The work is cut into UPD_PHASES phases so that it can be spread between MFMAs:
-// 0 the RNG counters, 1..10 the Philox rounds (these RNG_PHASES need no dW), 11 old-weight reads,
-// 12..19 two weights each (rounding and packing), 20 the exchange and the stores.
+// p = 0..7), feature 16u + 8 (p >> 2) + 4 hi + (p & 3) of the 32. The 32 features are the RNG
+// blocks 4 grp .. 4 grp + 3 (eight consecutive features each, grp the index of the row's 32-element
+// group), and register 8u + p sits in block 4 grp + 2u + (p >> 2) at position 4 hi + (p & 3): a
+// lane holds half of each of the four blocks. Lane half hi computes the two blocks 4 grp + 2 hi and
+// + 1 (Philox rounds on both at once), then the lane pair swaps the halves of the output words each
+// side needs (four v_permlane32_swap): afterwards words 2k + w (k, w = 0, 1) of u32x4 R_u hold word
+// 2 hi + w of block 4 grp + 2u + k, so that register 8u + p takes 16-bit half p & 1 of word p >> 1 of
+// R_u. Then t = fmaf(-lr, dW, w) and hardware stochastic rounding per element. Swapping the packed
+// results of u = 1 of lane half 0 with those of u = 0 of lane half 1 leaves each lane the 16
+// consecutive features 16 hi .. 16 hi + 15 of its label, stored in 16-byte pieces. The work is cut
+// into UPD_PHASES phases so that it can be spread between MFMAs: 0 the RNG counters, 1..10 the
+// Philox rounds and after the last the word exchange (these RNG_PHASES need no dW), 11 old-weight
+// reads, 12..19 two weights each (rounding and packing), 20 the exchange and the stores.
 //   ow    the label's W row in the LDS tile (BF16); owa/owb[u] element offsets of the runs
 //         16u + 4 hi and 16u + 8 + 4 hi of the wave's features in it
 //   roff  byte offset of the label's row in the chunk's weight resource plus that of the wave's
@@ -241,10 +246,20 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   if (p == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) st.c[u] = philox_counter(4 * grp + 2 * u + hi, step);
+    for (int k = 0; k < 2; ++k) st.c[k] = philox_counter(4 * grp + 2 * hi + k, step);
   } else if (p <= 10) {
     const uint32_t k0 = philox_key0(seed, p - 1), k1 = philox_key1(seed, p - 1);
     philox_round2(st.c[0], st.c[1], k0, k1);
+    if (p == 10) {
+      // word w of lane half 1's blocks (4 grp + 2 + k) <-> word 2 + w of lane half 0's blocks
+      // (4 grp + k): each side keeps its own half of the words and receives the other's
+      const auto s00 = __builtin_amdgcn_permlane32_swap(st.c[0].x, st.c[0].z, false, false);
+      const auto s01 = __builtin_amdgcn_permlane32_swap(st.c[0].y, st.c[0].w, false, false);
+      const auto s10 = __builtin_amdgcn_permlane32_swap(st.c[1].x, st.c[1].z, false, false);
+      const auto s11 = __builtin_amdgcn_permlane32_swap(st.c[1].y, st.c[1].w, false, false);
+      st.c[0] = u32x4{(uint32_t)s00[0], (uint32_t)s01[0], (uint32_t)s10[0], (uint32_t)s11[0]};
+      st.c[1] = u32x4{(uint32_t)s00[1], (uint32_t)s01[1], (uint32_t)s10[1], (uint32_t)s11[1]};
+    }
   } else if (p == 11) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -337,7 +352,6 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   static_assert(NBW >= 1 && NDW == NDX, "slots alternate dW and dX");
   constexpr int NSLOT = NDW + NDX;
   constexpr int PFS = NH == 2 ? 2 : 4;         // operand prefetch distance (slots)
-  constexpr int STAGE_MODE = 2;
   constexpr int GTE = TJ2 * MB;                // G tile elements
   constexpr int GCPR = MB / 8;                 // 16-byte chunks per G row
   constexpr int GPT = TJ2 * GCPR / NT;         // G chunks per thread
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     const int tn = t + 1 < nt ? t + 1 : nt - 1;
     uint16_t* gnext = GB ? Gs0 : Gs1;
     __syncthreads();                           // tile t resident; iteration t-1 fully done
-    if constexpr (NH == 2 && STAGE_MODE != 0) static_for<0, NLD>([&](auto K) { load_item(K, tn); });
+    if constexpr (NH == 2) static_for<0, NLD>([&](auto K) { load_item(K, tn); });
     pre(t);
     const uint16_t* gs = GB ? Gs1 : Gs0;
     const uint16_t* ws = Ws[wb];
@@ -551,14 +565,14 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
       constexpr int z = decltype(Z)::value, m = z >> 1;
       if constexpr (z + PFS < NSLOT) fetch(std::integral_constant<int, z + PFS>{});
       constexpr int HALF = NSLOT / 2;
-      if constexpr (NH == 1 || STAGE_MODE == 0)
+      if constexpr (NH == 1)                   // loads over the first half, LDS writes over the second
         static_for<0, NLD>([&](auto K) {
           if constexpr (decltype(K)::value * HALF / NLD == z) load_item(K, tn);
           if constexpr (HALF + decltype(K)::value * HALF / NLD == z) store_item(K, gnext, wbn);
         });
-      else if constexpr (STAGE_MODE >= 2)      // LDS writes spread over the slots from S0 on
+      else                                     // (loads issued after the barrier) LDS writes over the last third
         static_for<0, NLD>([&](auto K) {
-          constexpr int S0 = STAGE_MODE == 2 ? NSLOT - NSLOT / 3 : HALF;
+          constexpr int S0 = NSLOT - NSLOT / 3;
           if constexpr (S0 + decltype(K)::value * (NSLOT - S0) / NLD == z) store_item(K, gnext, wbn);
         });
       if constexpr ((z & 1) == 0) accW[m % NJB] = mfma_bf16(xT[m / NJB], opW[m], accW[m % NJB]);
@@ -575,7 +589,6 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 #pragma unroll
     for (int jl = 0; jl < NJB; ++jl) accP[jl] = accW[jl];
     post(t, wb);
-    if constexpr (NH == 2 && STAGE_MODE == 1) static_for<0, NLD>([&](auto K) { store_item(K, gnext, wbn); });
     tP = t;
     wbP = wb;
   };
