@@ -64,11 +64,11 @@ def lib():
         L.orc_step.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
                                ctypes.c_float, u64, u64, P, P, P, P, ctypes.c_int]
         L.orc_update_from_g.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_float,
-                                        u64, u64, P, ctypes.c_int]
+                                        u64, u64, P, P, ctypes.c_int]
         L.orc_logits.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P,
                                  ctypes.c_int, P, ctypes.c_int]
         L.orc_update_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P,
-                                      ctypes.c_float, u64, u64, P, ctypes.c_int, P, ctypes.c_int]
+                                      ctypes.c_float, u64, u64, P, ctypes.c_int, P, P, P, ctypes.c_int]
         L.orc_update_rows_from_g.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P,
                                              ctypes.c_float, u64, u64, P, ctypes.c_int, P, ctypes.c_int]
         L.orc_dx_rows.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, P, P, P,
@@ -170,14 +170,17 @@ def step(wfmt, W, X, row_ptr, ids, lr, seed, step_, want_z=False, want_g=False, 
     return Wn, dX, (loss.value if want_loss else None), Z, G
 
 
-def update_from_g(wfmt, W, X, G, lr, seed, step_, nthreads=0):
+def update_from_g(wfmt, W, X, G, lr, seed, step_, nthreads=0, want_t=False):
+    """Updated codes given gradient codes G [B][L]; with want_t also the FP32 values t [L][D] that
+    were stochastically rounded: returns W_new or (W_new, T)."""
     W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
     G = _c(G, np.uint16)
     assert G.shape == (B, L)
     out = np.empty_like(W)
-    _chk(lib().orc_update_from_g(wfmt, _p(W), L, D, _p(X), B, _p(G), float(lr), seed, step_, _p(out), nthreads),
-         "update_from_g")
-    return out
+    T = np.empty((L, D), np.float32) if want_t else None
+    _chk(lib().orc_update_from_g(wfmt, _p(W), L, D, _p(X), B, _p(G), float(lr), seed, step_, _p(out), _p(T),
+                                 nthreads), "update_from_g")
+    return (out, T) if want_t else out
 
 
 def logits(wfmt, W, X, js, nthreads=0):
@@ -187,14 +190,18 @@ def logits(wfmt, W, X, js, nthreads=0):
     return Z
 
 
-def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0):
+def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0, want_detail=False):
+    """Updated codes of weight rows js [nj][D]; with want_detail also their gradient codes G [B][nj]
+    and the FP32 values t [nj][D] before rounding: returns Wrows or (Wrows, G, T)."""
     W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
     rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32); js = _c(js, np.int64)
     out = np.empty((js.size, D), wdtype_np(wfmt))
+    G = np.empty((B, js.size), np.uint16) if want_detail else None
+    T = np.empty((js.size, D), np.float32) if want_detail else None
     _chk(lib().orc_update_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
-                               float(lr), seed, step_, _p(js), js.size, _p(out), nthreads),
+                               float(lr), seed, step_, _p(js), js.size, _p(out), _p(G), _p(T), nthreads),
          "update_rows")
-    return out
+    return (out, G, T) if want_detail else out
 
 
 def update_rows_from_g(wfmt, W, X, G, lr, seed, step_, js, nthreads=0):
@@ -225,6 +232,68 @@ def grad_exact(W, X, Y):
     _chk(lib().orc_grad_exact(L, D, B, _p(W), _p(X), _p(Y), _p(Z), _p(G), _p(dX), _p(dW),
                               ctypes.cast(ctypes.pointer(loss), ctypes.c_void_p)), "grad_exact")
     return Z, G, dX, dW, loss.value
+
+
+# ---- all-label logits and ranking for many queries at full size -------------------------------
+
+_LUT = {}
+
+
+def _value_lut(wfmt):
+    """Decoded value of every code, from the oracle's own decoders (65,536 BF16 or 256 E4M3 codes)."""
+    if wfmt not in _LUT:
+        if wfmt == W_BF16:
+            _LUT[wfmt] = bf16_value(np.arange(65536, dtype=np.uint16))
+        else:
+            _LUT[wfmt] = e4m3_value(np.arange(256, dtype=np.uint8))
+    return _LUT[wfmt]
+
+
+def forward_x_values(wfmt, X):
+    """The forward operand of queries X (BF16 codes) as binary64 values: X itself for BF16 weights,
+    E4M3-RNE(X) for E4M3 weights (the training forward's cast)."""
+    xv = _value_lut(W_BF16)[_c(X, np.uint16)]
+    if wfmt == W_E4M3:
+        xv = _value_lut(W_E4M3)[e4m3_rne_sat(xv)]
+    return xv
+
+
+def logits_dense(wfmt, W, X, block=1 << 16):
+    """FP32 logits of queries X [N][D] against every label of W [L][D]: the same definition as
+    orc_logits (z = FP32 of the binary64 sum of the exact products x~_k w_jk), with the sums taken by
+    numpy's binary64 matrix product (a library routine) over blocks of labels instead of a loop. It
+    differs from orc_logits only in the order of the binary64 additions, which can move z across an
+    FP32 rounding boundary only when the sum lies within ~D 2^-53 of it (pinned against orc_logits).
+    Returns Z [N][L] float32."""
+    W = np.ascontiguousarray(W)
+    L = W.shape[0]
+    xv = forward_x_values(wfmt, X)
+    lut = _value_lut(wfmt)
+    Z = np.empty((xv.shape[0], L), np.float32)
+    for j0 in range(0, L, block):
+        j1 = min(L, j0 + block)
+        Z[:, j0:j1] = (xv @ lut[W[j0:j1]].T).astype(np.float32)
+    return Z
+
+
+def rank_scores(Z, k):
+    """Top-k of each row of the score matrix Z [N][L] under the order (score desc, label asc, NaN
+    after every number): candidates are the labels whose score is at least the row's k-th largest
+    (NaN counted as -inf), ranked by numpy's lexsort. Returns idx [N][k] int32, score [N][k] float32."""
+    Z = np.asarray(Z, np.float32)
+    N, L = Z.shape
+    idx = np.empty((N, k), np.int32)
+    sc = np.empty((N, k), np.float32)
+    for n in range(N):
+        s = Z[n]
+        nan = np.isnan(s)
+        key = np.where(nan, -np.inf, s)
+        vk = np.partition(key, L - k)[L - k]
+        cand = np.nonzero(key >= vk)[0]
+        order = np.lexsort((cand, nan[cand], -key[cand]))[:k]
+        idx[n] = cand[order]
+        sc[n] = s[cand[order]]
+    return idx, sc
 
 
 def topk(wfmt, W, X, k, nthreads=0):

@@ -280,10 +280,12 @@ static float logit(int wfmt, const void* W, int64_t j, int D, const double* xt_r
   return (float)s;
 }
 
-/* updated code of weight (j, k) from its FP32 weight gradient */
+/* updated code of weight (j, k) from its FP32 weight gradient; Tout (nullable) receives the FP32
+ * value t that is stochastically rounded, at the same position i */
 static void store_update(int wfmt, void* Wout, int64_t i, double w, float dw, float lr,
-                         uint64_t seed, uint64_t step, uint64_t idx) {
+                         uint64_t seed, uint64_t step, uint64_t idx, float* Tout) {
   float t = fmaf(-lr, dw, (float)w);        /* one FP32 rounding: SGD without momentum */
+  if (Tout) Tout[i] = t;
   uint32_t r = orc_r16(seed, step, idx);
   if (wfmt == ORC_W_BF16) ((uint16_t*)Wout)[i] = orc_sr_bf16(t, r);
   else ((uint8_t*)Wout)[i] = orc_sr_e4m3(t, r);
@@ -341,7 +343,7 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
       double s = 0.0;
       for (int b = 0; b < B; b++) s += orc_bf16_value(G[(int64_t)b * L + j]) * xb[(int64_t)b * D + k];
       int64_t i = j * (int64_t)D + k;
-      store_update(wfmt, W, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i);
+      store_update(wfmt, W, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i, NULL);
     }
   }
 
@@ -352,7 +354,8 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
 }
 
 int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
-                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, int nthreads) {
+                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, float* Tout,
+                      int nthreads) {
   int rc = check_common(wfmt, W, L, D, X, B);
   if (rc) return rc;
   if (!G || !Wout) return ORC_EINVAL;
@@ -365,7 +368,7 @@ int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t*
       double s = 0.0;
       for (int b = 0; b < B; b++) s += orc_bf16_value(G[(int64_t)b * L + j]) * xb[(int64_t)b * D + k];
       int64_t i = j * (int64_t)D + k;
-      store_update(wfmt, Wout, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i);
+      store_update(wfmt, Wout, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i, Tout);
     }
   }
   free(xb);
@@ -390,20 +393,21 @@ int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int
 
 /* Row j's update given its gradient values g[b] (BF16 values): dW_jk = FP32(sum_b g_b x_bk), summed
  * in binary64 over b ascending; t = fmaf(-lr, dW, w); SR with the draw of element j*D + k; output
- * row i of Wrows. */
+ * row i of Wrows (and of Trows, the FP32 t, when not NULL). */
 static void update_row(int wfmt, const void* W, int64_t j, int D, const double* xb, const double* g, int B,
-                       float lr, uint64_t seed, uint64_t step, void* Wrows, int i) {
+                       float lr, uint64_t seed, uint64_t step, void* Wrows, float* Trows, int i) {
   for (int k = 0; k < D; k++) {
     double s = 0.0;
     for (int b = 0; b < B; b++) s += g[b] * xb[(int64_t)b * D + k];
     store_update(wfmt, Wrows, (int64_t)i * D + k, wval(wfmt, W, j, D, k), (float)s, lr, seed, step,
-                 (uint64_t)(j * (int64_t)D + k));
+                 (uint64_t)(j * (int64_t)D + k), Trows);
   }
 }
 
 int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                     const int32_t* row_ptr, const int32_t* ids, float lr, uint64_t seed,
-                    uint64_t step, const int64_t* js, int nj, void* Wrows, int nthreads) {
+                    uint64_t step, const int64_t* js, int nj, void* Wrows, uint16_t* Grows,
+                    float* Trows, int nthreads) {
   int rc = check_common(wfmt, W, L, D, X, B);
   if (rc) return rc;
   if (!row_ptr || (!ids && row_ptr[B] > 0) || !js || !Wrows || nj < 0) return ORC_EINVAL;
@@ -418,9 +422,12 @@ int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X
   for (int i = 0; i < nj; i++) {
     int64_t j = js[i];
     double* g = (double*)malloc(sizeof(double) * (size_t)B);
-    for (int b = 0; b < B; b++)
-      g[b] = orc_bf16_value(orc_grad_code(logit(wfmt, W, j, D, xt + (int64_t)b * D), has_label(&ls, b, j)));
-    update_row(wfmt, W, j, D, xb, g, B, lr, seed, step, Wrows, i);
+    for (int b = 0; b < B; b++) {
+      uint16_t gc = orc_grad_code(logit(wfmt, W, j, D, xt + (int64_t)b * D), has_label(&ls, b, j));
+      if (Grows) Grows[(int64_t)b * nj + i] = gc;
+      g[b] = orc_bf16_value(gc);
+    }
+    update_row(wfmt, W, j, D, xb, g, B, lr, seed, step, Wrows, Trows, i);
     free(g);
   }
   free(xt); free(xb); labelsets_free(&ls);
@@ -441,7 +448,7 @@ int orc_update_rows_from_g(int wfmt, const void* W, int64_t L, int D, const uint
   for (int i = 0; i < nj; i++) {
     double* g = (double*)malloc(sizeof(double) * (size_t)B);
     for (int b = 0; b < B; b++) g[b] = orc_bf16_value(G[(int64_t)b * nj + i]);
-    update_row(wfmt, W, js[i], D, xb, g, B, lr, seed, step, Wrows, i);
+    update_row(wfmt, W, js[i], D, xb, g, B, lr, seed, step, Wrows, NULL, i);
     free(g);
   }
   free(xb);

@@ -62,20 +62,25 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
              float* dX, double* loss, float* Z, uint16_t* G, int nthreads);
 
 /* The weight half of the step given the gradient codes G ([B][L] BF16): dW = FP32(G^T X) with the
- * BF16 X, t = fmaf(-lr, dW, w), W_out = SR(t). W is not modified; Wout receives [L][D] codes.
- * orc_step's weights equal this function applied to orc_step's own G. */
+ * BF16 X, t = fmaf(-lr, dW, w), W_out = SR(t). W is not modified; Wout receives [L][D] codes and
+ * Tout (nullable) the FP32 values t [L][D] before rounding. orc_step's weights equal this function
+ * applied to orc_step's own G. */
 int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
-                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, int nthreads);
+                      const uint16_t* G, float lr, uint64_t seed, uint64_t step, void* Wout, float* Tout,
+                      int nthreads);
 
 /* Sampled outputs of the same step for large shapes, without modifying W:
  *   orc_logits:      Z[b][i] for labels js[i] (all b)                      -> Z [B][nj]
  *   orc_update_rows: the updated codes of weight rows js[i]                 -> Wrows [nj][D]
+ *                    (nullable: their gradient codes -> Grows [B][nj], and the FP32 values t
+ *                    before rounding -> Trows [nj][D])
  *   orc_dx_rows:     dX rows bs[i] (sums over all L labels, pre-update W)  -> dXrows [nb][D] */
 int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                const int64_t* js, int nj, float* Z, int nthreads);
 int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                     const int32_t* row_ptr, const int32_t* ids, float lr, uint64_t seed,
-                    uint64_t step, const int64_t* js, int nj, void* Wrows, int nthreads);
+                    uint64_t step, const int64_t* js, int nj, void* Wrows, uint16_t* Grows,
+                    float* Trows, int nthreads);
 /* orc_update_rows with given gradient codes: G [B][nj] BF16 codes of labels js (teacher forcing). */
 int orc_update_rows_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,
                            const uint16_t* G, float lr, uint64_t seed, uint64_t step, const int64_t* js,

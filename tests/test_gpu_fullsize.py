@@ -1,15 +1,16 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times (its chunk
 size and workspace), on sampled outputs the oracle computes one by one: logits of sampled labels
 (chunk boundaries, the ragged end and the most frequent labels among them), the updated weight rows
-of those labels (given the device's gradient codes, and free-running), dX rows (sums over all L
-labels with the pre-update weights), and the top-k of sampled queries."""
+of those labels against the oracle's own step (free-running, every unequal element classified), dX
+rows (sums over all L labels with the pre-update weights), and the top-k of 64 held-out queries
+ranked by the oracle over all labels."""
 import numpy as np
 import pytest
 import torch
 
 import workloads as wk
-from tests._helpers import (RTOL, assert_close, assert_grad_codes_match, assert_weights_match, batch_to_dev,
-                            update_error_bound, weight_report)
+from tests._helpers import (RTOL, assert_close, assert_grad_codes_match, assert_weights_free_running, batch_to_dev,
+                            check_topk_rows, weight_report)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -61,26 +62,30 @@ def test_full_size_step_sampled(elmo, orc, name):
     Wg = _host_codes(W[torch.from_numpy(js).to(dev)])
     assert elmo.step_flags(elmo.last_workspace) == 0
 
-    # weights of the sampled rows, given the device's gradient codes, then free-running
-    Wt = orc.update_rows_from_g(wl.wfmt, W0, bt.X, Gg, wl.lr, wl.seed, 0, js)
-    eq = assert_weights_match(Wg, Wt, wl.wfmt, abs_bound=update_error_bound(Gg, bt.X, wl.lr, B))
-    Wf = orc.update_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, wl.lr, wl.seed, 0, js)
-    eq_free = weight_report(Wg, Wf, wl.wfmt)[0]
-    assert eq_free >= 0.999, f"free-running weights only {eq_free:.6f} equal"
+    # weights of the sampled rows against the oracle's own step (its gradient codes, its t values)
+    Wf, Gr, Tf = orc.update_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, wl.lr, wl.seed, 0, js, want_detail=True)
+    flips = assert_grad_codes_match(Gg, Gr)
+    R = np.stack([orc.r16(wl.seed, 0, int(j) * wl.D, wl.D) for j in js])
+    c = assert_weights_free_running(orc, Wg, Wf, Tf, R, wl.wfmt, bt.X, Gg, Gr, wl.lr, label=f" ({js.size} rows)")
+    eq = c["equal"] / c["n"]
+    # diagnostic: the oracle's weight half on the device's own gradient codes (the update kernel alone)
+    eq_tf = weight_report(Wg, orc.update_rows_from_g(wl.wfmt, W0, bt.X, Gg, wl.lr, wl.seed, 0, js), wl.wfmt)[0]
+    assert eq_tf >= 0.999, f"weights given the device's gradient codes only {eq_tf:.6f} equal"
 
     # dX rows: sums over every label
     bs = np.array([0, B - 1], np.int32)
     dXr = orc.dx_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, bs)
     edx = assert_close(dX.cpu().numpy()[bs], dXr, RTOL[wl.wfmt])
-    print(f"  Z rel {ez:.2e}  W equal {eq:.6f} (free {eq_free:.6f})  dX rel {edx:.2e}", flush=True)
+    print(f"  Z rel {ez:.2e}  G flips {flips:.2e}  W equal {eq:.6f} (given device G {eq_tf:.6f})  dX rel {edx:.2e}",
+          flush=True)
 
 
 @pytest.mark.parametrize("name", ["e4m3_3m", "bf16_8p6m"])
+@pytest.mark.timeout(900)
 def test_full_size_topk_sampled_queries(elmo, orc, name):
-    """Top-k over all labels of the full weight matrix for N held-out queries; two queries are
-    ranked by the oracle over all labels. Indices must be identical except where the oracle's
-    neighbouring scores are closer than the logit tolerance (then the device's label must score
-    within that tolerance of the oracle's at that rank)."""
+    """Top-k over all labels of the full weight matrix for N = 1024 held-out queries in one call; 64 of
+    them (spread over the query blocks) are ranked by the oracle over all labels, with the device's
+    and the oracle's logits of those rows over all labels giving each row's measured error."""
     wl = wk.WORKLOADS[name]
     k = wl.topk or 5
     dev = torch.device("cuda:0")
@@ -88,15 +93,16 @@ def test_full_size_topk_sampled_queries(elmo, orc, name):
     N = 1024
     Xe = wk.make_eval_x(wl, N)
     print(f"  {wl.name}: top-{k} of N={N}", flush=True)
-    idx, score = elmo.topk(W, torch.from_numpy(Xe.view(np.int16)).to(dev), k)
+    Xd = torch.from_numpy(Xe.view(np.int16)).to(dev)
+    idx, score = elmo.topk(W, Xd, k)
     idx = idx.cpu().numpy(); score = score.cpu().numpy()
+    qs = np.unique(np.concatenate([[0, 1, 127, 128, 511, 512, N - 2, N - 1],
+                                   np.random.default_rng(77).choice(N, 56, replace=False)]))[:64]
+    Zg = elmo.logits(W, Xd[torch.from_numpy(qs).to(dev)], 0, wl.L).cpu().numpy()
     W0 = _host_codes(W)
-    qs = np.array([0, N - 1])
-    oi, osc = orc.topk(wl.wfmt, W0, Xe[qs], k)
-    tol = RTOL[wl.wfmt] * 1e-2 * max(float(np.abs(osc).max()), 1e-30)
-    for r, q in enumerate(qs):
-        assert np.all(np.abs(score[q] - osc[r]) <= tol), (score[q], osc[r])
-        for p in range(k):
-            if idx[q, p] != oi[r, p]:
-                zg = orc.logits(wl.wfmt, W0, Xe[q:q + 1], np.array([idx[q, p]], np.int64))[0, 0]
-                assert abs(zg - osc[r, p]) <= tol, f"query {q} rank {p}: label {idx[q, p]} vs {oi[r, p]}"
+    del W
+    torch.cuda.empty_cache()
+    print(f"  oracle logits of {qs.size} queries over {wl.L} labels", flush=True)
+    Zr = orc.logits_dense(wl.wfmt, W0, Xe[qs])
+    oi, osc = orc.rank_scores(Zr, k)
+    check_topk_rows(idx[qs], score[qs], oi, osc, Zg, Zr, label=f" {wl.name}")

@@ -276,3 +276,88 @@ def test_topk_nan_ranks_last(orc):
     idx, score = orc.topk(0, W, bt.X, 4)
     assert np.all(np.sort(idx[:, :2], axis=1) == [10, 20])
     assert np.all(np.isnan(score[:, 2:])) and np.array_equal(idx[:, 2:], np.tile([0, 1], (4, 1)))
+
+
+# ---------------------------------------------------------------------------------------------- #
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_update_t_outputs_are_the_rounded_values(orc, wfmt):
+    """The FP32 value t the oracle hands to stochastic rounding: t = fmaf(-lr, dW, w) with dW the
+    binary32 rounding of the exact sum (recomputed here with exact rationals), and the stored code is
+    the stochastic rounding of exactly that t with the element's draw."""
+    wl, W, bt = _small_case(wfmt, B=7, D=64, L=40)
+    lr, seed, step = 0.05, 3, 1
+    Wn, _, _, _, G = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, lr, seed, step, want_g=True)
+    Wu, T = orc.update_from_g(wfmt, W, bt.X, G, lr, seed, step, want_t=True)
+    assert np.array_equal(Wu, Wn)
+    g = _bf16_val(G); x = _bf16_val(bt.X); w = _wval(wfmt, W)
+    lr32 = Fraction(float(np.float32(lr)))
+    for (j, k) in [(0, 0), (3, 17), (39, 63), (20, 5)]:
+        dw = float(np.float32(float(sum(Fraction(g[b, j]) * Fraction(x[b, k]) for b in range(7)))))
+        t = float(np.float32(float(Fraction(w[j, k]) - lr32 * Fraction(dw))))
+        assert T[j, k] == np.float32(t)
+    R = orc.r16(seed, step, 0, W.size).reshape(W.shape)
+    sr = orc.sr_bf16 if wfmt == wk.W_BF16 else orc.sr_e4m3
+    assert np.array_equal(sr(T, R), Wn)
+    js = np.array([0, 5, 39], np.int64)
+    Wr, Gr, Tr = orc.update_rows(wfmt, W, bt.X, bt.row_ptr, bt.ids, lr, seed, step, js, want_detail=True)
+    assert np.array_equal(Wr, Wn[js]) and np.array_equal(Gr, G[:, js]) and np.array_equal(Tr, T[js])
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_dense_logits_and_ranking_match_the_loops(orc, wfmt):
+    """The blocked binary64 matrix-product form of the logits equals orc_logits (same definition,
+    other summation order: at most one FP32 unit, almost always bit-equal), and the ranking of a score
+    matrix by lexsort equals orc_topk, exact ties (duplicated rows) and NaN included."""
+    wl, W, bt = _small_case(wfmt, B=21, D=128, L=3000, seed=4)
+    W = W.copy()
+    W[2999] = W[5]; W[1000] = W[5]; W[77] = W[1500]
+    X = wk.make_eval_x(wl, 21)
+    Zd = orc.logits_dense(wfmt, W, X, block=700)
+    Zl = orc.logits(wfmt, W, X, np.arange(wl.L))
+    assert np.all(np.abs(Zd.astype(np.float64) - Zl) <= np.spacing(np.abs(Zl)))
+    assert (Zd == Zl).mean() >= 0.9999
+    for k in (1, 5, 64):
+        i_ref, s_ref = orc.topk(wfmt, W, X, k)
+        i_d, s_d = orc.rank_scores(Zl, k)
+        assert np.array_equal(i_d, i_ref) and np.array_equal(s_d, s_ref)
+    Zn = Zl.copy(); Zn[:, 10:] = np.nan; Zn[0, 3] = -np.inf
+    i_n, _ = orc.rank_scores(Zn, 12)
+    assert np.array_equal(i_n[1], np.concatenate([np.argsort(-Zl[1, :10], kind="stable"), [10, 11]]))
+    assert list(i_n[0][:10]) == [j for j in np.lexsort((np.arange(10), -Zn[0, :10].astype(np.float64)))]
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_nan_propagation(orc, wfmt):
+    """NaN follows IEEE arithmetic through the step: a NaN weight makes its label's logits, gradient
+    codes and updated row NaN and every dX element NaN (each sums over that label); a NaN feature
+    makes its sample's logits and dX row NaN and, through dW = G^T X, every updated weight NaN."""
+    wl, W, bt = _small_case(wfmt, B=6, D=64, L=50)
+    nan_code = 0x7FC0 if wfmt == wk.W_BF16 else 0x7F
+    Wb = W.copy(); Wb[13, 9] = nan_code
+    Wn, dX, _, Z, G = orc.step(wfmt, Wb, bt.X, bt.row_ptr, bt.ids, 0.05, 1, 0, want_z=True, want_g=True)
+    isnan = np.isnan(_wval(wfmt, Wn))
+    assert isnan[13].all() and not isnan[np.arange(50) != 13].any()
+    assert np.isnan(Z[:, 13]).all() and np.isfinite(np.delete(Z, 13, axis=1)).all()
+    assert np.isnan(_bf16_val(G[:, 13])).all() and np.isnan(dX).all()
+    Xb = bt.X.copy(); Xb[2, 40] = 0x7FC0
+    Wn, dX, _, Z, _ = orc.step(wfmt, W, Xb, bt.row_ptr, bt.ids, 0.05, 1, 0, want_z=True)
+    assert np.isnan(_wval(wfmt, Wn)).all()
+    assert np.isnan(Z[2]).all() and np.isfinite(np.delete(Z, 2, axis=0)).all()
+    assert np.isnan(dX[2]).all() and np.isfinite(np.delete(dX, 2, axis=0)).all()
+
+
+@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
+def test_sample_permutation_invariance(orc, wfmt):
+    """Permuting the samples (feature rows with their label rows) permutes dX's rows exactly (each is
+    a sum over labels, in the same order) and leaves the weights unchanged except where the new order
+    of the binary64 sum over samples moves dW across a binary32 rounding boundary (rare)."""
+    wl, W, bt = _small_case(wfmt, B=12, D=64, L=200)
+    perm = np.random.default_rng(3).permutation(12)
+    rows = [bt.ids[bt.row_ptr[b]:bt.row_ptr[b + 1]] for b in perm]
+    rp = np.zeros(13, np.int32); rp[1:] = np.cumsum([len(r) for r in rows])
+    ids = np.concatenate(rows).astype(np.int32)
+    Wa, dXa, _, _, _ = orc.step(wfmt, W, bt.X, bt.row_ptr, bt.ids, 0.05, 2, 0)
+    Wp, dXp, _, _, _ = orc.step(wfmt, W, bt.X[perm], rp, ids, 0.05, 2, 0)
+    d = np.abs(np.asarray(Wa, np.int64) - np.asarray(Wp, np.int64))
+    assert (d == 0).mean() >= 0.9999
+    assert np.array_equal(dXa[perm], dXp)
