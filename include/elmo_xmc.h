@@ -49,7 +49,7 @@ enum { ELMO_W_BF16 = 0, ELMO_W_E4M3 = 1 };
  * one chunk of weight rows stays below 2 GiB). */
 #define ELMO_MAX_B 256
 #define ELMO_MAX_D 1024
-#define ELMO_MAX_TOPK 32
+#define ELMO_MAX_TOPK 64
 
 int elmo_abi_version(void);
 const char* elmo_status_str(int status);
@@ -68,11 +68,10 @@ const char* elmo_status_str(int status);
  *            raise ELMO_FLAG_ROW_PTR). `nnz` is the host-side count.
  *   lr       SGD learning rate (cast to FP32 by the caller's value).
  *   seed, step  key the counter-based RNG of the stochastic rounding: Philox4x32-10 with key =
- *            seed, counter = (g, step); element idx = j*D + k belongs to block
- *            g = 4 (idx >> 5) + 2 ((idx >> 4) & 1) + ((idx >> 2) & 1) at position
- *            p = 4 ((idx >> 3) & 1) + (idx & 3), which takes 16-bit half p & 1 of output word
- *            p >> 1. Calling with the same (seed, step) on the same inputs reproduces the same W
- *            bit for bit, whatever the chunk size.
+ *            seed, counter = (g, step); element idx = j*D + k belongs to block g = idx >> 3 at
+ *            position p = idx & 7, which takes 16-bit half p & 1 of output word p >> 1. Calling
+ *            with the same (seed, step) on the same inputs reproduces the same W bit for bit,
+ *            whatever the chunk size.
  *   chunk    labels per chunk: bounds the transient G buffer to B_pad * chunk * 2 bytes.
  *   dX       [B, D] FP32, OVERWRITTEN with sum_j G[b, j] * W_old[j, :] (pre-update weights).
  *   loss_sum nullable; if given, receives the FP32 value of the summed BCE over all (b, j).

@@ -4,7 +4,7 @@
 // weights), never materialised: each work-group owns 128 samples and one label range, computes
 // 128 x 128 score tiles on the matrix cores (the same forward tile as the training step), stages
 // each tile in LDS and lets two threads per sample keep running top-KK lists in registers (KK is k
-// rounded up to 8 or 32). Lists are ordered by (score desc, label asc) with NaN after numbers.
+// rounded up to 8, 32 or 64). Lists are ordered by (score desc, label asc) with NaN after numbers.
 // Each list publishes its last entry's score in LDS as a bound: a tile's scores are first tested
 // against the bounds in registers, and only those that may enter a list (usually none, once the
 // lists have filled) go through an LDS queue to their list's thread; a tile with more such
@@ -54,8 +54,9 @@ __device__ __forceinline__ float reg_pick16(const f32x16_t& a, int i) {
   return v;
 }
 
+// (lists of 64 take the whole register file of a SIMD lane: one work-group per CU)
 template <int WF, int KK>
-__global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
+__global__ __launch_bounds__(256, KK > 32 ? 1 : 2) void k_topk_scan(const uint8_t* __restrict__ W, int64_t L, int D,
                                                    const uint8_t* __restrict__ Xf, int nbn, int NRg,
                                                    float* __restrict__ cs, int* __restrict__ ci) {
   constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void k_topk_scan(const uint8_t* __restrict_
 }
 
 template <int KK>
-__global__ void k_topk_merge(const float* __restrict__ cs, const int* __restrict__ ci, int N, int Npad, int NRg,
+__global__ __launch_bounds__(128) void k_topk_merge(const float* __restrict__ cs, const int* __restrict__ ci, int N, int Npad, int NRg,
                              int k, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
@@ -262,7 +263,7 @@ static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 TopkLayout topk_layout(int N, int D, int64_t L, int k, int wdtype) {
   TopkLayout s{};
-  const int KK = k <= 8 ? 8 : 32;
+  const int KK = k <= 8 ? 8 : k <= 32 ? 32 : 64;
   const int nbn = (N + TN - 1) / TN;
   s.MB = nbn * TN;                                    // padded sample count
   const int64_t ntile = (L + TJ1 - 1) / TJ1;
@@ -307,8 +308,9 @@ int run_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, 
                      wdtype == W_BF16_ ? (uint16_t*)(ws + s.xb) : (uint16_t*)nullptr,
                      wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr);
   if (hipGetLastError() != hipSuccess) return ELMO_EHIP_;
-  return k <= 8 ? topk_launch<8>(W, wdtype, L, D, N, k, idx, score, s, ws, st)
-                : topk_launch<32>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
+  if (k <= 8) return topk_launch<8>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
+  if (k <= 32) return topk_launch<32>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
+  return topk_launch<64>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
 }
 
 }  // namespace elmo

@@ -72,7 +72,7 @@ def test_step_rejects_invalid_arguments_before_launch(L):
 def test_topk_rejects_invalid_arguments(L):
     null = None
     assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 0, null, null, null, 0, null) == -2
-    assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 33, null, null, null, 0, null) == -2
+    assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 65, null, null, null, 0, null) == -2      # k > 64
     assert L.elmo_xmc_topk(null, 0, 10, 128, null, 4, 11, null, null, null, 0, null) == -2
     assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 5, null, null, null, 0, null) == -1
     assert L.elmo_xmc_topk_workspace_bytes(4, 128, 1000, 0, 0) == 0
