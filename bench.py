@@ -14,7 +14,9 @@ timed steps carry no event between kernels; the per-kernel averages come from a 
 same number of steps with HIP events around every forward and backward launch (its own ms/step is
 reported beside them, since the events add a few microseconds between the kernels they bracket,
 with the median of its per-step times). The first warm-up step, with cold caches, is timed on its
-own (`first_step_ms`).
+own (`first_step_ms`). The same line carries a `bf16_8p6m` object measured the same way on the
+8.6M-label BF16 head (B=128, D=768, chunk 262,144, lr 0.05), whose step is bound by HBM, with its
+own top-5 pass over 4,096 held-out queries, roofline and CPU baseline.
 """
 from __future__ import annotations
 
@@ -44,6 +46,10 @@ def parse():
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--topk-n", type=int, default=4096)
     ap.add_argument("--no-kahan", action="store_true")
+    ap.add_argument("--second-workload", default="bf16_8p6m",
+                    help="workload measured into its own object of the same line ('none' to skip)")
+    ap.add_argument("--no-8p6m", action="store_true", help="same as --second-workload none")
+    ap.add_argument("--steps-8p6m", type=int, default=10, help="timed steps of the second workload")
     ap.add_argument("--kahan-params", type=int, default=110_000_000,
                     help="encoder parameters of the Kahan-compensated BF16 update pass (768-wide, 12 layers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -189,32 +195,39 @@ def cpu_topk_baseline(wl, W_dev, Xe, k, target_s, nq=256):
                       f"{t:.2f} s; scaled linearly to all labels", "seconds": round(t, 3), "labels": Ls}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: runs on exactly one GPU (--gpus 1); multi-GPU runs are not implemented",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.copy_bytes:
-        copy_reference(args.copy_bytes)
-        return
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo) and logical CPU count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
 
+
+def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
+    """One workload: W resident in HBM, `warmup` untimed steps (the first timed on its own), `steps`
+    timed steps with no event between kernels, then the same number again with events around every
+    forward and backward launch for the per-kernel averages; the top-k pass; the CPU oracle on a
+    bounded sample. Returns the workload's JSON object; frees its device memory."""
     import numpy as np
     import torch
 
     import precision_label_chunk_amd as elmo
     import workloads as wk
 
-    wl = wk.WORKLOADS[args.workload]
+    wl = wk.WORKLOADS[name]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    elmo.lib()
+    stream = torch.cuda.current_stream()
     torch.cuda.reset_peak_memory_stats(dev)
 
     # inputs resident in HBM before timing
     W = wk.make_w_device(wl.L, wl.D, wl.wfmt, seed=wl.seed, device=dev)
-    nb = args.warmup + args.steps
+    nb = warmup + steps
     host_batches = [wk.make_batch(wl, step=s) for s in range(nb)]
     batches = []
     for bt in host_batches:
@@ -227,6 +240,7 @@ def main():
     torch.cuda.synchronize()
     # the step's peak HBM counts what is resident while it runs (the library allocates nothing),
     # not the transients of generating the weights
+    torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats(dev)
     hbm_parts = {"weights": W.numel() * W.element_size(), "workspace": ws.numel(),
                  "batches": sum(t.numel() * t.element_size() for b in batches for t in b),
@@ -234,103 +248,117 @@ def main():
 
     # the first warm-up step runs with cold caches (and the library's lazy set-up): timed on its own
     evc = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for s in range(args.warmup):
+    for s in range(warmup):
         X, rp, ids = batches[s]
         if s == 0:
-            evc[0].record(torch.cuda.current_stream())
+            evc[0].record(stream)
         elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
         if s == 0:
-            evc[1].record(torch.cuda.current_stream())
+            evc[1].record(stream)
     torch.cuda.synchronize()
-    first_ms = evc[0].elapsed_time(evc[1]) if args.warmup else None
+    first_ms = evc[0].elapsed_time(evc[1]) if warmup else None
 
     # the timed steps: whole-step throughput, with no event between the step's kernels
-    stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
-    for s in range(args.warmup, nb):
+    for s in range(warmup, nb):
         X, rp, ids = batches[s]
         elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    ms_step = total_ms / args.steps
+    ms_step = total_ms / steps
 
     # the same number of steps again with HIP events around every forward and backward launch (on
     # the step's stream) for the per-kernel averages; the events add a few microseconds between
     # the kernels they bracket, so this pass is timed separately and reported as such
     elmo.kernel_timing(True)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record(stream)
-    for i, s in enumerate(range(args.warmup, nb)):
+    for i, s in enumerate(range(warmup, nb)):
         X, rp, ids = batches[s]
         elmo.step(W, X, rp, ids, wl.lr, wl.seed, nb + s, wl.chunk, dX=dX, workspace=ws)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     elmo.kernel_timing(False)
     kt = elmo.kernel_timing_read()
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-    events_ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    events_ms_step = evs[0].elapsed_time(evs[-1]) / steps
     h = len(per_step) // 2
     events_median = per_step[h] if len(per_step) % 2 else 0.5 * (per_step[h - 1] + per_step[h])
     peak_hbm = torch.cuda.max_memory_allocated(dev)
     free_b, total_b = torch.cuda.mem_get_info(dev)   # hipMemGetInfo: the device's own view, for comparison
+    reserved = torch.cuda.memory_reserved(dev)
 
     B, D, L = wl.B, wl.D, wl.L
     flops = 6.0 * B * D * L
     fwd_peak = PEAK["fp8"] if wl.wfmt == wk.W_E4M3 else PEAK["bf16"]
-    t_ideal = 2.0 * B * D * L / fwd_peak + 4.0 * B * D * L / PEAK["bf16"]
+    t_mfma = 2.0 * B * D * L / fwd_peak + 4.0 * B * D * L / PEAK["bf16"]
     alg_bytes = 2.0 * L * D * wl.wbytes
-    samples_s = B * args.steps / (total_ms / 1e3)
+    t_hbm = alg_bytes / PEAK["hbm"]
+    samples_s = B * steps / (total_ms / 1e3)
 
-    # dominant kernel roofline from the live per-launch events
+    # per-kernel rooflines from the live per-launch events. Algorithmic work per label: forward
+    # 2 B D flops and D w bytes (W read); backward 4 B D flops and 2 D w bytes (W read and write).
+    # A kernel is MFMA- or HBM-bound by its arithmetic intensity against the ridge point.
     kern = {}
-    for name, per_label, peak in (("bwd", 4.0 * B * D, PEAK["bf16"]), ("fwd", 2.0 * B * D, fwd_peak)):
-        ms, n, labels = kt[name]
-        if n:
-            ach = labels * per_label / (ms / 1e3)
-            kern[name] = {"ms_total": ms, "launches": n, "avg_ms": ms / n, "achieved": ach, "peak": peak}
+    for kn, per_label_f, per_label_b, peak_f in (("bwd", 4.0 * B * D, 2.0 * D * wl.wbytes, PEAK["bf16"]),
+                                                  ("fwd", 2.0 * B * D, 1.0 * D * wl.wbytes, fwd_peak)):
+        ms, n, labels = kt[kn]
+        if not n:
+            continue
+        sec = ms / 1e3
+        hbm_bound = per_label_f / per_label_b < peak_f / PEAK["hbm"]
+        if hbm_bound:
+            ach, peak, unit = labels * per_label_b / sec, PEAK["hbm"], "GB/s"
+        else:
+            ach, peak, unit = labels * per_label_f / sec, peak_f, "TFLOP/s"
+        kern[kn] = {"ms_total": ms, "launches": n, "avg_ms": ms / n, "achieved": ach, "peak": peak, "unit": unit,
+                    "bound": "hbm" if hbm_bound else "mfma", "labels_per_launch": labels / n,
+                    "per_label": per_label_b if hbm_bound else per_label_f}
     dom = max(kern, key=lambda k: kern[k]["ms_total"])
     kd = kern[dom]
-    kname = "k_bwd_update" if dom == "bwd" else "k_fwd_g"
-    tr = measured_traffic(args.workload, kname)
-    roofline = {"kernel": kname, "bound": "mfma",
-                "achieved": round(kd["achieved"] / 1e12, 2), "peak": round(kd["peak"] / 1e12, 1),
-                "unit": "TFLOP/s", "frac": round(kd["achieved"] / kd["peak"], 4),
+    kname = {"bwd": "k_bwd_update", "fwd": "k_fwd_g"}
+    scale = 1e9 if kd["unit"] == "GB/s" else 1e12
+    tr = measured_traffic(name, kname[dom])
+    roofline = {"kernel": kname[dom], "bound": kd["bound"],
+                "achieved": round(kd["achieved"] / scale, 2), "peak": round(kd["peak"] / scale, 1),
+                "unit": kd["unit"], "frac": round(kd["achieved"] / kd["peak"], 4),
                 "traffic": None if tr is None else int(tr["bytes"]),
                 "traffic_read_write": None if tr is None else [int(tr["read"]), int(tr["write"])],
                 "avg_launch_ms": round(kd["avg_ms"], 4), "launches": kd["launches"],
+                "labels_per_launch": round(kd["labels_per_launch"], 1),
                 "events_pass_ms_per_step": round(events_ms_step, 4),
                 "events_pass_median_ms_per_step": round(events_median, 4),
-                "flops_per_label": (4 if dom == "bwd" else 2) * B * D}
-    other = [k for k in kern if k != dom]
-    if other:
-        ko = kern[other[0]]
-        roofline["other_kernel"] = {"kernel": "k_fwd_g" if other[0] == "fwd" else "k_bwd_update",
-                                    "achieved_tflops": round(ko["achieved"] / 1e12, 2),
-                                    "peak_tflops": round(ko["peak"] / 1e12, 1),
-                                    "frac": round(ko["achieved"] / ko["peak"], 4),
+                ("bytes_per_label" if kd["bound"] == "hbm" else "flops_per_label"): int(kd["per_label"])}
+    for other in [k for k in kern if k != dom]:
+        ko = kern[other]
+        so = 1e9 if ko["unit"] == "GB/s" else 1e12
+        roofline["other_kernel"] = {"kernel": kname[other], "bound": ko["bound"],
+                                    "achieved": round(ko["achieved"] / so, 2), "peak": round(ko["peak"] / so, 1),
+                                    "unit": ko["unit"], "frac": round(ko["achieved"] / ko["peak"], 4),
                                     "avg_launch_ms": round(ko["avg_ms"], 4)}
 
-    out = {"metric": METRIC, "value": round(samples_s, 1), "unit": "samples/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+    out = {"ms_per_step": round(ms_step, 4), "samples_s": round(samples_s, 1), "steps": steps, "warmup": warmup,
            "first_step_ms": None if first_ms is None else round(first_ms, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "e4m3+bf16" if wl.wfmt == wk.W_E4M3 else "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "B": B, "D": D, "L": L, "chunk": wl.chunk,
                       "weights": "e4m3" if wl.wfmt == wk.W_E4M3 else "bf16", "lr": wl.lr},
+           "dtype": "e4m3+bf16" if wl.wfmt == wk.W_E4M3 else "bf16",
            "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
-           "mfma_roofline_frac": round(t_ideal / (ms_step / 1e3), 4),
+           "mfma_roofline_frac": round(t_mfma / (ms_step / 1e3), 4),
            "alg_hbm_gbs": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
-           "hbm_frac": round(alg_bytes / (ms_step / 1e3) / PEAK["hbm"], 4),
+           "hbm_frac": round(t_hbm / (ms_step / 1e3), 4),
+           "roofline_bound": "mfma" if t_mfma >= t_hbm else "hbm",
+           "roofline_frac": round(max(t_mfma, t_hbm) / (ms_step / 1e3), 4),
            "peak_hbm_bytes": int(peak_hbm),
            "peak_hbm_breakdown": {k: int(v) for k, v in hbm_parts.items()},
-           "device_used_bytes": int(total_b - free_b),
+           "peak_hbm_budget_bytes": int(L * D * wl.wbytes + 2 * B * wl.chunk + 64 * 2**20),
+           "device_used_bytes": int(total_b - free_b), "torch_reserved_bytes": int(reserved),
            "weights_bytes": int(L * D * wl.wbytes),
            "roofline": roofline}
 
-    if not args.no_topk:
+    if with_topk:
         N, k = args.topk_n, (wl.topk or 5)
         Xe_host = wk.make_eval_x(wl, N)
         Xe = torch.from_numpy(Xe_host.view(np.int16)).to(dev)
@@ -347,14 +375,65 @@ def main():
         out["topk"] = {"N": N, "k": k, "ms": round(tk, 3), "samples_s": round(N / (tk / 1e3), 1),
                        "tflops": round(tf / (tk / 1e3) / 1e12, 2),
                        "frac": round(tf / (tk / 1e3) / fwd_peak, 4)}
-        if not args.no_cpu_baseline:
+        if with_cpu:
             out["topk"]["cpu_baseline"] = cpu_topk_baseline(wl, W, Xe_host, k, args.cpu_seconds / 3)
+        del Xe, tws
+
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, W, host_batches[0], args.cpu_seconds)
+
+    del W, ws, dX, batches
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: runs on exactly one GPU (--gpus 1); multi-GPU runs are not implemented",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_bytes:
+        copy_reference(args.copy_bytes)
+        return
+
+    import torch
+
+    import precision_label_chunk_amd as elmo
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    elmo.lib()
+
+    main_w = bench_workload(args.workload, args.steps, args.warmup, args, with_topk=not args.no_topk,
+                            with_cpu=not args.no_cpu_baseline)
+    out = {"metric": METRIC, "value": main_w["samples_s"], "unit": "samples/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_w["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": main_w["dtype"], "data": "synthetic", "config": main_w["config"]}
+    for key in ("first_step_ms", "tflops", "mfma_roofline_frac", "alg_hbm_gbs", "hbm_frac", "peak_hbm_bytes",
+                "peak_hbm_breakdown", "peak_hbm_budget_bytes", "device_used_bytes", "torch_reserved_bytes",
+                "weights_bytes", "roofline", "topk", "cpu_baseline"):
+        if key in main_w:
+            out[key] = main_w[key]
 
     if not args.no_kahan:
-        out["kahan_update"] = kahan_bench(args.kahan_params, stream)
+        out["kahan_update"] = kahan_bench(args.kahan_params, torch.cuda.current_stream())
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, W, host_batches[0], args.cpu_seconds)
+    # the second label space the method is measured on (default: 8.6M labels in BF16 with B = 128,
+    # bound by HBM), in an object of its own keyed by the workload's name
+    second = "none" if args.no_8p6m else args.second_workload
+    if second != "none":
+        out[second] = bench_workload(second, args.steps_8p6m, 2, args, with_topk=not args.no_topk,
+                                     with_cpu=not args.no_cpu_baseline)
+
+    info = cpu_info()
+    for obj in (out, out.get(second, {})):
+        for cb in (obj.get("cpu_baseline"), obj.get("topk", {}).get("cpu_baseline")):
+            if cb is not None:
+                cb.update(info)
 
     print(json.dumps(out), flush=True)
 

@@ -1,6 +1,7 @@
-"""The benchmark's output contract on a small workload: one JSON line with the metric, the
+"""The benchmark's output contract on small workloads: one JSON line with the metric, the
 whole-step throughput, the dominant kernel's roofline from live event timing, the top-k pass and
-the CPU oracle baselines (with their bounded samples)."""
+the CPU oracle baselines (with their bounded samples and the host CPU), and the second workload's
+object measured the same way."""
 import json
 import os
 import subprocess
@@ -14,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_bench_json_line_on_the_tiny_workload():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3", "--warmup", "1",
-           "--topk-n", "64", "--kahan-params", "100000", "--cpu-seconds", "0.3"]
+           "--topk-n", "64", "--kahan-params", "100000", "--cpu-seconds", "0.3", "--second-workload", "bf16_131k",
+           "--steps-8p6m", "2"]
     print("  " + " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -28,11 +30,18 @@ def test_bench_json_line_on_the_tiny_workload():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
     assert d["config"]["workload"] == "xmc-bf16-L4096-D64-B32"
     ro = d["roofline"]
-    assert ro["bound"] == "mfma" and ro["unit"] == "TFLOP/s" and ro["peak"] == 2500.0
+    # B = 32, D = 64: the backward's 4 B D flops per 2 D w bytes (32 flop/B) sit below the ridge point
+    assert ro["bound"] == "hbm" and ro["unit"] == "GB/s" and ro["peak"] == 8000.0
     assert ro["achieved"] > 0 and ro["frac"] == pytest.approx(ro["achieved"] / ro["peak"], rel=1e-2, abs=1e-4)
     assert ro["launches"] == 3 * 4                          # 4 chunks per step, one launch each
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["nproc"] >= 1 and "cpu_model" in cb
     tk = d["topk"]
     assert tk["N"] == 64 and tk["k"] == 5 and tk["ms"] > 0 and tk["cpu_baseline"]["value"] > 0
     assert d["kahan_update"]["params"] == 100000
+    s2 = d["bf16_131k"]
+    assert s2["config"]["workload"] == "xmc-bf16-L131072-D768-B256" and s2["samples_s"] > 0
+    # (B = 256, BF16: the backward moves 2 D w = 3,072 bytes per 786,432 flops, 256 flop/B: below the ridge)
+    assert s2["roofline"]["bound"] == "hbm" and s2["roofline"]["launches"] == 2 * 4
+    assert s2["cpu_baseline"]["value"] > 0 and s2["topk"]["ms"] > 0 and s2["peak_hbm_bytes"] > 0
