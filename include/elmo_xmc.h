@@ -37,7 +37,8 @@ typedef enum {
   ELMO_EDTYPE = -3,        /* unknown weight format                                      */
   ELMO_EWORKSPACE = -4,    /* workspace missing or smaller than the *_workspace_bytes   */
   ELMO_EHIP = -5,          /* a HIP runtime call or kernel launch failed                 */
-  ELMO_EUNSUPPORTED = -6   /* valid request that this library does not implement         */
+  ELMO_EUNSUPPORTED = -6,  /* valid request that this library does not implement         */
+  ELMO_ESCRATCH = -7       /* step too large for elmo_xmc_step_noalloc's static scratch  */
 } elmo_status;
 
 /* Weight storage formats. BF16: uint16 codes. E4M3: OCP FP8 E4M3FN codes (uint8; max 448, no
@@ -89,6 +90,24 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B,
                   const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr, uint64_t seed,
                   uint64_t step, int64_t chunk, float* dX, float* loss_sum, void* workspace,
                   size_t workspace_bytes, void* stream);
+/*
+ * The same step for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): arguments, results and errors as elmo_xmc_step,
+ * with the workspace replaced by a static device array of ELMO_NOALLOC_SCRATCH_BYTES bytes inside
+ * the library (one per GPU, held from the library's first use of that GPU until the process ends;
+ * its address is looked up on the first call on each device). No device memory is allocated or
+ * freed. A step whose workspace (elmo_xmc_step_workspace_bytes) exceeds that size returns
+ * ELMO_ESCRATCH and enqueues nothing: at B = 256, D = 768 that allows chunks of up to about
+ * 131,072 labels (3M-label E4M3 step: 97 MB); at B = 128, D = 768, chunks of 262,144 BF16 labels.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU (other streams or
+ * threads) race and give undefined results; serialise them. The flags word is not readable here.
+ */
+#define ELMO_NOALLOC_SCRATCH_BYTES (128u << 20)
+int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B,
+                          const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr,
+                          uint64_t seed, uint64_t step, int64_t chunk, float* dX, float* loss_sum,
+                          void* stream);
+
 /* Copies the flags word of a step's workspace to *flags (HOST pointer); synchronises `stream`. */
 int elmo_xmc_step_flags(const void* workspace, uint32_t* flags, void* stream);
 

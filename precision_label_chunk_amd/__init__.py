@@ -27,7 +27,8 @@ FLAG_LABEL_RANGE = 1
 FLAG_ROW_PTR = 2
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "unknown weight format",
-           -4: "workspace missing or too small", -5: "HIP runtime error", -6: "not supported"}
+           -4: "workspace missing or too small", -5: "HIP runtime error", -6: "not supported",
+           -7: "step too large for the allocation-free entry point's static scratch"}
 
 
 class ElmoError(RuntimeError):
@@ -57,6 +58,8 @@ def lib():
         L.elmo_xmc_step.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P, sz, P]
         L.elmo_xmc_step.restype = i32
         L.elmo_xmc_step_flags.argtypes = [P, P, P]; L.elmo_xmc_step_flags.restype = i32
+        L.elmo_xmc_step_noalloc.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P]
+        L.elmo_xmc_step_noalloc.restype = i32
         L.elmo_xmc_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32]
         L.elmo_xmc_topk_workspace_bytes.restype = sz
         L.elmo_xmc_topk.argtypes = [P, i32, i64, i32, P, i32, i32, P, P, P, sz, P]
@@ -126,6 +129,19 @@ def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, wo
     _chk("elmo_xmc_step", rc)
     global last_workspace
     last_workspace = workspace
+    return dX, loss
+
+
+def step_noalloc(W, X, row_ptr, ids, lr, seed, step, chunk, dX, loss=None):
+    """The same step through the allocation-free entry point (static scratch inside the library):
+    dX [B, D] float32 and the optional loss [1] float32 are caller-allocated outputs."""
+    _check_dev(W, X, row_ptr, ids, dX, loss)
+    L, D = W.shape
+    B = X.shape[0]
+    nnz = int(ids.numel())
+    rc = lib().elmo_xmc_step_noalloc(_ptr(W), wdtype_of(W), L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None,
+                                     nnz, float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss), _stream())
+    _chk("elmo_xmc_step_noalloc", rc)
     return dX, loss
 
 

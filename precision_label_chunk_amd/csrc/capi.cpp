@@ -35,6 +35,7 @@ const char* elmo_status_str(int status) {
     case ELMO_EWORKSPACE: return "workspace missing or too small";
     case ELMO_EHIP: return "HIP runtime error";
     case ELMO_EUNSUPPORTED: return "not supported by this library";
+    case ELMO_ESCRATCH: return "step needs more scratch than the allocation-free entry point's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -62,6 +63,26 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B, c
   a.row_ptr = row_ptr; a.ids = ids; a.nnz = nnz; a.lr = lr; a.seed = seed; a.step = step;
   a.dX = dX; a.loss = loss_sum; a.l0 = 0; a.l1 = L; a.Z = nullptr;
   return elmo::run_step(a, s, workspace, (hipStream_t)stream);
+}
+
+int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
+                          const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
+                          float* dX, float* loss_sum, void* stream) {
+  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return ELMO_EDTYPE;
+  int rc = check_shapes(B, D, L);
+  if (rc != ELMO_OK) return rc;
+  if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
+  if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
+  const elmo::StepLayout s = elmo::step_layout(B, D, L, chunk, wdtype, nnz);
+  if (s.total > (size_t)ELMO_NOALLOC_SCRATCH_BYTES) return ELMO_ESCRATCH;
+  void* ws = nullptr;
+  if ((rc = elmo::noalloc_scratch(&ws)) != ELMO_OK) return rc;
+  elmo::StepArgs a{};
+  a.W = W; a.wdtype = wdtype; a.L = L; a.D = D; a.X = X; a.B = B;
+  a.row_ptr = row_ptr; a.ids = ids; a.nnz = nnz; a.lr = lr; a.seed = seed; a.step = step;
+  a.dX = dX; a.loss = loss_sum; a.l0 = 0; a.l1 = L; a.Z = nullptr;
+  return elmo::run_step(a, s, ws, (hipStream_t)stream);
 }
 
 int elmo_xmc_step_flags(const void* workspace, uint32_t* flags, void* stream) {

@@ -8,7 +8,7 @@ namespace elmo {
 
 // status and format codes (mirror include/elmo_xmc.h)
 constexpr int ELMO_OK_ = 0, ELMO_EINVAL_ = -1, ELMO_ESHAPE_ = -2, ELMO_EDTYPE_ = -3, ELMO_EWORKSPACE_ = -4,
-              ELMO_EHIP_ = -5, ELMO_EUNSUPPORTED_ = -6;
+              ELMO_EHIP_ = -5, ELMO_EUNSUPPORTED_ = -6, ELMO_ESCRATCH_ = -7;
 constexpr int W_BF16_ = 0, W_E4M3_ = 1;
 constexpr uint32_t ELMO_FLAG_LABEL_RANGE_ = 1u, ELMO_FLAG_ROW_PTR_ = 2u;
 
@@ -66,6 +66,10 @@ int run_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, 
 
 // Kahan-compensated BF16 update of encoder parameters (elementwise)
 int run_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float lr, hipStream_t st);
+
+// this device's copy of the static scratch array of the allocation-free step (noalloc.hip): its
+// device address, looked up on the first call on the current device
+int noalloc_scratch(void** out);
 
 // elementwise numerics hook
 int run_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
