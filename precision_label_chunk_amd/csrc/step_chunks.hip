@@ -195,6 +195,197 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
 }
 
 // ------------------------------------------------------------------------------------------------
+// forward + gradient with the features stationary in registers (E4M3 weights, 256 samples, D = 768)
+// ------------------------------------------------------------------------------------------------
+// The tiled forward above reloads every feature row for every 128-label tile and waits on those
+// loads in each K slice. Here each work-group holds all 256 E4M3 feature rows in registers for the
+// whole launch (wave w: samples 32 w .. 32 w + 31, lane (l32, hi) the MFMA A fragments of row
+// 32 w + l32, 32 bytes per 64-byte K step: D / 8 registers) and streams the chunk's weights through
+// LDS in 64-label tiles, three tile buffers deep: tile t's rows are loaded (into registers) at the
+// start of iteration t - 2 and written to LDS at its end, a whole iteration ahead of their use. One
+// work-group per CU takes tiles blockIdx.x, + gridDim.x, ...
+// The waves come in two groups of four, one wave of each per SIMD, in complementary phases: in
+// iteration i group A (waves 0-3) runs tile i's MFMAs and then its gradient epilogue, group B (4-7)
+// runs the epilogue of tile i - 1 and then tile i's MFMAs, so that on every SIMD one wave's matrix
+// work overlaps the other's epilogue arithmetic. One barrier per iteration. The positives of tile
+// i + 1 are gathered into label bits during iteration i (four buffers: A reads tile i's, B tile
+// i - 1's, i + 1's is being filled and i + 2's cleared).
+constexpr int XS_TJ = 64;                                      // labels per tile
+
+// NK: 64-byte K steps of the FP8 MFMA (D = 64 NK; the features take 8 NK registers)
+template <int NK, bool LOSS, bool ZOUT>
+__global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq,
+                                                int D, int64_t c0, int clen,
+                                                const uint32_t* __restrict__ tile_off,
+                                                const uint32_t* __restrict__ bucket, int64_t bucket_cap,
+                                                int B, uint16_t* __restrict__ G, int64_t gpitch,
+                                                float* __restrict__ loss_part,
+                                                float* __restrict__ Z, uint16_t* __restrict__ Gout,
+                                                int64_t zpitch, int64_t zoff) {
+  constexpr int MB = 256;
+  constexpr int D_ = 64 * NK;
+  constexpr int PITCH = D_ + 16;                      // LDS row pitch: 16 consecutive rows on distinct banks
+  constexpr int PPR = D_ / 16;                        // 16-byte parts per weight row
+  constexpr int CPT = (XS_TJ * PPR + 511) / 512;      // 16-byte weight chunks per thread and tile
+  __shared__ __attribute__((aligned(16))) uint8_t Ws[3][XS_TJ * PITCH];
+  __shared__ uint32_t ybits[4][XS_TJ * (MB / 32)];   // label-major: bit b & 31 of word [j][b >> 5]
+  __shared__ float lred[8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                          // 0: MFMAs then epilogue; 1: epilogue then MFMAs
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int bb = 32 * wave;                           // the wave's first sample
+  const int ntl = (clen + XS_TJ - 1) / XS_TJ;         // tiles of the chunk
+  const int nmy = ntl > (int)blockIdx.x ? (ntl - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  auto tile_of = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
+  (void)D;
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)D_, clen * D_);
+  constexpr int OOB = 0x7ffffff0;
+
+  // weight tile staging through registers: chunk c of this thread is ci = tid + 512 c, row ci / PPR,
+  // part ci % PPR; rows past the chunk read as zero (resource bound), chunks past the tile are idle
+  i32x4_t stg[CPT];
+  auto wload = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + 512 * c, row = ci / PPR, part = ci % PPR;
+      const bool in = row < XS_TJ;
+      stg[c] = buffer_load16(wres, in ? (t * XS_TJ + row) * D_ + part * 16 : OOB);
+    }
+  };
+  auto wstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + 512 * c, row = ci / PPR, part = ci % PPR;
+      if (row < XS_TJ) *(i32x4_t*)(&Ws[buf][row * PITCH + part * 16]) = stg[c];
+    }
+  };
+  // positives of tile t (64 labels: half (c0 / 64 + t) & 1 of 128-label bucket tile (c0 / 64 + t) >> 1)
+  auto yclear = [&](int buf) {
+    for (int i = tid; i < XS_TJ * (MB / 32); i += 512) ybits[buf][i] = 0u;
+  };
+  auto yscan = [&](int t, int buf) {
+    const int64_t g64 = c0 / XS_TJ + t;
+    const int64_t tb = g64 >> 1;
+    const uint32_t half = (uint32_t)(g64 & 1);
+    const uint64_t e0 = tile_off[tb];
+    const uint64_t e1 = tile_off[tb + 1] < (uint64_t)bucket_cap ? tile_off[tb + 1] : (uint64_t)bucket_cap;
+    for (uint64_t e = e0 + tid; e < e1; e += 512) {
+      const uint32_t v = bucket[e];
+      const uint32_t b = v >> 16, jl = v & (TJ1 - 1);
+      if (b < (uint32_t)MB && (jl >> 6) == half)
+        atomicOr(&ybits[buf][(jl & (XS_TJ - 1)) * (MB / 32) + (b >> 5)], 1u << (b & 31));
+    }
+  };
+
+  // prologue: tiles 0 and 1 into LDS, tile 0's positives, the stationary feature fragments
+  if (nmy > 0) { wload(tile_of(0)); wstore(0); }
+  if (nmy > 1) { wload(tile_of(1)); wstore(1); }
+  yclear(0); yclear(1); yclear(2);
+  __syncthreads();
+  if (nmy > 0) yscan(tile_of(0), 0);
+  i32x8_t xf[NK];
+  {
+    const uint8_t* xr = Xq + (int64_t)(bb + l32) * D_ + hi * 32;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const i32x4_t a0 = *(const i32x4_t*)(xr + kk * 64), a1 = *(const i32x4_t*)(xr + kk * 64 + 16);
+      xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+  }
+  __syncthreads();
+
+  f32x16_t acc[2];
+  float lsum = 0.0f;
+  // the tile's 2 NK MFMAs (slot z: K step z / 2, label block z % 2), each slot's weight fragment read
+  // from LDS two slots ahead; a scheduling fence closes every slot so that the reads stay spread
+  auto mfmas = [&](int buf) {
+    acc[0] = f32x16_t{}; acc[1] = f32x16_t{};
+    const uint8_t* wb = &Ws[buf][l32 * PITCH + hi * 32];
+    auto rd = [&](int z) {
+      const uint8_t* p = wb + (z & 1) * 32 * PITCH + (z >> 1) * 64;
+      const i32x4_t b0 = *(const i32x4_t*)p, b1 = *(const i32x4_t*)(p + 16);
+      return i32x8_t{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    };
+    constexpr int NS = 2 * NK;
+    i32x8_t f[3];
+    f[0] = rd(0); f[1] = rd(1);
+    static_for<0, NS>([&](auto Z) {
+      constexpr int z = decltype(Z)::value;
+      if constexpr (z + 2 < NS) f[(z + 2) % 3] = rd(z + 2);
+      acc[z & 1] = mfma_e4m3(xf[z >> 1], f[z % 3], acc[z & 1]);
+      sched_fence();
+    });
+  };
+  auto epilogue = [&](int t, int buf) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int jl = ni * 32 + l32;
+      const int jc = t * XS_TJ + jl;                  // label within the chunk
+      const bool jvalid = jc < clen;
+      const uint32_t yw = ybits[buf][jl * (MB / 32) + wave];
+      float gv[16];
+      fwd_grad_block(acc[ni], yw, jvalid, bb, B, hi, gv);
+      if constexpr (LOSS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int bl = 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (jvalid && (bb + bl < B)) lsum += bce_loss(acc[ni][i], (yw >> bl) & 1u);
+        }
+      }
+      if constexpr (ZOUT) {
+        // (diagnostic) element (sample bb + bl, label c0 + jc) at row-major [B][zpitch] offset
+        // (bb + bl) zpitch + c0 + jc - zoff, from one base per lane and row steps of zpitch
+        const int64_t lab = c0 + jc;
+        const bool lok = jvalid && lab >= zoff;
+        const int64_t base = (int64_t)(bb + 4 * hi) * zpitch + (lab - zoff);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + (i & 3);
+          if (lok && bb + 4 * hi + r < B) {
+            const int64_t o = base + r * zpitch;
+            if (Z) Z[o] = acc[ni][i];
+            if (Gout) Gout[o] = (uint16_t)f32_to_bf16_rne(gv[i]);
+          }
+        }
+      }
+      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)jc * gpitch, bb, hi);
+    }
+  };
+
+  // (the diagnostic variant, whose stores take more registers, writes the weight tile to LDS right
+  // after loading it: the same arithmetic, without the loads in flight across the iteration)
+  constexpr bool LATE_STORE = !ZOUT;
+  for (int i = 0; i <= nmy; ++i) {
+    if (i + 2 < nmy) {
+      wload(tile_of(i + 2));
+      if constexpr (!LATE_STORE) wstore((i + 2) % 3);
+    }
+    // group A: MFMAs of tile i, then its epilogue; group B: epilogue of tile i - 1, then MFMAs of tile i
+    const int ie = i - grp;                           // the tile index whose epilogue this wave runs
+    if (grp == 0 && i < nmy) mfmas(i % 3);
+    if (ie >= 0 && ie < nmy) epilogue(tile_of(ie), ie & 3);
+    if (grp == 1 && i < nmy) mfmas(i % 3);
+    if constexpr (LATE_STORE) if (i + 2 < nmy) wstore((i + 2) % 3);
+    if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
+    yclear((i + 2) & 3);
+    __syncthreads();
+  }
+
+  if constexpr (LOSS) {
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) lred[wave] = lsum;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.0f;
+      for (int w = 0; w < 8; ++w) s += lred[w];
+      loss_part[c0 / XS_TJ + blockIdx.x] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // backward + fused update over one d-slice and one label range of the chunk
 // ------------------------------------------------------------------------------------------------
 // LDS tiles keep rows of CPR 16-byte chunks; chunk c of row j sits at slot c ^ row_swz<CPR>(j).
@@ -660,22 +851,35 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
   float* part = (float*)(ws + s.part);
   float* lpart = (float*)(ws + s.loss);
   const int64_t l_end = a.l1;
+  // the forward with the features stationary in registers where it is built (E4M3, 256 padded
+  // samples, D = 768); the tiled forward elsewhere
+  constexpr bool XS_OK = MB == 256 && WF == W_E4M3_;
+  const bool xs = XS_OK && a.D == 768;
   for (int64_t c0 = a.l0; c0 < l_end; c0 += s.Cc) {
     const int clen = (int)((l_end - c0) < s.Cc ? (l_end - c0) : s.Cc);
     const int nt1 = (clen + TJ1 - 1) / TJ1;
+    const int ntx = (clen + XS_TJ - 1) / XS_TJ;
+    const int gx = ntx < s.cus ? ntx : s.cus;
+    auto forward = [&](auto LOSS, auto ZOUT, float* Z, uint16_t* Gout, int64_t zpitch, int64_t zoff) {
+      constexpr bool L_ = decltype(LOSS)::value, Z_ = decltype(ZOUT)::value;
+      if constexpr (XS_OK) {
+        if (xs) {
+          hipLaunchKernelGGL((k_fwd_xs<12, L_, Z_>), dim3(gx), dim3(512), 0, st, W, ws + s.xq, a.D, c0, clen, toff,
+                             bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+          return;
+        }
+      }
+      hipLaunchKernelGGL((k_fwd_g<MB, WF, L_, Z_>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen, toff, bucket,
+                         a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+    };
     if (a.forward_only()) {
-      hipLaunchKernelGGL((k_fwd_g<MB, WF, false, true>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, a.Z, a.Gout, a.zpitch, a.zoff);
+      forward(std::false_type{}, std::true_type{}, a.Z, a.Gout, a.zpitch, a.zoff);
       LAUNCH_CHECK();
       continue;
     }
     kt_begin(KT_FWD, st, clen);
-    if (a.loss)
-      hipLaunchKernelGGL((k_fwd_g<MB, WF, true, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
-    else
-      hipLaunchKernelGGL((k_fwd_g<MB, WF, false, false>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen,
-                         toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+    if (a.loss) forward(std::true_type{}, std::false_type{}, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
+    else forward(std::false_type{}, std::false_type{}, (float*)nullptr, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
     LAUNCH_CHECK();
     kt_end(KT_FWD, st);
     const int nt2 = (clen + TJ2 - 1) / TJ2;

@@ -314,7 +314,7 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   s.xbt = off;      off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
   s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
-  s.loss = off;     off = align_up(off + 4 * (size_t)s.ntiles, A);
+  s.loss = off;     off = align_up(off + 4 * (size_t)(2 * s.ntiles + 2), A);
   s.total = off;
   return s;
 }
@@ -331,6 +331,12 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags, (int64_t)16, 0u);
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, cnt, s.ntiles + 1, 0u);
   LAUNCH_CHECK();
+  if (a.loss) {
+    // loss partials: one slot per 128-label tile (tiled forward) or per work-group and 64 labels
+    // (stationary-feature forward); the slots a launch does not write stay zero
+    hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, (uint32_t*)(ws + s.loss), 2 * s.ntiles + 2, 0u);
+    LAUNCH_CHECK();
+  }
   if (!a.forward_only()) {
     // the first chunk stores all partial slots unless it has fewer label ranges than there are slots
     const int64_t clen0 = (a.l1 - a.l0) < s.Cc ? (a.l1 - a.l0) : s.Cc;
@@ -379,7 +385,7 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     LAUNCH_CHECK();
   }
   if (a.loss) {
-    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, st, (const float*)(ws + s.loss), s.ntiles, a.loss);
+    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, st, (const float*)(ws + s.loss), 2 * s.ntiles + 2, a.loss);
     LAUNCH_CHECK();
   }
   return ELMO_OK_;

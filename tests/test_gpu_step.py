@@ -44,6 +44,11 @@ CASES = [  # B, D, L, chunk, wfmt
     (256, 768, 3000, 1024, wk.W_E4M3),     # full batch and width
     (256, 768, 2100, 1024, wk.W_BF16),
     (64, 1024, 700, 384, wk.W_BF16),       # largest D
+    # E4M3 with 129..256 samples and D = 768: the forward with the features held in registers
+    (200, 768, 1000, 1000, wk.W_E4M3),     # chunk rounded down to 896, ragged second chunk
+    (129, 768, 70, 128, wk.W_E4M3),        # one chunk of two 64-label tiles, the second ragged
+    (256, 768, 5000, 65536, wk.W_E4M3),    # chunk larger than L
+    (160, 768, 1337, 128, wk.W_E4M3),      # eleven chunks of one 128-label tile each
 ]
 
 
@@ -93,17 +98,20 @@ def test_step_matches_oracle(elmo, orc, B, D, L, chunk, wfmt):
     check_step(elmo, orc, W0, bt, wfmt, lr, seed, step, Wg, dXg, lossg)
 
 
-def test_logits_subrange(elmo, orc):
-    wl, W0, bt = _case(20, 128, 1000, wk.W_BF16)
-    js = np.arange(333, 901)
-    Zg = elmo.logits(to_dev_codes(W0), batch_to_dev(bt)[0], 333, 901).cpu().numpy()
-    Zr = orc.logits(wk.W_BF16, W0, bt.X, js)
-    assert_close(Zg, Zr, 1e-2)
+@pytest.mark.parametrize("B,D,wfmt", [(20, 128, wk.W_BF16), (200, 768, wk.W_E4M3)])
+def test_logits_subrange(elmo, orc, B, D, wfmt):
+    wl, W0, bt = _case(B, D, 1000, wfmt)
+    Wd, Xd = to_dev_codes(W0), batch_to_dev(bt)[0]
+    for l0, l1 in [(333, 901), (0, 1), (999, 1000), (130, 131), (0, 1000)]:
+        js = np.arange(l0, l1)
+        Zg = elmo.logits(Wd, Xd, l0, l1).cpu().numpy()
+        Zr = orc.logits(wfmt, W0, bt.X, js)
+        assert_close(Zg, Zr, RTOL[wfmt])
 
 
-@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
-def test_chunk_size_invariance(elmo, wfmt):
-    wl, W0, bt = _case(48, 128, 2000, wfmt)
+@pytest.mark.parametrize("B,D,wfmt", [(48, 128, wk.W_BF16), (48, 128, wk.W_E4M3), (256, 768, wk.W_E4M3)])
+def test_chunk_size_invariance(elmo, B, D, wfmt):
+    wl, W0, bt = _case(B, D, 2000, wfmt)
     outs = [_run(elmo, W0, bt, wfmt, 0.1, 5, 1, c) for c in (128, 1000, 2000, 1 << 20)]
     for Wg, dXg, _ in outs[1:]:
         assert np.array_equal(Wg, outs[0][0])               # weights: bit-identical
