@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "libelmo_oracle.so")
 
 W_BF16 = 0
 W_E4M3 = 1
+W_MXFP4 = 2
 
 
 def build(force: bool = True) -> str:
@@ -75,6 +76,12 @@ def lib():
                                   ctypes.c_int, P, ctypes.c_int]
         L.orc_grad_exact.argtypes = [i64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P]
         L.orc_kahan_update.argtypes = [i64, P, P, P, ctypes.c_float]; L.orc_kahan_update.restype = None
+        L.orc_e2m1_value.argtypes = [u8]; L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [u8]; L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_sr_e2m1.argtypes = [ctypes.c_double, u32]; L.orc_sr_e2m1.restype = u8
+        L.orc_mx_block_exponent.argtypes = [ctypes.c_float]; L.orc_mx_block_exponent.restype = ctypes.c_int
+        L.orc_mx_quantize_block.argtypes = [P, P, P, P]; L.orc_mx_quantize_block.restype = None
+        L.orc_mx_row_bytes.argtypes = [ctypes.c_int]; L.orc_mx_row_bytes.restype = i64
         L.orc_topk.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                P, P, ctypes.c_int]
         for name in ("orc_step", "orc_update_from_g", "orc_logits", "orc_update_rows", "orc_update_rows_from_g",
@@ -100,6 +107,20 @@ def _c(a, dtype):
 
 def wdtype_np(wfmt):
     return np.uint16 if wfmt == W_BF16 else np.uint8
+
+
+def dims(wfmt, W):
+    """(L, D) of a weight array: [L][D] codes, or for MXFP4 [L][D/2 + D/32] bytes per row."""
+    L, c = W.shape
+    if wfmt == W_MXFP4:
+        assert (c * 32) % 17 == 0, "MXFP4 rows hold D/2 + D/32 bytes"
+        return L, c * 32 // 17
+    return L, c
+
+
+def row_units(wfmt, D):
+    """array columns of one weight row: D codes, or D/2 + D/32 bytes for MXFP4"""
+    return D // 2 + D // 32 if wfmt == W_MXFP4 else D
 
 
 # ---- scalar / elementwise codecs ---------------------------------------------------------------
@@ -149,13 +170,58 @@ def grad_code(z, y):
     return lib().orc_grad_code(float(z), int(y))
 
 
+def e2m1_value(codes):
+    if np.ndim(codes) == 0:
+        return lib().orc_e2m1_value(int(codes))
+    c = _c(codes, np.uint8)
+    return np.array([lib().orc_e2m1_value(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e8m0_value(codes):
+    if np.ndim(codes) == 0:
+        return lib().orc_e8m0_value(int(codes))
+    c = _c(codes, np.uint8)
+    return np.array([lib().orc_e8m0_value(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def sr_e2m1(v, r):
+    v = np.asarray(v, np.float64); r = np.broadcast_to(np.asarray(r, np.uint32), v.shape)
+    return np.array([lib().orc_sr_e2m1(float(a), int(b)) for a, b in zip(v.ravel(), r.ravel())],
+                    np.uint8).reshape(v.shape)
+
+
+def mx_block_exponent(amax):
+    return int(lib().orc_mx_block_exponent(float(amax)))
+
+
+def mx_quantize_block(t, r):
+    """32 FP32 values and their 16-bit draws -> (32 element codes, scale code)"""
+    t = _c(np.asarray(t, np.float32).ravel(), np.float32); r = _c(np.asarray(r, np.uint32).ravel(), np.uint32)
+    assert t.size == 32 and r.size == 32
+    codes = np.empty(32, np.uint8); scale = np.empty(1, np.uint8)
+    lib().orc_mx_quantize_block(_p(t), _p(r), _p(codes), _p(scale))
+    return codes, int(scale[0])
+
+
+def mx_decode(W, D=None):
+    """binary64 values [L][D] of MXFP4 rows W [L][D/2 + D/32] (the oracle's element and scale decoders)"""
+    W = _c(W, np.uint8)
+    L, D = dims(W_MXFP4, W)
+    e = _value_lut(W_MXFP4)
+    sc = _scale_lut()
+    codes = np.empty((L, D), np.uint8)
+    codes[:, 0::2] = W[:, :D // 2] & 15
+    codes[:, 1::2] = W[:, :D // 2] >> 4
+    return e[codes] * np.repeat(sc[W[:, D // 2:]], 32, axis=1)
+
+
 # ---- the step ----------------------------------------------------------------------------------
 
 def step(wfmt, W, X, row_ptr, ids, lr, seed, step_, want_z=False, want_g=False, want_loss=False,
          nthreads=0):
     """Returns (W_new, dX, loss|None, Z|None, G|None); W is not modified."""
     Wn = np.array(W, dtype=wdtype_np(wfmt), order="C", copy=True)
-    L, D = Wn.shape
+    L, D = dims(wfmt, Wn)
     X = _c(X, np.uint16); B = X.shape[0]
     rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32)
     dX = np.empty((B, D), np.float32)
@@ -173,7 +239,7 @@ def step(wfmt, W, X, row_ptr, ids, lr, seed, step_, want_z=False, want_g=False, 
 def update_from_g(wfmt, W, X, G, lr, seed, step_, nthreads=0, want_t=False):
     """Updated codes given gradient codes G [B][L]; with want_t also the FP32 values t [L][D] that
     were stochastically rounded: returns W_new or (W_new, T)."""
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); B = X.shape[0]
     G = _c(G, np.uint16)
     assert G.shape == (B, L)
     out = np.empty_like(W)
@@ -184,7 +250,7 @@ def update_from_g(wfmt, W, X, G, lr, seed, step_, nthreads=0, want_t=False):
 
 
 def logits(wfmt, W, X, js, nthreads=0):
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); B = X.shape[0]
     js = _c(js, np.int64); Z = np.empty((B, js.size), np.float32)
     _chk(lib().orc_logits(wfmt, _p(W), L, D, _p(X), B, _p(js), js.size, _p(Z), nthreads), "logits")
     return Z
@@ -193,9 +259,9 @@ def logits(wfmt, W, X, js, nthreads=0):
 def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0, want_detail=False):
     """Updated codes of weight rows js [nj][D]; with want_detail also their gradient codes G [B][nj]
     and the FP32 values t [nj][D] before rounding: returns Wrows or (Wrows, G, T)."""
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); B = X.shape[0]
     rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32); js = _c(js, np.int64)
-    out = np.empty((js.size, D), wdtype_np(wfmt))
+    out = np.empty((js.size, row_units(wfmt, D)), wdtype_np(wfmt))
     G = np.empty((B, js.size), np.uint16) if want_detail else None
     T = np.empty((js.size, D), np.float32) if want_detail else None
     _chk(lib().orc_update_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
@@ -206,17 +272,17 @@ def update_rows(wfmt, W, X, row_ptr, ids, lr, seed, step_, js, nthreads=0, want_
 
 def update_rows_from_g(wfmt, W, X, G, lr, seed, step_, js, nthreads=0):
     """Updated codes of weight rows js given the gradient codes G [B][len(js)] of those labels."""
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); B = X.shape[0]
     js = _c(js, np.int64); G = _c(G, np.uint16)
     assert G.shape == (B, js.size)
-    out = np.empty((js.size, D), wdtype_np(wfmt))
+    out = np.empty((js.size, row_units(wfmt, D)), wdtype_np(wfmt))
     _chk(lib().orc_update_rows_from_g(wfmt, _p(W), L, D, _p(X), B, _p(G), float(lr), seed, step_, _p(js), js.size,
                                       _p(out), nthreads), "update_rows_from_g")
     return out
 
 
 def dx_rows(wfmt, W, X, row_ptr, ids, bs, nthreads=0):
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); B = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); B = X.shape[0]
     rp = _c(row_ptr, np.int32); ids = _c(ids, np.int32); bs = _c(bs, np.int32)
     out = np.empty((bs.size, D), np.float32)
     _chk(lib().orc_dx_rows(wfmt, _p(W), L, D, _p(X), B, _p(rp), _p(ids) if ids.size else None,
@@ -240,20 +306,29 @@ _LUT = {}
 
 
 def _value_lut(wfmt):
-    """Decoded value of every code, from the oracle's own decoders (65,536 BF16 or 256 E4M3 codes)."""
+    """Decoded value of every code, from the oracle's own decoders (65,536 BF16, 256 E4M3 or 16 E2M1
+    codes)."""
     if wfmt not in _LUT:
         if wfmt == W_BF16:
             _LUT[wfmt] = bf16_value(np.arange(65536, dtype=np.uint16))
-        else:
+        elif wfmt == W_E4M3:
             _LUT[wfmt] = e4m3_value(np.arange(256, dtype=np.uint8))
+        else:
+            _LUT[wfmt] = e2m1_value(np.arange(16, dtype=np.uint8))
     return _LUT[wfmt]
+
+
+def _scale_lut():
+    if "e8m0" not in _LUT:
+        _LUT["e8m0"] = e8m0_value(np.arange(256, dtype=np.uint8))
+    return _LUT["e8m0"]
 
 
 def forward_x_values(wfmt, X):
     """The forward operand of queries X (BF16 codes) as binary64 values: X itself for BF16 weights,
     E4M3-RNE(X) for E4M3 weights (the training forward's cast)."""
     xv = _value_lut(W_BF16)[_c(X, np.uint16)]
-    if wfmt == W_E4M3:
+    if wfmt in (W_E4M3, W_MXFP4):
         xv = _value_lut(W_E4M3)[e4m3_rne_sat(xv)]
     return xv
 
@@ -268,11 +343,11 @@ def logits_dense(wfmt, W, X, block=1 << 16):
     W = np.ascontiguousarray(W)
     L = W.shape[0]
     xv = forward_x_values(wfmt, X)
-    lut = _value_lut(wfmt)
     Z = np.empty((xv.shape[0], L), np.float32)
     for j0 in range(0, L, block):
         j1 = min(L, j0 + block)
-        Z[:, j0:j1] = (xv @ lut[W[j0:j1]].T).astype(np.float32)
+        wv = mx_decode(W[j0:j1]) if wfmt == W_MXFP4 else _value_lut(wfmt)[W[j0:j1]]
+        Z[:, j0:j1] = (xv @ wv.T).astype(np.float32)
     return Z
 
 
@@ -297,7 +372,7 @@ def rank_scores(Z, k):
 
 
 def topk(wfmt, W, X, k, nthreads=0):
-    W = _c(W, wdtype_np(wfmt)); L, D = W.shape; X = _c(X, np.uint16); N = X.shape[0]
+    W = _c(W, wdtype_np(wfmt)); L, D = dims(wfmt, W); X = _c(X, np.uint16); N = X.shape[0]
     idx = np.empty((N, k), np.int32); score = np.empty((N, k), np.float32)
     _chk(lib().orc_topk(wfmt, _p(W), L, D, _p(X), N, k, _p(idx), _p(score), nthreads), "topk")
     return idx, score

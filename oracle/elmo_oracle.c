@@ -124,6 +124,62 @@ uint8_t orc_sr_e4m3(float t, uint32_t r) {
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * MX-scaled FP4 (OCP Microscaling formats): blocks of 32 E2M1 elements sharing one E8M0 scale.
+ * E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal (m x 0.5); no
+ * infinity or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. E8M0: the power of two 2^(c - 127),
+ * c = 255 is NaN. The pages name FP4 weights as the recipe gap that needs micro-tensor scaling
+ * (summary page, Limitations); the scaling rule and the rounding of the elements are the reading
+ * documented with the build: the block's shared exponent is floor(log2(max |t|)) minus the element
+ * format's largest exponent (2), clamped to the scale's range; each element t / 2^X is rounded to
+ * E2M1 stochastically with the rule of orc_sr_bf16 (16 random bits), saturating at 6.
+ * ---------------------------------------------------------------------------------------------- */
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(uint8_t code) {
+  double v = e2m1_mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+double orc_e8m0_value(uint8_t code) { return code == 255 ? NAN : ldexp(1.0, (int)code - 127); }
+
+uint8_t orc_sr_e2m1(double v, uint32_t r) {
+  uint8_t s = signbit(v) ? 8 : 0;
+  double a = fabs(v);
+  if (a >= 6.0) return (uint8_t)(s | 7);
+  int c = 0;
+  while (c < 7 && e2m1_mag[c + 1] <= a) c++;        /* largest magnitude <= a */
+  if (e2m1_mag[c] == a) return (uint8_t)(s | c);
+  double u = e2m1_mag[c + 1] - e2m1_mag[c];
+  double q = floor((a - e2m1_mag[c]) / u * 65536.0);
+  return (uint8_t)(s | (((uint32_t)q + (r & 0xFFFFu) >= 65536u) ? c + 1 : c));
+}
+
+int orc_mx_block_exponent(float amax) {
+  if (isnan(amax)) return 128;                       /* marks a NaN block (scale code 255) */
+  if (amax == 0.0f) return -127;
+  if (isinf(amax)) return 127;
+  int x = ilogb((double)amax) - 2;                   /* floor(log2 amax) - (largest E2M1 exponent) */
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+void orc_mx_quantize_block(const float* t, const uint32_t* r, uint8_t* codes, uint8_t* scale) {
+  float amax = 0.0f;
+  int nan = 0;
+  for (int k = 0; k < 32; k++) {
+    if (isnan(t[k])) nan = 1;
+    else if (fabsf(t[k]) > amax) amax = fabsf(t[k]);
+  }
+  int x = nan ? 128 : orc_mx_block_exponent(amax);
+  if (x == 128) {
+    *scale = 255;
+    for (int k = 0; k < 32; k++) codes[k] = 0;
+    return;
+  }
+  *scale = (uint8_t)(x + 127);
+  for (int k = 0; k < 32; k++) codes[k] = orc_sr_e2m1(ldexp((double)t[k], -x), r[k]);
+}
+
+/* ------------------------------------------------------------------------------------------------
  * Philox4x32 as defined in "Parallel Random Numbers: As Easy as 1, 2, 3" (Salmon et al., SC'11):
  * each round multiplies counter words 0 and 2 by two fixed 32-bit constants, and the new counter
  * is (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)); the key is advanced by the
@@ -207,10 +263,42 @@ static void set_threads(int nthreads) {
 }
 
 /* decoded value of weight element (j, k) */
+/* MXFP4 rows: D / 2 bytes of E2M1 codes (element 2i in the low nibble of byte i, 2i + 1 in the high
+ * nibble), then D / 32 E8M0 scale bytes (block b = elements 32b .. 32b + 31) */
+int64_t orc_mx_row_bytes(int D) { return (int64_t)D / 2 + D / 32; }
+
 static double wval(int wfmt, const void* W, int64_t j, int D, int k) {
+  if (wfmt == ORC_W_MXFP4) {
+    const uint8_t* row = (const uint8_t*)W + j * orc_mx_row_bytes(D);
+    uint8_t byte = row[k / 2];
+    return orc_e2m1_value((uint8_t)((k & 1) ? byte >> 4 : byte & 15)) * orc_e8m0_value(row[D / 2 + k / 32]);
+  }
   int64_t i = j * (int64_t)D + k;
   return wfmt == ORC_W_BF16 ? orc_bf16_value(((const uint16_t*)W)[i])
                             : orc_e4m3_value(((const uint8_t*)W)[i]);
+}
+
+/* the updated codes of weight row j from its FP32 values t[0..D): per element for BF16 and E4M3;
+ * per 32-element block for MXFP4. The row is written at row `i` of Wout. */
+static void write_row(int wfmt, void* Wout, int64_t i, int64_t j, int D, const float* t, uint64_t seed,
+                      uint64_t step) {
+  if (wfmt == ORC_W_MXFP4) {
+    uint8_t* row = (uint8_t*)Wout + i * orc_mx_row_bytes(D);
+    for (int b = 0; b < D / 32; b++) {
+      uint32_t r[32];
+      uint8_t codes[32];
+      for (int k = 0; k < 32; k++) r[k] = orc_r16(seed, step, (uint64_t)(j * (int64_t)D + 32 * b + k));
+      orc_mx_quantize_block(t + 32 * b, r, codes, &row[D / 2 + b]);
+      for (int k = 0; k < 32; k += 2) row[(32 * b + k) / 2] = (uint8_t)(codes[k] | (codes[k + 1] << 4));
+    }
+    return;
+  }
+  for (int k = 0; k < D; k++) {
+    int64_t o = i * (int64_t)D + k;
+    uint32_t r = orc_r16(seed, step, (uint64_t)(j * (int64_t)D + k));
+    if (wfmt == ORC_W_BF16) ((uint16_t*)Wout)[o] = orc_sr_bf16(t[k], r);
+    else ((uint8_t*)Wout)[o] = orc_sr_e4m3(t[k], r);
+  }
 }
 
 /* per-sample label sets, sorted and deduplicated, for membership tests */
@@ -261,7 +349,7 @@ static double* forward_x(int wfmt, const uint16_t* X, int B, int D) {
   if (!xt) return NULL;
   for (int64_t i = 0; i < (int64_t)B * D; i++) {
     double v = orc_bf16_value(X[i]);
-    xt[i] = wfmt == ORC_W_BF16 ? v : orc_e4m3_value(orc_e4m3_rne_sat(v));
+    xt[i] = wfmt == ORC_W_BF16 ? v : orc_e4m3_value(orc_e4m3_rne_sat(v));   /* E4M3 and MXFP4 */
   }
   return xt;
 }
@@ -280,19 +368,12 @@ static float logit(int wfmt, const void* W, int64_t j, int D, const double* xt_r
   return (float)s;
 }
 
-/* updated code of weight (j, k) from its FP32 weight gradient; Tout (nullable) receives the FP32
- * value t that is stochastically rounded, at the same position i */
-static void store_update(int wfmt, void* Wout, int64_t i, double w, float dw, float lr,
-                         uint64_t seed, uint64_t step, uint64_t idx, float* Tout) {
-  float t = fmaf(-lr, dw, (float)w);        /* one FP32 rounding: SGD without momentum */
-  if (Tout) Tout[i] = t;
-  uint32_t r = orc_r16(seed, step, idx);
-  if (wfmt == ORC_W_BF16) ((uint16_t*)Wout)[i] = orc_sr_bf16(t, r);
-  else ((uint8_t*)Wout)[i] = orc_sr_e4m3(t, r);
-}
+/* SGD without momentum: t = fmaf(-lr, dW, w), one FP32 rounding */
+static float sgd_t(double w, float dw, float lr) { return fmaf(-lr, dw, (float)w); }
 
 static int check_common(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B) {
-  if (wfmt != ORC_W_BF16 && wfmt != ORC_W_E4M3) return ORC_EINVAL;
+  if (wfmt != ORC_W_BF16 && wfmt != ORC_W_E4M3 && wfmt != ORC_W_MXFP4) return ORC_EINVAL;
+  if (wfmt == ORC_W_MXFP4 && (D % 32 != 0 || D > 4096)) return ORC_EINVAL;
   if (!W || !X || L < 1 || D < 1 || B < 1) return ORC_EINVAL;
   return ORC_OK;
 }
@@ -336,15 +417,17 @@ int orc_step(int wfmt, void* W, int64_t L, int D, const uint16_t* X, int B,
     free(acc);
   }
 
-  /* weight gradient dW_jk = FP32(sum_b g_bj * x_bk) with the BF16 X, then SGD + SR in place */
+  /* weight gradient dW_jk = FP32(sum_b g_bj * x_bk) with the BF16 X, then SGD + SR in place (the
+   * whole row's t first: an MXFP4 block shares its scale) */
   #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < L; j++) {
+    float t[4096];
     for (int k = 0; k < D; k++) {
       double s = 0.0;
       for (int b = 0; b < B; b++) s += orc_bf16_value(G[(int64_t)b * L + j]) * xb[(int64_t)b * D + k];
-      int64_t i = j * (int64_t)D + k;
-      store_update(wfmt, W, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i, NULL);
+      t[k] = sgd_t(wval(wfmt, W, j, D, k), (float)s, lr);
     }
+    write_row(wfmt, W, j, j, D, t, seed, step);
   }
 
   if (loss) *loss = lsum;
@@ -364,12 +447,14 @@ int orc_update_from_g(int wfmt, const void* W, int64_t L, int D, const uint16_t*
   if (!xb) return ORC_ENOMEM;
   #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < L; j++) {
+    float t[4096];
     for (int k = 0; k < D; k++) {
       double s = 0.0;
       for (int b = 0; b < B; b++) s += orc_bf16_value(G[(int64_t)b * L + j]) * xb[(int64_t)b * D + k];
-      int64_t i = j * (int64_t)D + k;
-      store_update(wfmt, Wout, i, wval(wfmt, W, j, D, k), (float)s, lr, seed, step, (uint64_t)i, Tout);
+      t[k] = sgd_t(wval(wfmt, W, j, D, k), (float)s, lr);
+      if (Tout) Tout[j * (int64_t)D + k] = t[k];
     }
+    write_row(wfmt, Wout, j, j, D, t, seed, step);
   }
   free(xb);
   return ORC_OK;
@@ -396,12 +481,14 @@ int orc_logits(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int
  * row i of Wrows (and of Trows, the FP32 t, when not NULL). */
 static void update_row(int wfmt, const void* W, int64_t j, int D, const double* xb, const double* g, int B,
                        float lr, uint64_t seed, uint64_t step, void* Wrows, float* Trows, int i) {
+  float t[4096];
   for (int k = 0; k < D; k++) {
     double s = 0.0;
     for (int b = 0; b < B; b++) s += g[b] * xb[(int64_t)b * D + k];
-    store_update(wfmt, Wrows, (int64_t)i * D + k, wval(wfmt, W, j, D, k), (float)s, lr, seed, step,
-                 (uint64_t)(j * (int64_t)D + k), Trows);
+    t[k] = sgd_t(wval(wfmt, W, j, D, k), (float)s, lr);
+    if (Trows) Trows[(int64_t)i * D + k] = t[k];
   }
+  write_row(wfmt, Wrows, i, j, D, t, seed, step);
 }
 
 int orc_update_rows(int wfmt, const void* W, int64_t L, int D, const uint16_t* X, int B,

@@ -19,7 +19,10 @@
  * binary64 and are rounded once to binary32 where the method holds an FP32 value.
  *
  * All pointers are HOST pointers. Functions return 0 on success or a negative ORC_E* code.
- * Weight codes: BF16 as uint16 [L][D] row-major; E4M3 (OCP E4M3FN) as uint8 [L][D] row-major.
+ * Weight codes: BF16 as uint16 [L][D] row-major; E4M3 (OCP E4M3FN) as uint8 [L][D] row-major;
+ * MXFP4 as rows of orc_mx_row_bytes(D) = D/2 + D/32 bytes: the E2M1 codes two per byte (element 2i in
+ * the low nibble of byte i) then one E8M0 scale byte per 32-element block. For MXFP4, D % 32 == 0
+ * and the forward operand is E4M3-RNE(X), as for E4M3 weights.
  * X: BF16 codes [B][D] row-major. Labels: CSR row_ptr[B+1], ids[row_ptr[B]], int32, set semantics.
  */
 #ifndef ELMO_ORACLE_H
@@ -30,7 +33,7 @@ extern "C" {
 #endif
 
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENOMEM = -2 };
-enum { ORC_W_BF16 = 0, ORC_W_E4M3 = 1 };
+enum { ORC_W_BF16 = 0, ORC_W_E4M3 = 1, ORC_W_MXFP4 = 2 };
 
 /* codecs */
 double   orc_bf16_value(uint16_t code);
@@ -40,6 +43,16 @@ uint8_t  orc_e4m3_rne_sat(double x);
 /* stochastic rounding of an FP32 value with a 16-bit random integer r in [0, 65536) */
 uint16_t orc_sr_bf16(float t, uint32_t r);
 uint8_t  orc_sr_e4m3(float t, uint32_t r);
+/* OCP MX FP4: E2M1 element (4-bit code) and E8M0 scale values; stochastic rounding of v (the value
+ * already divided by the block's scale) to an E2M1 code with 16 random bits, saturating at 6; the
+ * block exponent X = clamp(floor(log2 amax) - 2, -127, 127) (0 -> -127, inf -> 127, NaN -> 128);
+ * one 32-element block: codes[k] (one per byte) and the scale code X + 127 (255 for a NaN block). */
+double   orc_e2m1_value(uint8_t code);
+double   orc_e8m0_value(uint8_t code);
+uint8_t  orc_sr_e2m1(double v, uint32_t r);
+int      orc_mx_block_exponent(float amax);
+void     orc_mx_quantize_block(const float* t, const uint32_t* r, uint8_t* codes, uint8_t* scale);
+int64_t  orc_mx_row_bytes(int D);
 /* Philox4x32 (Salmon, Moraes, Dror, Shaw, SC'11) with the given number of rounds */
 void     orc_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds, uint32_t out[4]);
 /* the 16 random bits used for weight element idx = j*D + k at (seed, step) */

@@ -131,6 +131,48 @@ static void step(int wfmt) {
   free(W); free(W2); free(Wu); free(Wr);
 }
 
+/* MX-scaled FP4: codecs, a block with a NaN, and a tiny step with its sampled entry points */
+static void mxfp4(void) {
+  for (int c = 0; c < 16; ++c) CHECK(fabs(orc_e2m1_value((uint8_t)c)) <= 6.0);
+  CHECK(isnan(orc_e8m0_value(255)) && orc_e8m0_value(127) == 1.0);
+  CHECK(orc_sr_e2m1(7.5, 3) == 7 && orc_sr_e2m1(-0.25, 65535) == 9);
+  float t[32];
+  uint32_t r[32];
+  uint8_t codes[32], scale;
+  for (int k = 0; k < 32; ++k) { t[k] = (float)(0.03 * rnd_gauss()); r[k] = rnd32() & 0xFFFF; }
+  orc_mx_quantize_block(t, r, codes, &scale);
+  CHECK(scale < 255);
+  t[3] = NAN;
+  orc_mx_quantize_block(t, r, codes, &scale);
+  CHECK(scale == 255);
+  enum { B = 4, D = 64, L = 19 };
+  const int64_t rb = orc_mx_row_bytes(D);
+  uint8_t* W = malloc((size_t)(rb * L));
+  uint8_t* W2 = malloc((size_t)(rb * L));
+  for (int64_t i = 0; i < rb * L; ++i) W[i] = (uint8_t)rnd32();
+  for (int j = 0; j < L; ++j)
+    for (int b = 0; b < D / 32; ++b) W[j * rb + D / 2 + b] = (uint8_t)(118 + (rnd32() % 4));
+  uint16_t X[B * D];
+  for (int i = 0; i < B * D; ++i) X[i] = orc_bf16_rne((float)(0.3 * rnd_gauss()));
+  int32_t row_ptr[B + 1] = {0, 2, 2, 4, 5};
+  int32_t ids[5] = {3, 18, 0, 3, 7};
+  float dX[B * D], T[L * D];
+  uint16_t G[B * L];
+  memcpy(W2, W, (size_t)(rb * L));
+  CHECK(orc_step(ORC_W_MXFP4, W2, L, D, X, B, row_ptr, ids, 0.05f, 2, 1, dX, NULL, NULL, G, 2) == ORC_OK);
+  uint8_t* Wu = malloc((size_t)(rb * L));
+  CHECK(orc_update_from_g(ORC_W_MXFP4, W, L, D, X, B, G, 0.05f, 2, 1, Wu, T, 1) == ORC_OK);
+  CHECK(memcmp(Wu, W2, (size_t)(rb * L)) == 0);
+  int64_t js[2] = {0, 18};
+  uint8_t Wr[2 * 64];
+  CHECK(orc_update_rows(ORC_W_MXFP4, W, L, D, X, B, row_ptr, ids, 0.05f, 2, 1, js, 2, Wr, NULL, NULL, 1) == ORC_OK);
+  CHECK(memcmp(Wr + rb, W2 + 18 * rb, (size_t)rb) == 0);
+  int32_t idx[2 * 3];
+  CHECK(orc_topk(ORC_W_MXFP4, W, L, D, X, 2, 3, idx, NULL, 1) == ORC_OK);
+  CHECK(orc_step(ORC_W_MXFP4, W2, L, 48, X, B, row_ptr, ids, 0.05f, 2, 1, dX, NULL, NULL, NULL, 1) == ORC_EINVAL);
+  free(W); free(W2); free(Wu);
+}
+
 static void exact_and_kahan(void) {
   enum { B = 3, D = 5, L = 4 };
   double W[L * D], X[B * D], Y[B * L], Z[B * L], G[B * L], dX[B * D], dW[L * D], loss;
@@ -151,6 +193,7 @@ int main(void) {
   rounding();
   step(ORC_W_BF16);
   step(ORC_W_E4M3);
+  mxfp4();
   exact_and_kahan();
   printf("oracle sanitizer run: ok\n");
   return 0;

@@ -9,7 +9,9 @@ Workloads stand in for the label spaces the ELMO pages train on (LF-AmazonTitles
 (Amazon|AmazonTitles)-670K, Amazon-3M and LF-Paper2Keywords-8.6M, named in the summary page's
 "Experimental setup" and "Key results"); no dataset item is reproduced, only sizes and shapes:
   * X: N(0, 1) rows normalised to unit L2 norm (tiny case: N(0, 1)/sqrt(D)), cast to BF16;
-  * W: N(0, 0.02^2), cast to BF16 or E4M3;
+  * W: N(0, 0.02^2), cast to BF16 or E4M3; MX-scaled FP4 weights are drawn in code space: E8M0
+    scales 2^-8 .. 2^-6 and E2M1 elements whose magnitudes follow |N(0, 0.02^2)| / 2^-7 binned to the
+    nearest E2M1 magnitude (signs uniform), which gives values of the same size;
   * labels: per sample 1 + Poisson(lam) positives with ids drawn from a finite Zipf(s) law over
     ranks 1..L (id = rank - 1), without replacement within a sample (tiny case: 1..8 positives,
     uniform ids without replacement).
@@ -23,6 +25,7 @@ import torch
 
 W_BF16 = 0
 W_E4M3 = 1
+W_MXFP4 = 2
 
 
 @dataclass(frozen=True)
@@ -51,7 +54,8 @@ class Workload:
 
     @property
     def wbytes(self):
-        return 2 if self.wfmt == W_BF16 else 1
+        """storage bytes per weight (MXFP4: half a byte plus a scale byte per 32)"""
+        return 2 if self.wfmt == W_BF16 else (17 / 32 if self.wfmt == W_MXFP4 else 1)
 
 
 WORKLOADS = {
@@ -65,7 +69,34 @@ WORKLOADS = {
                         "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=3),
     "bf16_8p6m": Workload("xmc-bf16-L8600000-D768-B128", 128, 768, 8600000, 262144, W_BF16, 0.05, 5,
                           "rownorm", "zipf", lam=9.0, zipf_s=1.2, topk=5, n_eval=4096, tag=4),
+    # the FP4 weights the pages leave open (with micro-tensor scaling), at the 3M-label head's shape
+    "mxfp4_3m": Workload("xmc-mxfp4-L3000000-D768-B256", 256, 768, 3000000, 131072, W_MXFP4, 0.1, 10,
+                         "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=5),
 }
+
+
+def mx_row_bytes(D: int) -> int:
+    return D // 2 + D // 32
+
+
+def _mx_magnitude_probs() -> np.ndarray:
+    """P(nearest E2M1 magnitude) of |N(0, (0.02 / 2^-7)^2)| (bin edges halfway between magnitudes)."""
+    import math
+    sd = 0.02 / 2.0 ** -7
+    edges = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    cdf = [math.erf(e / (sd * math.sqrt(2.0))) for e in edges] + [1.0]
+    p = np.diff(np.array([0.0] + cdf))
+    return p / p.sum()
+
+
+def make_w_mx(L: int, D: int, g: np.random.Generator) -> np.ndarray:
+    """MX-scaled FP4 rows [L][D/2 + D/32] drawn in code space (see the module docstring)."""
+    mag = g.choice(8, size=(L, D), p=_mx_magnitude_probs()).astype(np.uint8)
+    codes = mag | (g.integers(0, 2, (L, D), dtype=np.uint8) << 3)
+    out = np.empty((L, mx_row_bytes(D)), np.uint8)
+    out[:, :D // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    out[:, D // 2:] = g.integers(119, 122, (L, D // 32), dtype=np.uint8)
+    return out
 
 _PURPOSE = {"x": 0, "w": 1, "labels": 2, "eval_x": 3}
 
@@ -98,6 +129,8 @@ def make_x(B: int, D: int, kind: str, g: np.random.Generator) -> np.ndarray:
 
 
 def make_w(L: int, D: int, wfmt: int, g: np.random.Generator, block: int = 1 << 16) -> np.ndarray:
+    if wfmt == W_MXFP4:
+        return make_w_mx(L, D, g)
     out = np.empty((L, D), np.uint16 if wfmt == W_BF16 else np.uint8)
     for r0 in range(0, L, block):
         r1 = min(L, r0 + block)
@@ -111,6 +144,21 @@ def make_w_device(L: int, D: int, wfmt: int, seed: int, device, block: int = 1 <
     Returns a uint16/uint8 tensor [L, D] of codes."""
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
+    if wfmt == W_MXFP4:
+        out = torch.empty((L, mx_row_bytes(D)), dtype=torch.uint8, device=device)
+        probs = torch.from_numpy(_mx_magnitude_probs()).to(device=device, dtype=torch.float32)
+        cum = torch.cumsum(probs, 0)
+        cum[-1] = 1.0
+        for r0 in range(0, L, block):
+            r1 = min(L, r0 + block)
+            u = torch.rand((r1 - r0, D), generator=gen, device=device)
+            mag = torch.searchsorted(cum, u.contiguous()).clamp_(max=7).to(torch.uint8)
+            sign = (torch.rand((r1 - r0, D), generator=gen, device=device) < 0.5).to(torch.uint8) << 3
+            codes = mag | sign
+            out[r0:r1, :D // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+            out[r0:r1, D // 2:] = torch.randint(119, 122, (r1 - r0, D // 32), generator=gen, device=device,
+                                                dtype=torch.uint8)
+        return out
     dt = torch.int16 if wfmt == W_BF16 else torch.uint8
     out = torch.empty((L, D), dtype=dt, device=device)
     for r0 in range(0, L, block):
