@@ -42,10 +42,19 @@ typedef enum {
 } elmo_status;
 
 /* Weight storage formats. BF16: uint16 codes. E4M3: OCP FP8 E4M3FN codes (uint8; max 448, no
- * infinity, 0x7F/0xFF NaN) — the "E4M3" of the summary page's "Surprising findings". */
-enum { ELMO_W_BF16 = 0, ELMO_W_E4M3 = 1 };
+ * infinity, 0x7F/0xFF NaN) — the "E4M3" of the summary page's "Surprising findings".
+ * MXFP4: OCP Microscaling FP4 (the FP4 weights that the summary page's "Limitations" leave to
+ * micro-tensor scaling): each row is D/2 bytes of E2M1 codes (element 2i in the low nibble of byte
+ * i, 2i+1 in the high nibble; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) followed by D/32 E8M0 scale
+ * bytes (2^(c-127), 255 = NaN), scale b applying to elements 32b .. 32b+31: 17*D/32 bytes per row,
+ * "L x D" below meaning L such rows. Requires D % 256 == 0. The forward scores against
+ * E4M3-RNE(X); the update recomputes each block's scale from the new values t: X = floor(log2
+ * max|t|) - 2 clamped to [-127, 127] (an all-zero block takes -127, a block with a NaN scale 255
+ * and zero codes), then each element SR(t / 2^X) to E2M1 with the element's 16 random bits (the
+ * same rule and draws as the other formats), saturating at magnitude 6. */
+enum { ELMO_W_BF16 = 0, ELMO_W_E4M3 = 1, ELMO_W_MXFP4 = 2 };
 
-/* Supported shapes: 1 <= B <= 256; 64 <= D <= 1024 with D % 64 == 0; 1 <= L < 2^31;
+/* Supported shapes: 1 <= B <= 256; 64 <= D <= 1024 with D % 64 == 0 (MXFP4: D % 256 == 0); 1 <= L < 2^31;
  * chunk >= 1 (rounded down internally to a multiple of 128 labels, at least 128, and capped so that
  * one chunk of weight rows stays below 2 GiB). */
 #define ELMO_MAX_B 256
@@ -60,7 +69,7 @@ const char* elmo_status_str(int status);
  * classifier, stochastic rounding, no momentum, gradient computation fused with the SGD update,
  * label dimension chunked; arXiv abstract: "gradient fusion and chunking").
  *
- *   W        [L, D] row-major weight codes (BF16 or E4M3 per `wdtype`), updated IN PLACE.
+ *   W        [L, D] row-major weight codes (BF16, E4M3 or MXFP4 rows per `wdtype`), updated IN PLACE.
  *   X        [B, D] row-major BF16 codes (encoder features). Read only.
  *   row_ptr  [B+1] int32, ids [nnz] int32: the positive labels of each sample in CSR form; set
  *            semantics (duplicates collapse, any order, empty rows allowed). Ids outside [0, L)
@@ -79,8 +88,9 @@ const char* elmo_status_str(int status);
  *   workspace, workspace_bytes: at least elmo_xmc_step_workspace_bytes(...) bytes of device
  *            memory, used for label buckets, padded/cast copies of X, one chunk of G and the dX
  *            partial sums. Its first 4 bytes are the flags word after the step completes.
- * Per element: z = X~ . w_j (X~ = X, or E4M3-RNE(X) for E4M3 weights), g = BF16-RNE(sigmoid(z) - y),
- * dX += g W_old, dW = g^T X, t = fmaf(-lr, dW, w), W = SR(t).
+ * Per element: z = X~ . w_j (X~ = X, or E4M3-RNE(X) for E4M3 and MXFP4 weights), g =
+ * BF16-RNE(sigmoid(z) - y), dX += g W_old, dW = g^T X, t = fmaf(-lr, dW, w), W = SR(t) (for MXFP4
+ * per 32-element block, as described with the formats).
  */
 #define ELMO_FLAG_LABEL_RANGE 1u
 #define ELMO_FLAG_ROW_PTR 2u
@@ -178,6 +188,15 @@ int elmo_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float
  *                               in0 float z[n], in1 uint32 y[n] -> out float[n]
  *   op 9  gradient, the forward's split-exponent form (meant for |z| <= 80), binary32 before rounding:
  *                               in0 float z[n], in1 uint32 y[n] -> out float[n]
+ *   op 10 SR to E2M1 (v already divided by its block scale): in0 float[n], in1 uint32 r[n] -> out uint8[n]
+ *   op 11 MX block quantisation: in0 float t[32 n], in1 uint32 r[32 n] -> out uint8[33 n] (per block the
+ *                               32 E2M1 codes, then the E8M0 scale code; 255 for a block with a NaN)
+ *   op 12 E2M1 -> BF16 as the backward decodes MXFP4 weight tiles: in0 uint32 w[n] (8 codes, low
+ *                               nibble first), in1 uint32 E8M0 scale code[n] -> out uint32[4 n] (BF16 pairs)
+ *   op 13 one scaled MFMA in the forward's MXFP4 operand layout (E4M3 A, E2M1 B, E8M0 scales per
+ *                               32-element block): in0 uint8[3200] = A codes [32][64], B codes [32][32]
+ *                               (two per byte), A scales [32][2], B scales [32][2]; out float[1024] = C
+ *                               [32][32] row-major; n must be 1
  */
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n,
                         uint64_t seed, uint64_t step, void* stream);

@@ -8,8 +8,9 @@ declared in include/elmo_xmc.h. PyTorch supplies device memory and the current s
     idx, score = elmo.topk(W, X_eval, k=5)
 
 W: [L, D] torch tensor of weight codes on the GPU, updated in place: int16/uint16/bfloat16 for
-BF16 weights, uint8/float8_e4m3fn for OCP E4M3 weights. X: [B, D] BF16 codes (int16/uint16/
-bfloat16). row_ptr/ids: int32 CSR positive labels on the GPU.
+BF16 weights, uint8/float8_e4m3fn for OCP E4M3 weights; MX-scaled FP4 weights are uint8 rows of
+D/2 code bytes and D/32 scale bytes ([L, 17 D / 32]) and need wfmt=ELMO_W_MXFP4. X: [B, D] BF16
+codes (int16/uint16/bfloat16). row_ptr/ids: int32 CSR positive labels on the GPU.
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libelmo_xmc.so")
 
 ELMO_W_BF16 = 0
 ELMO_W_E4M3 = 1
+ELMO_W_MXFP4 = 2
 FLAG_LABEL_RANGE = 1
 FLAG_ROW_PTR = 2
 
@@ -98,6 +100,18 @@ def wdtype_of(W: torch.Tensor) -> int:
     raise TypeError(f"unsupported weight dtype {W.dtype}")
 
 
+def _wdims(W: torch.Tensor, wfmt):
+    """(format, L, D) of a weight tensor: by dtype, or MXFP4 rows of 17 D / 32 bytes when asked."""
+    if wfmt is None or wfmt != ELMO_W_MXFP4:
+        wd = wdtype_of(W)
+        if wfmt is not None and wfmt != wd:
+            raise TypeError(f"weight dtype {W.dtype} does not hold format {wfmt}")
+        return wd, W.shape[0], W.shape[1]
+    if W.dtype != torch.uint8 or W.dim() != 2 or (W.shape[1] * 32) % 17:
+        raise TypeError("MXFP4 weights are uint8 rows of D/2 code bytes and D/32 scale bytes")
+    return ELMO_W_MXFP4, W.shape[0], W.shape[1] * 32 // 17
+
+
 def _check_dev(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
@@ -108,12 +122,11 @@ def step_workspace_bytes(B, D, L, chunk, wdtype, max_nnz):
     return int(lib().elmo_xmc_step_workspace_bytes(B, D, L, chunk, wdtype, max_nnz))
 
 
-def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, workspace=None):
+def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, workspace=None, wfmt=None):
     """One fused training step; W is updated in place. Returns (dX [B, D] float32, loss tensor|None)."""
     _check_dev(W, X, row_ptr, ids)
-    L, D = W.shape
+    wd, L, D = _wdims(W, wfmt)
     B = X.shape[0]
-    wd = wdtype_of(W)
     nnz = int(ids.numel())
     if dX is None:
         dX = torch.empty((B, D), dtype=torch.float32, device=W.device)
@@ -132,14 +145,14 @@ def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, wo
     return dX, loss
 
 
-def step_noalloc(W, X, row_ptr, ids, lr, seed, step, chunk, dX, loss=None):
+def step_noalloc(W, X, row_ptr, ids, lr, seed, step, chunk, dX, loss=None, wfmt=None):
     """The same step through the allocation-free entry point (static scratch inside the library):
     dX [B, D] float32 and the optional loss [1] float32 are caller-allocated outputs."""
     _check_dev(W, X, row_ptr, ids, dX, loss)
-    L, D = W.shape
+    wd, L, D = _wdims(W, wfmt)
     B = X.shape[0]
     nnz = int(ids.numel())
-    rc = lib().elmo_xmc_step_noalloc(_ptr(W), wdtype_of(W), L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None,
+    rc = lib().elmo_xmc_step_noalloc(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None,
                                      nnz, float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss), _stream())
     _chk("elmo_xmc_step_noalloc", rc)
     return dX, loss
@@ -155,12 +168,11 @@ def topk_workspace_bytes(N, D, L, k, wdtype):
     return int(lib().elmo_xmc_topk_workspace_bytes(N, D, L, k, wdtype))
 
 
-def topk(W, X, k, workspace=None, want_score=True):
+def topk(W, X, k, workspace=None, want_score=True, wfmt=None):
     """Top-k labels per row of X by FP32 logit (ties to the smaller label). Returns (idx, score)."""
     _check_dev(W, X)
-    L, D = W.shape
+    wd, L, D = _wdims(W, wfmt)
     N = X.shape[0]
-    wd = wdtype_of(W)
     idx = torch.empty((N, k), dtype=torch.int32, device=W.device)
     score = torch.empty((N, k), dtype=torch.float32, device=W.device) if want_score else None
     need = topk_workspace_bytes(N, D, L, k, wd)
@@ -173,12 +185,11 @@ def topk(W, X, k, workspace=None, want_score=True):
     return idx, score
 
 
-def logits(W, X, l0, l1):
+def logits(W, X, l0, l1, wfmt=None):
     """FP32 logits [B, l1 - l0] from the step's forward kernel (diagnostic)."""
     _check_dev(W, X)
-    L, D = W.shape
+    wd, L, D = _wdims(W, wfmt)
     B = X.shape[0]
-    wd = wdtype_of(W)
     Z = torch.empty((B, l1 - l0), dtype=torch.float32, device=W.device)
     need = step_workspace_bytes(B, D, L, l1 - l0, wd, 0)
     ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=W.device)
@@ -187,13 +198,12 @@ def logits(W, X, l0, l1):
     return Z
 
 
-def forward(W, X, row_ptr, ids, l0, l1, want_z=True, want_g=True):
+def forward(W, X, row_ptr, ids, l0, l1, want_z=True, want_g=True, wfmt=None):
     """The step's forward kernel over labels [l0, l1): (Z float32 | None, G int16 BF16 codes | None),
     each [B, l1 - l0]. Weights are not modified (diagnostic)."""
     _check_dev(W, X, row_ptr, ids)
-    L, D = W.shape
+    wd, L, D = _wdims(W, wfmt)
     B = X.shape[0]
-    wd = wdtype_of(W)
     nnz = int(ids.numel()) if ids is not None else 0
     Z = torch.empty((B, l1 - l0), dtype=torch.float32, device=W.device) if want_z else None
     G = torch.empty((B, l1 - l0), dtype=torch.int16, device=W.device) if want_g else None
@@ -232,11 +242,13 @@ def kahan_update(w, c, g, lr):
 def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):
     """Device codec / SR / RNG / gradient applied elementwise (test hook; see elmo_xmc.h)."""
     out_dtype = {0: torch.int16, 1: torch.uint8, 2: torch.float32, 3: torch.int16, 4: torch.uint8,
-                 5: torch.int32, 6: torch.int16, 7: torch.int32, 8: torch.float32, 9: torch.float32}[op]
+                 5: torch.int32, 6: torch.int16, 7: torch.int32, 8: torch.float32, 9: torch.float32,
+                 10: torch.uint8, 11: torch.uint8, 12: torch.int32, 13: torch.float32}[op]
     if n is None:
-        n = in0.numel()
+        n = in0.numel() if op not in (11, 13) else (in0.numel() // 32 if op == 11 else 1)
     dev = in0.device if in0 is not None else torch.device("cuda")
-    out = torch.empty((2 * n if op == 7 else n,), dtype=out_dtype, device=dev)
+    size = {7: 2 * n, 11: 33 * n, 12: 4 * n, 13: 1024}.get(op, n)
+    out = torch.empty((size,), dtype=out_dtype, device=dev)
     if op == 5:
         host = ctypes.c_uint64(idx0)
         rc = lib().elmo_numerics_probe(op, ctypes.cast(ctypes.byref(host), ctypes.c_void_p), None, _ptr(out), n,

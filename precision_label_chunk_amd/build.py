@@ -26,7 +26,7 @@ HIPCC_FLAGS = [
 
 # sources compiled once per variant (each variant defines the macros listed)
 VARIANTS = {
-    "step_chunks.hip": [{"ELMO_MB": mb, "ELMO_WF": wf} for wf in (0, 1) for mb in (32, 64, 128, 256)],
+    "step_chunks.hip": [{"ELMO_MB": mb, "ELMO_WF": wf} for wf in (0, 1, 2) for mb in (32, 64, 128, 256)],
 }
 
 

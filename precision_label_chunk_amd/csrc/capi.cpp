@@ -13,6 +13,13 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// the weight format, and the feature sizes it supports (MXFP4 rows must be 8-byte aligned)
+int check_format(int wdtype, int D) {
+  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3 && wdtype != ELMO_W_MXFP4) return ELMO_EDTYPE;
+  if (wdtype == ELMO_W_MXFP4 && D % 256 != 0) return ELMO_ESHAPE;
+  return ELMO_OK;
+}
+
 int check_shapes(int B, int D, int64_t L) {
   if (B < 1 || B > ELMO_MAX_B) return ELMO_ESHAPE;
   if (D < 64 || D > ELMO_MAX_D || D % 64 != 0) return ELMO_ESHAPE;
@@ -42,16 +49,16 @@ const char* elmo_status_str(int status) {
 
 size_t elmo_xmc_step_workspace_bytes(int B, int D, int64_t L, int64_t chunk, int wdtype, int64_t max_nnz) {
   if (check_shapes(B, D, L) != ELMO_OK || chunk < 1 || max_nnz < 0) return 0;
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return 0;
+  if (check_format(wdtype, D) != ELMO_OK) return 0;
   return elmo::step_layout(B, D, L, chunk, wdtype, max_nnz).total;
 }
 
 int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
                   const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
                   float* dX, float* loss_sum, void* workspace, size_t workspace_bytes, void* stream) {
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return ELMO_EDTYPE;
-  int rc = check_shapes(B, D, L);
+  int rc = check_format(wdtype, D);
   if (rc != ELMO_OK) return rc;
+  if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
   if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
   if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
   if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
@@ -68,9 +75,9 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B, c
 int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
                           const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
                           float* dX, float* loss_sum, void* stream) {
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return ELMO_EDTYPE;
-  int rc = check_shapes(B, D, L);
+  int rc = check_format(wdtype, D);
   if (rc != ELMO_OK) return rc;
+  if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
   if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
   if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
   if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
@@ -96,9 +103,9 @@ int elmo_xmc_step_flags(const void* workspace, uint32_t* flags, void* stream) {
 int elmo_xmc_forward(const void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
                      const int32_t* ids, int64_t nnz, int64_t l0, int64_t l1, float* Z, uint16_t* G,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return ELMO_EDTYPE;
-  int rc = check_shapes(B, D, L);
+  int rc = check_format(wdtype, D);
   if (rc != ELMO_OK) return rc;
+  if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
   if (l0 < 0 || l1 > L || l1 <= l0) return ELMO_ESHAPE;
   if (nnz < 0 || (nnz > 0 && (!ids || !row_ptr))) return ELMO_EINVAL;
   if (!W || !X || (!Z && !G) || !aligned16(W) || !aligned16(X)) return ELMO_EINVAL;

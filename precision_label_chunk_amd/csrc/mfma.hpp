@@ -6,6 +6,13 @@
 //                             C: lane l, register i holds col n = l%32, row m = 8*(i/4) + 4*(l/32) + i%4
 //   v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, no block scaling): as above with k = 32*(l/32) + e,
 //                             e = 0..31 bytes; it reads 0x7E as 448 and honours subnormals.
+//                             (With both operands 8-bit only their common K order matters.)
+//   v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 A x E2M1 B: B lane l holds col n = l%32, k = 32*(l/32) + e,
+//                             e = 0..31 in 16 bytes (element e in nibble e & 1 of byte e / 2); A lane l
+//                             holds row m = l%32 with k = 16*(l/32) + e in bytes 0..15 and
+//                             k = 32 + 16*(l/32) + e - 16 in bytes 16..31; each lane's E8M0 scale
+//                             (byte 0 of the operand) applies to its row's / column's K block
+//                             [32*(l/32), 32*(l/32) + 32).
 //   ds_read_b64_tr_b16        a group of 16 lanes reads a 4 x 16 block of 16-bit elements whose
 //                             row r is supplied (4 consecutive elements each) by lanes 4r..4r+3;
 //                             lane i of the group receives column i (rows 0..3).
@@ -33,6 +40,12 @@ __device__ __forceinline__ f32x16_t mfma_bf16(s16x8_t a, s16x8_t b, f32x16_t c) 
 __device__ __forceinline__ f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
   // format 0 = E4M3 for both operands; zero scale operands select the unscaled instruction
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// E4M3 A x E2M1 B with E8M0 block scales (one per lane: the scale of its 32-element K block; the
+// FP4 operand takes the low four registers)
+__device__ __forceinline__ f32x16_t mfma_e4m3_fp4(i32x8_t a, i32x8_t b, f32x16_t c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, scale_b);
 }
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;

@@ -90,6 +90,45 @@ __device__ __forceinline__ uint32_t sr_e4m3_into(uint32_t old, float t, uint32_t
 __device__ __forceinline__ uint32_t sr_bf16(float t, uint32_t r16) { return sr_bf16_into(0u, t, r16 << 16, false) & 0xffffu; }
 __device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) { return sr_e4m3_into<0>(0u, t, r16 << 16) & 0xffu; }
 
+// ---- MX-scaled FP4 (OCP Microscaling: 32 E2M1 elements share one E8M0 scale) -------------------
+// E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7, bit 3 the sign); E8M0 code c is 2^(c - 127).
+// Stochastic rounding of a value v already divided by its block's scale, with the 16 random bits r:
+// the spacing u is 0.5 below 2, 1 below 4 and 2 below 6 (|v| >= 6 saturates to 6); the magnitude in
+// units of u splits exactly into its floor n and fraction f, and it rounds up iff
+// floor(f * 2^16) + r >= 2^16 (the rule of the BF16 and E4M3 roundings). Returns the 4-bit code.
+__device__ __forceinline__ uint32_t sr_e2m1(float v, uint32_t r16) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t sgn = (f2u(v) >> 28) & 8u;
+  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);          // 1 / u, exact
+  const float au = a * inv;                                                 // exact (power of two)
+  const float n = __builtin_floorf(au);
+  const uint32_t q = (uint32_t)((au - n) * 65536.0f);                       // exact, < 2^16
+  const uint32_t up = q + r16 >= 65536u ? 1u : 0u;
+  const uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);              // code of value 0 in units of u
+  const uint32_t code = a >= 6.0f ? 7u : (uint32_t)n + up + base;
+  return sgn | code;
+}
+
+// the block exponent X = clamp(floor(log2 amax) - 2, -127, 127) for a finite amax > 0 (v_frexp_exp:
+// amax = m 2^e with m in [0.5, 1), so floor(log2 amax) = e - 1); 0 gives -127 and infinity 127
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  if (amax == __builtin_inff()) return 127;
+  const int x = __builtin_amdgcn_frexp_expf(amax) - 3;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// two E2M1 codes (byte `sel` of w) times the E8M0 scale c as a BF16 pair (gfx950's scaled FP4 ->
+// BF16 conversion: exact for the scales that keep the products inside BF16's range)
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  c &= 0xffu;
+  return c == 0u ? u2f(0x00400000u) : (c == 255u ? u2f(0x7fc00000u) : u2f(c << 23));   // 2^-127 is subnormal
+}
+
 // ---- Philox4x32-10 ------------------------------------------------------------------------------
 struct u32x4 { uint32_t x, y, z, w; };
 

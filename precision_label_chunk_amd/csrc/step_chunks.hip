@@ -94,53 +94,21 @@ __device__ __forceinline__ void fwd_stage_block(const float (&gv)[16], uint8_t* 
   }
 }
 
-template <int MB, int WF, bool LOSS, bool ZOUT>
-__global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
-                                               int D, int64_t c0, int clen,
-                                               const uint32_t* __restrict__ tile_off,
-                                               const uint32_t* __restrict__ bucket, int64_t bucket_cap,
-                                               int B, uint16_t* __restrict__ G, int64_t gpitch,
-                                               float* __restrict__ loss_part,
-                                               float* __restrict__ Z, uint16_t* __restrict__ Gout,
-                                               int64_t zpitch, int64_t zoff) {
-  constexpr int WB = MB >= 64 ? 2 : 1, WJ = 4 / WB;
-  constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
+// The epilogue of a 128-label forward tile (4 waves; wave (wb, wj) holds samples wb RW .. + RW - 1
+// and labels wj CW .. + CW - 1 of the tile in 32 x 32 accumulator blocks): the gradient straight
+// from the accumulators, block by block, into the label-major chunk buffer G. With 128 or 256
+// samples each wave's rows of G (CW = 64 labels) are staged in LDS (`smem`, free after the K loop:
+// at least 4 CW 144 bytes) 64 samples at a time, so that every row leaves as one whole 128-byte
+// segment instead of 16-byte pieces of 32 rows. The loss partial of the tile goes to loss_part[lslot].
+template <int MB, int RW, int CW, bool LOSS, bool ZOUT>
+__device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], uint8_t* smem,
+                                             const uint32_t* ybits, float* lred, int tid, int wb, int wj,
+                                             int jbase, int clen, int B, int64_t c0, uint16_t* __restrict__ G,
+                                             int64_t gpitch, float* __restrict__ loss_part, int64_t lslot,
+                                             float* __restrict__ Z, uint16_t* __restrict__ Gout, int64_t zpitch,
+                                             int64_t zoff) {
   constexpr int MI = RW / 32, NI = CW / 32;
-  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
-  // K slice: small enough for two work-groups per CU; 128 bytes (64 BF16 elements, half the
-  // barriers) where the LDS stages of 256 rows still leave room for the second work-group
-  constexpr int KS = (MB <= 128 && WF == W_BF16_) ? 128 : 64;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
-  __shared__ uint32_t ybits[TJ1 * (MB / 32)];    // positives, label-major: bit b & 31 of word [j][b >> 5]
-  __shared__ float lred[4];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wb = wave / WJ, wj = wave % WJ;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int tile = blockIdx.x;
-  const int64_t tg = c0 / TJ1 + tile;          // global 128-label tile index
-  const int jbase = tile * TJ1;                // first label of the tile, relative to c0
-  const int64_t rowbytes = (int64_t)D * ESZ;
-
-  f32x16_t acc[MI][NI];
-  // the tile's positives into ybits while the first K slices load
-  auto scan = [&]() {
-    for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
-    __syncthreads();
-    const uint64_t e0 = tile_off[tg];
-    const uint64_t e1 = tile_off[tg + 1] < (uint64_t)bucket_cap ? tile_off[tg + 1] : (uint64_t)bucket_cap;
-    for (uint64_t e = e0 + tid; e < e1; e += 256) {
-      uint32_t v = bucket[e];
-      uint32_t b = v >> 16, jl = v & (TJ1 - 1);
-      if (b < (uint32_t)MB) atomicOr(&ybits[jl * (MB / 32) + (b >> 5)], 1u << (b & 31));
-    }
-  };
-  fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj, scan);
-
-  // epilogue: gradient straight from the accumulators, block by block. With 128 or 256 samples
-  // each wave's rows of G (CW = 64 labels) are staged in LDS (free after the K loop) 64 samples at
-  // a time, so that every row leaves as one whole 128-byte segment instead of 16-byte pieces of
-  // 32 rows.
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   constexpr bool GST = MB >= 128 && !ZOUT;
   constexpr int GSP = 144;                     // staging row pitch (bytes): 16 rows per bank cycle
   uint8_t* gst = smem + wave * (CW * GSP);
@@ -190,8 +158,149 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     if (lane == 0) lred[wave] = lsum;
     __syncthreads();
-    if (tid == 0) loss_part[tg] = ((lred[0] + lred[1]) + lred[2]) + lred[3];
+    if (tid == 0) loss_part[lslot] = ((lred[0] + lred[1]) + lred[2]) + lred[3];
   }
+}
+
+template <int MB, int WF, bool LOSS, bool ZOUT>
+__global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xf,
+                                               int D, int64_t c0, int clen,
+                                               const uint32_t* __restrict__ tile_off,
+                                               const uint32_t* __restrict__ bucket, int64_t bucket_cap,
+                                               int B, uint16_t* __restrict__ G, int64_t gpitch,
+                                               float* __restrict__ loss_part,
+                                               float* __restrict__ Z, uint16_t* __restrict__ Gout,
+                                               int64_t zpitch, int64_t zoff) {
+  constexpr int WB = MB >= 64 ? 2 : 1, WJ = 4 / WB;
+  constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
+  constexpr int MI = RW / 32, NI = CW / 32;
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  // K slice: small enough for two work-groups per CU; 128 bytes (64 BF16 elements, half the
+  // barriers) where the LDS stages of 256 rows still leave room for the second work-group
+  constexpr int KS = (MB <= 128 && WF == W_BF16_) ? 128 : 64;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[fwd_smem_bytes(MB, KS)];
+  __shared__ uint32_t ybits[TJ1 * (MB / 32)];    // positives, label-major: bit b & 31 of word [j][b >> 5]
+  __shared__ float lred[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wb = wave / WJ, wj = wave % WJ;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tile = blockIdx.x;
+  const int64_t tg = c0 / TJ1 + tile;          // global 128-label tile index
+  const int jbase = tile * TJ1;                // first label of the tile, relative to c0
+  const int64_t rowbytes = (int64_t)D * ESZ;
+
+  f32x16_t acc[MI][NI];
+  // the tile's positives into ybits while the first K slices load
+  auto scan = [&]() {
+    for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
+    __syncthreads();
+    const uint64_t e0 = tile_off[tg];
+    const uint64_t e1 = tile_off[tg + 1] < (uint64_t)bucket_cap ? tile_off[tg + 1] : (uint64_t)bucket_cap;
+    for (uint64_t e = e0 + tid; e < e1; e += 256) {
+      uint32_t v = bucket[e];
+      uint32_t b = v >> 16, jl = v & (TJ1 - 1);
+      if (b < (uint32_t)MB) atomicOr(&ybits[jl * (MB / 32) + (b >> 5)], 1u << (b & 31));
+    }
+  };
+  fwd_tile<MB, WF, RW, CW, KS>(acc, smem, W + (c0 + jbase) * rowbytes, clen - jbase, Xf, rowbytes, tid, wb, wj, scan);
+
+  fwd_epilogue<MB, RW, CW, LOSS, ZOUT>(acc, smem, ybits, lred, tid, wb, wj, jbase, clen, B, c0, G, gpitch, loss_part, tg,
+                                      Z, Gout, zpitch, zoff);
+}
+
+// ------------------------------------------------------------------------------------------------
+// forward + gradient for MX-scaled FP4 weights (E2M1 elements, one E8M0 scale per 32 features)
+// ------------------------------------------------------------------------------------------------
+// One work-group per 128-label tile, 4 waves (the wave tiles of k_fwd_g). Z = X~ W_c^T on the scaled
+// matrix cores: E4M3 features (scale 1) times E2M1 weights with each lane's E8M0 block scale, one
+// 32 x 32 x 64 MFMA per K step and block. Every lane loads its own operand fragments from global
+// memory (the features from the E4M3 copy in the workspace, which stays in L2; the weight rows once
+// per work-group), one K step ahead of their use. Weight rows: D/2 code bytes then D/32 scale bytes
+// (17 D / 32 bytes: with D % 256 == 0 every row, and so every weight load, is 8-byte aligned, which
+// is why the code fragments are fetched in 8-byte pieces); rows past the chunk read as zero. The
+// epilogue is the tiled forward's.
+template <int MB, bool LOSS, bool ZOUT>
+__global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq,
+                                                int D, int64_t c0, int clen,
+                                                const uint32_t* __restrict__ tile_off,
+                                                const uint32_t* __restrict__ bucket, int64_t bucket_cap,
+                                                int B, uint16_t* __restrict__ G, int64_t gpitch,
+                                                float* __restrict__ loss_part,
+                                                float* __restrict__ Z, uint16_t* __restrict__ Gout,
+                                                int64_t zpitch, int64_t zoff) {
+  constexpr int WB = MB >= 64 ? 2 : 1, WJ = 4 / WB;
+  constexpr int RW = MB / WB, CW = TJ1 / WJ;   // wave tile: RW samples x CW labels
+  constexpr int MI = RW / 32, NI = CW / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * 64 * 144];   // the epilogue's G staging
+  __shared__ uint32_t ybits[TJ1 * (MB / 32)];
+  __shared__ float lred[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wb = wave / WJ, wj = wave % WJ;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tile = blockIdx.x;
+  const int64_t tg = c0 / TJ1 + tile;
+  const int jbase = tile * TJ1;
+  const int rb = D / 2 + D / 32;                     // bytes per weight row
+  const int nk = D / 64;
+  const int nvalid = clen - jbase < TJ1 ? clen - jbase : TJ1;
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + (c0 + jbase) * (int64_t)rb, nvalid * rb);
+  const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xq, MB * D);
+
+  for (int i = tid; i < TJ1 * (MB / 32); i += 256) ybits[i] = 0u;
+  __syncthreads();
+  {
+    const uint64_t e0 = tile_off[tg];
+    const uint64_t e1 = tile_off[tg + 1] < (uint64_t)bucket_cap ? tile_off[tg + 1] : (uint64_t)bucket_cap;
+    for (uint64_t e = e0 + tid; e < e1; e += 256) {
+      const uint32_t v = bucket[e];
+      const uint32_t b = v >> 16, jl = v & (TJ1 - 1);
+      if (b < (uint32_t)MB) atomicOr(&ybits[jl * (MB / 32) + (b >> 5)], 1u << (b & 31));
+    }
+  }
+
+  // operand fragments of K step kk: A rows wb RW + 32 mi + l32 (16 bytes at kk 64 + 16 hi and 16 at
+  // kk 64 + 32 + 16 hi), B rows wj CW + 32 ni + l32 (16 code bytes at kk 32 + 16 hi, scale byte
+  // D/2 + 2 kk + hi)
+  struct Frag { i32x8_t a[MI]; i32x4_t b[NI]; int sc[NI]; };
+  auto load = [&](int kk, Frag& f) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int o = (wb * RW + 32 * mi + l32) * D + kk * 64 + hi * 16;
+      const i32x4_t a0 = buffer_load16(xres, o), a1 = buffer_load16(xres, o + 32);
+      f.a[mi] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = wj * CW + 32 * ni + l32;
+      const i32x2_t b0 = __builtin_amdgcn_raw_buffer_load_b64(wres, row * rb + kk * 32 + hi * 16, 0, 0);
+      const i32x2_t b1 = __builtin_amdgcn_raw_buffer_load_b64(wres, row * rb + kk * 32 + hi * 16 + 8, 0, 0);
+      f.b[ni] = i32x4_t{b0[0], b0[1], b1[0], b1[1]};
+      f.sc[ni] = (int)__builtin_amdgcn_raw_buffer_load_b8(wres, row * rb + D / 2 + 2 * kk + hi, 0, 0);
+    }
+  };
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
+  Frag cur, nxt;
+  load(0, cur);
+  for (int kk = 0; kk < nk; ++kk) {
+    if (kk + 1 < nk) load(kk + 1, nxt);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const i32x8_t bv = {cur.b[ni][0], cur.b[ni][1], cur.b[ni][2], cur.b[ni][3], 0, 0, 0, 0};
+        acc[mi][ni] = mfma_e4m3_fp4(cur.a[mi], bv, acc[mi][ni], 127, cur.sc[ni]);
+      }
+    cur = nxt;
+  }
+  __syncthreads();                                   // label bits complete
+  fwd_epilogue<MB, RW, CW, LOSS, ZOUT>(acc, smem, ybits, lred, tid, wb, wj, jbase, clen, B, c0, G, gpitch, loss_part, tg,
+                                      Z, Gout, zpitch, zoff);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -428,13 +537,70 @@ struct UpdState {
   u32x4 c[2];
   i32x4_t ow[2];
   uint32_t pk[8];                              // packed results: 4 words per block (BF16), 2 (E4M3)
+  uint32_t amax;                               // MXFP4: largest |t| (bit pattern; NaN above +inf)
+  int x;                                       // MXFP4: the block exponent (128: NaN block)
 };
+
+// MXFP4 (the 32 features are one scale block): phases 12..15 compute four values t each and the
+// lane's largest magnitude, 16 takes the block's from the lane pair and its shared exponent X,
+// 17..20 recompute four values t each (one FMA: cheaper than keeping all 16 live) and round
+// t / 2^X to E2M1, packing runs of four codes (16 bits); then the lane pair swaps halves so that
+// lane half hi holds bytes 8 hi .. 8 hi + 7 of the block's 16 code bytes, and lane half 0 also
+// stores the scale byte (at soff).
+template <int WF>
+__device__ __forceinline__ void upd_phase_mx(int p, UpdState& st, const f32x16_t& acc, __amdgpu_buffer_rsrc_t wres,
+                                             int roff, int soff, int hi, float lr) {
+  auto tval = [&](int u, int hf, int e) {                      // register 8u + 4 hf + e
+    const uint32_t wb = (uint32_t)st.ow[u][2 * hf + (e >> 1)];
+    return fmaf(-lr, acc[8 * u + 4 * hf + e], u2f((e & 1) ? (wb & 0xffff0000u) : (wb << 16)));
+  };
+  if (p < 16) {
+    const int u = (p - 12) >> 1, hf = (p - 12) & 1;
+    if (p == 12) st.amax = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m = f2u(tval(u, hf, e)) & 0x7fffffffu;
+      st.amax = m > st.amax ? m : st.amax;
+    }
+  } else if (p == 16) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(st.amax, st.amax, false, false);
+    const uint32_t m = (uint32_t)sw[0] > (uint32_t)sw[1] ? (uint32_t)sw[0] : (uint32_t)sw[1];
+    st.x = m > 0x7f800000u ? 128 : mx_block_exponent(u2f(m));
+  } else {
+    const int u = (p - 17) >> 1, hf = (p - 17) & 1;
+    uint32_t run = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t r16 = rng_pick_hi(st.c[u], 4 * hf + e) >> 16;
+      const uint32_t c = st.x == 128 ? 0u : sr_e2m1(__builtin_amdgcn_ldexpf(tval(u, hf, e), -st.x), r16);
+      run |= c << (4 * e);
+    }
+    st.pk[2 * u + hf] = run;
+    if (p == 20) {
+      // runs 4u + 2 hf + hi of the block; A = runs hi | 2 + hi, B = runs 4 + hi | 6 + hi
+      const auto sw = __builtin_amdgcn_permlane32_swap(st.pk[0] | (st.pk[1] << 16), st.pk[2] | (st.pk[3] << 16),
+                                                       false, false);
+      const uint32_t x = (uint32_t)sw[0], y = (uint32_t)sw[1];
+      const i32x2_t v = {(int)((x & 0xffffu) | (y << 16)), (int)((x >> 16) | (y & 0xffff0000u))};
+      __builtin_amdgcn_raw_buffer_store_b64(v, wres, roff + 8 * hi, 0, 0);
+      const uint8_t sc = (uint8_t)(st.x == 128 ? 255 : st.x + 127);
+      __builtin_amdgcn_raw_buffer_store_b8(sc, wres, hi == 0 ? soff : 0x7ffffff0, 0, 0);
+    }
+  }
+}
 
 template <int WF>
 __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& acc, const uint16_t* ow,
                                           const int (&owa)[2], const int (&owb)[2], __amdgpu_buffer_rsrc_t wres,
-                                          int roff, uint64_t grp, int hi, float lr, uint64_t seed, uint64_t step) {
+                                          int roff, int soff, uint64_t grp, int hi, float lr, uint64_t seed,
+                                          uint64_t step) {
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  if constexpr (WF == W_MXFP4_) {
+    if (p >= 12) {
+      upd_phase_mx<WF>(p, st, acc, wres, roff, soff, hi, lr);
+      return;
+    }
+  }
   if (p == 0) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) st.c[k] = philox_counter(4 * grp + 2 * hi + k, step);
@@ -531,7 +697,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
                                                             uint64_t seed, uint64_t step, int first) {
   constexpr int NFB = DS / 32;                 // feature blocks
   constexpr int NW = NFB * NH, NT = 64 * NW;   // waves, threads
-  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
+  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;   // (MXFP4: the staging and stores below have their own forms)
   constexpr int NB = MB / 32;                  // sample blocks
   constexpr int NJB = 2 / NH;                  // label blocks per wave (dW, update)
   constexpr int NBW = NB / NH;                 // sample blocks per wave (dX)
@@ -546,7 +712,8 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   constexpr int GTE = TJ2 * MB;                // G tile elements
   constexpr int GCPR = MB / 8;                 // 16-byte chunks per G row
   constexpr int GPT = TJ2 * GCPR / NT;         // G chunks per thread
-  constexpr int WCPR = DS * ESZ / 16;          // 16-byte global W chunks per tile row
+  // global W items per tile row: 16-byte chunks (BF16, E4M3), 16-element parts (MXFP4: 8 code bytes)
+  constexpr int WCPR = WF == W_MXFP4_ ? DS / 16 : DS * ESZ / 16;
   constexpr int WPT = TJ2 * WCPR / NT;         // W chunks per thread
   constexpr int NOW = KK < 8 ? KK : 8;         // distinct dW operand offsets per lane
   constexpr int NOB = NBW < 4 ? NBW : 4;       // distinct dX operand offsets per lane and row
@@ -569,7 +736,7 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   const int nt = (clen + TJ2 - 1) / TJ2;
   const int t0 = (int)((int64_t)nt * r / NR), t1 = (int)((int64_t)nt * (r + 1) / NR);
   const int dsl = s * DS;
-  const int rowbytes = D * ESZ;
+  const int rowbytes = (int)w_row_bytes(WF, D);
   // the chunk's weight rows: rows past the chunk's end (the ragged last tile) load as zero and
   // drop their stores
   const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)rowbytes, clen * rowbytes);
@@ -663,7 +830,15 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     } else {
       constexpr int c = k - GPT;
       const int ci = tid + c * NT, jr = ci / WCPR, p = ci % WCPR;
-      wst[c] = buffer_load16(wres, (tn * TJ2 + jr) * rowbytes + dsl * ESZ + p * 16);
+      if constexpr (WF == W_MXFP4_) {
+        // 16 codes (8 bytes) and the scale byte of their 32-element block
+        const int ro = (tn * TJ2 + jr) * rowbytes;
+        const i32x2_t cd = __builtin_amdgcn_raw_buffer_load_b64(wres, ro + dsl / 2 + p * 8, 0, 0);
+        const int sc = (int)__builtin_amdgcn_raw_buffer_load_b8(wres, ro + D / 2 + dsl / 32 + p / 2, 0, 0);
+        wst[c] = i32x4_t{cd[0], cd[1], sc, 0};
+      } else {
+        wst[c] = buffer_load16(wres, (tn * TJ2 + jr) * rowbytes + dsl * ESZ + p * 16);
+      }
     }
   };
   auto store_item = [&](auto K, uint16_t* gdst, int wb) {
@@ -678,6 +853,15 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
       uint16_t* row = &Ws[wb][jr * DS];
       if constexpr (WF == W_BF16_) {
         *(i32x4_t*)(row + ((p ^ sw) << 3)) = wst[c];
+      } else if constexpr (WF == W_MXFP4_) {
+        const float sc = e8m0_to_f32((uint32_t)wst[c][2]);
+        const uint32_t w0 = (uint32_t)wst[c][0], w1 = (uint32_t)wst[c][1];
+        *(i32x4_t*)(row + (((2 * p) ^ sw) << 3)) =
+            i32x4_t{(int)fp4x2_to_bf16x2<0>(w0, sc), (int)fp4x2_to_bf16x2<1>(w0, sc),
+                    (int)fp4x2_to_bf16x2<2>(w0, sc), (int)fp4x2_to_bf16x2<3>(w0, sc)};
+        *(i32x4_t*)(row + (((2 * p + 1) ^ sw) << 3)) =
+            i32x4_t{(int)fp4x2_to_bf16x2<0>(w1, sc), (int)fp4x2_to_bf16x2<1>(w1, sc),
+                    (int)fp4x2_to_bf16x2<2>(w1, sc), (int)fp4x2_to_bf16x2<3>(w1, sc)};
       } else {
         uint32_t b[8];
 #pragma unroll
@@ -694,8 +878,9 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   auto upd_args = [&](auto PH, UpdState& st, const uint16_t* wsU, int tU) {
     constexpr int ph = decltype(PH)::value, jl = ph / UPD_PHASES;
     const int jb = jb0 + jl;
+    const int ro = (tU * TJ2 + jb * 32 + l32) * rowbytes;
     upd_phase<WF>(ph % UPD_PHASES, st, accP[jl], wsU + jb * 32 * DS, offUA, offUB, wres,
-                  (tU * TJ2 + jb * 32 + l32) * rowbytes + fU * ESZ,
+                  ro + (WF == W_MXFP4_ ? fU / 2 : fU * ESZ), ro + D / 2 + fU / 32,
                   ((uint64_t)(c0 + tU * TJ2 + jb * 32 + l32) * (uint64_t)D + (uint64_t)fU) >> 5, hi, lr, seed, step);
   };
   auto update = [&](int tU, int wbU) {         // the whole update of tile tU, in sequence
@@ -869,8 +1054,13 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
           return;
         }
       }
-      hipLaunchKernelGGL((k_fwd_g<MB, WF, L_, Z_>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen, toff, bucket,
-                         a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+      if constexpr (WF == W_MXFP4_) {
+        hipLaunchKernelGGL((k_fwd_mx<MB, L_, Z_>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen, toff, bucket,
+                           a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+      } else {
+        hipLaunchKernelGGL((k_fwd_g<MB, WF, L_, Z_>), dim3(nt1), dim3(256), 0, st, W, Xf, a.D, c0, clen, toff,
+                           bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+      }
     };
     if (a.forward_only()) {
       forward(std::false_type{}, std::true_type{}, a.Z, a.Gout, a.zpitch, a.zoff);

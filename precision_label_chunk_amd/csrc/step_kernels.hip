@@ -291,7 +291,7 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   if (c < TJ1) c = TJ1;
   if (c > Lr) c = Lr;
   // chunk-relative 32-bit byte offsets into the chunk's weight rows (one tile of slack)
-  const int64_t rb = (int64_t)D * (wdtype == W_E4M3_ ? 1 : 2);
+  const int64_t rb = w_row_bytes(wdtype, D);
   const int64_t cmax = ((int64_t)0x7fffffff / rb - TJ1) / TJ1 * TJ1;
   if (c > cmax) c = cmax;
   s.Cc = c;
@@ -310,7 +310,7 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   s.tile_off = off; off = align_up(off + 4 * (size_t)(s.ntiles + 1), A);
   s.bucket = off;   off = align_up(off + 4 * (size_t)(max_nnz > 0 ? max_nnz : 1), A);
   s.xb = off;       off = align_up(off + 2 * (size_t)s.MB * D, A);
-  s.xq = off;       off = align_up(off + (wdtype == W_E4M3_ ? (size_t)s.MB * D : 0), A);
+  s.xq = off;       off = align_up(off + (wdtype != W_BF16_ ? (size_t)s.MB * D : 0), A);
   s.xbt = off;      off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
   s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
@@ -363,7 +363,7 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     const int64_t n = (int64_t)s.MB * a.D;
     const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
     hipLaunchKernelGGL(k_prep_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)a.X, a.B, a.D, s.MB,
-                       (uint16_t*)(ws + s.xb), a.wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr,
+                       (uint16_t*)(ws + s.xb), a.wdtype != W_BF16_ ? ws + s.xq : (uint8_t*)nullptr,
                        (uint16_t*)(ws + s.xbt));
     LAUNCH_CHECK();
   }
@@ -372,9 +372,12 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   if (a.wdtype == W_BF16_) {
     rc = MB == 32 ? run_chunks<32, W_BF16_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_BF16_>(a, s, ws, st)
        : MB == 128 ? run_chunks<128, W_BF16_>(a, s, ws, st) : run_chunks<256, W_BF16_>(a, s, ws, st);
-  } else {
+  } else if (a.wdtype == W_E4M3_) {
     rc = MB == 32 ? run_chunks<32, W_E4M3_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_E4M3_>(a, s, ws, st)
        : MB == 128 ? run_chunks<128, W_E4M3_>(a, s, ws, st) : run_chunks<256, W_E4M3_>(a, s, ws, st);
+  } else {
+    rc = MB == 32 ? run_chunks<32, W_MXFP4_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_MXFP4_>(a, s, ws, st)
+       : MB == 128 ? run_chunks<128, W_MXFP4_>(a, s, ws, st) : run_chunks<256, W_MXFP4_>(a, s, ws, st);
   }
   if (rc != ELMO_OK_ || a.forward_only()) return rc;
   {

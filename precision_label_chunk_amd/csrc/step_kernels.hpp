@@ -9,7 +9,12 @@ namespace elmo {
 // status and format codes (mirror include/elmo_xmc.h)
 constexpr int ELMO_OK_ = 0, ELMO_EINVAL_ = -1, ELMO_ESHAPE_ = -2, ELMO_EDTYPE_ = -3, ELMO_EWORKSPACE_ = -4,
               ELMO_EHIP_ = -5, ELMO_EUNSUPPORTED_ = -6, ELMO_ESCRATCH_ = -7;
-constexpr int W_BF16_ = 0, W_E4M3_ = 1;
+constexpr int W_BF16_ = 0, W_E4M3_ = 1, W_MXFP4_ = 2;
+// bytes of one weight row: D codes (BF16, E4M3), or D/2 bytes of E2M1 code pairs then D/32 E8M0
+// block scales (MXFP4)
+__host__ __device__ constexpr int64_t w_row_bytes(int wf, int D) {
+  return wf == W_BF16_ ? 2 * (int64_t)D : wf == W_E4M3_ ? (int64_t)D : (int64_t)D / 2 + D / 32;
+}
 constexpr uint32_t ELMO_FLAG_LABEL_RANGE_ = 1u, ELMO_FLAG_ROW_PTR_ = 2u;
 
 constexpr int TJ1 = 128;       // labels per forward tile (and label-bucket granularity)
@@ -57,6 +62,10 @@ extern template int run_chunks<32, W_E4M3_>(const StepArgs&, const StepLayout&, 
 extern template int run_chunks<64, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 extern template int run_chunks<128, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 extern template int run_chunks<256, W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<32, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<64, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<128, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_chunks<256, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 
 // top-k
 struct TopkLayout { int MB, NRg; int64_t ncand; size_t xb, xq, cand_s, cand_i, total; };

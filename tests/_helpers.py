@@ -1,5 +1,5 @@
 """Comparison helpers shared by the GPU parity tests (tolerances follow the stated bar:
-logits and dX within 1e-2 relative for BF16 weights and 6e-2 for E4M3 weights, with an RMS floor;
+logits and dX within 1e-2 relative for BF16 weights and 6e-2 for E4M3 and MXFP4 weights, with an RMS floor;
 updated weights >= 99.9% bit-equal and every other element within one unit of the storage format,
 or explained by a named, bounded difference of the FP32 arithmetic before the rounding; top-k
 indices exact where the ranking is decided by more than the measured logit error)."""
@@ -219,3 +219,111 @@ def check_topk_rows(idx_g, sc_g, idx_r, sc_r, Zg_rows, Zr_rows, label=""):
             assert np.all(zr[ig][fin_s] >= kth - tol), f"row {n}: a label far below the k-th"
     print(f"  top-{k}{label}: {N} rows, {tolerant} on the tolerant path", flush=True)
     return tolerant
+
+
+# ---- MX-scaled FP4 weights (rows of D/2 code bytes and D/32 E8M0 scale bytes) --------------------
+RTOL[wk.W_MXFP4] = 6e-2
+
+
+def mx_split(W):
+    """(element codes [n][D] uint8, scale codes [n][D/32] int64) of MXFP4 rows."""
+    W = np.ascontiguousarray(W, np.uint8)
+    D = W.shape[1] * 32 // 17
+    c = np.empty((W.shape[0], D), np.uint8)
+    c[:, 0::2] = W[:, :D // 2] & 15
+    c[:, 1::2] = W[:, :D // 2] >> 4
+    return c, W[:, D // 2:].astype(np.int64)
+
+
+def mx_signed(c):
+    """E2M1 codes as signed magnitude indices (monotone in the value; +-0 both 0)"""
+    c = np.asarray(c).astype(np.int64)
+    return np.where(c & 8, -(c & 7), c & 7)
+
+
+def mx_weight_report(got, ref):
+    """(fraction of elements with equal scale and equal value index, NaN-scale blocks in got)"""
+    cg, sg = mx_split(got)
+    cr, sr = mx_split(ref)
+    eq = (np.repeat(sg, 32, 1) == np.repeat(sr, 32, 1)) & (mx_signed(cg) == mx_signed(cr))
+    return float(eq.mean()), int((sg == 255).sum())
+
+
+def classify_weights_mx(orc, Wg, Wr, T, R, X, Gg, Gr, lr):
+    """classify_weights for MXFP4 rows. An element is equal when its block scale and its value index
+    equal the oracle's, class a when the scale is equal and the index one away. Otherwise it is
+    explained (class b or c, with the deltas D_b, D_c of classify_weights) when the device's values
+    t within D of the oracle's can give both the device's block scale and its code: the block's
+    largest |t| then lies in [max_k min|t_k +- D_k|, max_k max|t_k +- D_k|], the shared exponent is
+    monotone in it, so the device's must lie between the exponents of those two ends; and with that
+    exponent X fixed, SR(t / 2^X) with a fixed draw is monotone in t, so the device's code must lie in
+    [SR((t - D) / 2^X), SR((t + D) / 2^X)] (the oracle's rounding at both ends)."""
+    B = X.shape[0]
+    cg, sg = mx_split(Wg)
+    cr, sr = mx_split(Wr)
+    n, D = cg.shape
+    nb = D // 32
+    lr32 = abs(float(np.float32(lr)))
+    gg = code_value(Gg, wk.W_BF16)
+    gr = code_value(Gr, wk.W_BF16)
+    xa = np.abs(code_value(X, wk.W_BF16))
+    u = 2.0 ** -24
+    gam = B * u / (1 - B * u)
+    T64 = T.astype(np.float64)
+    S = np.maximum(np.abs(gg), np.abs(gr)).T @ xa
+    dc = 2.0 * lr32 * (gam + 2.0 ** -23) * S + 2.0 ** -22 * np.abs(T64)
+    db = dc + lr32 * (np.abs(gg - gr).T @ xa)
+    flipped = (np.asarray(Gg) != np.asarray(Gr)).any(axis=0)
+    sge, sre = np.repeat(sg, 32, 1), np.repeat(sr, 32, 1)
+    ig, ir = mx_signed(cg), mx_signed(cr)
+    equal = (sge == sre) & (ig == ir)
+    a = (sge == sre) & (np.abs(ig - ir) == 1)
+    rest = ~equal & ~a & (sge != 255)
+    rr, kk = np.nonzero(rest)
+
+    def explained(delta):
+        ok = np.zeros(rr.size, bool)
+        blocks = sorted(set(zip(rr.tolist(), (kk // 32).tolist())))
+        sc_ok = {}
+        for (j, b) in blocks:
+            t = T64[j, 32 * b:32 * b + 32]; d = delta[j, 32 * b:32 * b + 32]
+            lo = _outward_f32(t - d, -1).astype(np.float64); hi = _outward_f32(t + d, +1).astype(np.float64)
+            mlo = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+            mhi = np.maximum(np.abs(lo), np.abs(hi))
+            xlo = orc.mx_block_exponent(np.float32(mlo.max()))
+            xhi = orc.mx_block_exponent(np.float32(mhi.max()))
+            sc_ok[(j, b)] = xlo <= sg[j, b] - 127 <= xhi
+        for i, (j, k) in enumerate(zip(rr.tolist(), kk.tolist())):
+            if not sc_ok[(j, k // 32)]:
+                continue
+            x = int(sg[j, k // 32]) - 127
+            lo = float(_outward_f32(np.array([T64[j, k] - delta[j, k]]), -1)[0])
+            hi = float(_outward_f32(np.array([T64[j, k] + delta[j, k]]), +1)[0])
+            clo = mx_signed(orc.sr_e2m1(np.array([lo * 2.0 ** -x]), R[j, k]))[0]
+            chi = mx_signed(orc.sr_e2m1(np.array([hi * 2.0 ** -x]), R[j, k]))[0]
+            ok[i] = clo <= ig[j, k] <= chi
+        return ok
+
+    in_b = flipped[rr] & explained(db)
+    in_c = explained(dc)
+    cls_b = in_b
+    cls_c = ~in_b & in_c
+    fail = np.zeros((n, D), bool)
+    fail[rr[~in_b & ~in_c], kk[~in_b & ~in_c]] = True
+    d = np.abs(ig - ir)
+    return {"n": int(n * D), "equal": int(equal.sum()), "a": int(a.sum()), "b": int(cls_b.sum()),
+            "c": int(cls_c.sum()), "fail": int(fail.sum()), "max_dist": int(d.max()) if d.size else 0,
+            "scale_diff_blocks": int((sg != sr).sum()), "flipped_rows": int(flipped.sum()),
+            "nan_blocks": int((sg == 255).sum()), "fail_mask": fail}
+
+
+def assert_weights_free_running_mx(orc, Wg, Wr, T, R, X, Gg, Gr, lr, min_equal=0.999, label=""):
+    c = classify_weights_mx(orc, Wg, Wr, T, R, X, Gg, Gr, lr)
+    eq = c["equal"] / max(c["n"], 1)
+    print(f"  W free-running{label}: equal {eq:.6f} of {c['n']}  a(1 code) {c['a']}  b(flipped G row) {c['b']}"
+          f"  c(FP32 bound) {c['c']}  unexplained {c['fail']}  blocks with another scale {c['scale_diff_blocks']}"
+          f"  rows with flipped G {c['flipped_rows']}", flush=True)
+    assert c["nan_blocks"] == 0, f"{c['nan_blocks']} NaN weight blocks"
+    assert c["fail"] == 0, f"{c['fail']} weights outside every bound"
+    assert eq >= min_equal, f"only {eq:.6f} of weights equal"
+    return c
