@@ -16,7 +16,8 @@ reported beside them, since the events add a few microseconds between the kernel
 with the median of its per-step times). The first warm-up step, with cold caches, is timed on its
 own (`first_step_ms`). The same line carries a `bf16_8p6m` object measured the same way on the
 8.6M-label BF16 head (B=128, D=768, chunk 262,144, lr 0.05), whose step is bound by HBM, with its
-own top-5 pass over 4,096 held-out queries, roofline and CPU baseline.
+own top-5 pass over 4,096 held-out queries, roofline and CPU baseline, and a `mxfp4_3m` object for
+the 3M-label head with MX-scaled FP4 weights (B=256, D=768, chunk 131,072, lr 0.1).
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="e4m3_3m",
-                    help="one of tiny, bf16_131k, bf16_670k, e4m3_3m, bf16_8p6m")
+                    help="one of tiny, bf16_131k, bf16_670k, e4m3_3m, bf16_8p6m, mxfp4_3m")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
@@ -50,6 +51,10 @@ def parse():
                     help="workload measured into its own object of the same line ('none' to skip)")
     ap.add_argument("--no-8p6m", action="store_true", help="same as --second-workload none")
     ap.add_argument("--steps-8p6m", type=int, default=10, help="timed steps of the second workload")
+    ap.add_argument("--third-workload", default="mxfp4_3m",
+                    help="a third workload in its own object of the line ('none' to skip): by default the "
+                         "3M-label head with MX-scaled FP4 weights")
+    ap.add_argument("--steps-third", type=int, default=10, help="timed steps of the third workload")
     ap.add_argument("--kahan-params", type=int, default=110_000_000,
                     help="encoder parameters of the Kahan-compensated BF16 update pass (768-wide, 12 layers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -252,7 +257,7 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
         X, rp, ids = batches[s]
         if s == 0:
             evc[0].record(stream)
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
         if s == 0:
             evc[1].record(stream)
     torch.cuda.synchronize()
@@ -264,7 +269,7 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     ev0.record(stream)
     for s in range(warmup, nb):
         X, rp, ids = batches[s]
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -278,7 +283,7 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     evs[0].record(stream)
     for i, s in enumerate(range(warmup, nb)):
         X, rp, ids = batches[s]
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, nb + s, wl.chunk, dX=dX, workspace=ws)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, nb + s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     elmo.kernel_timing(False)
@@ -293,7 +298,9 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
 
     B, D, L = wl.B, wl.D, wl.L
     flops = 6.0 * B * D * L
-    fwd_peak = PEAK["fp8"] if wl.wfmt == wk.W_E4M3 else PEAK["bf16"]
+    # the forward's contraction: BF16 x BF16, E4M3 x E4M3, or E4M3 x E2M1 (MXFP4), which the scaled
+    # matrix cores run at the FP8 rate (an 8-bit operand sets it)
+    fwd_peak = PEAK["bf16"] if wl.wfmt == wk.W_BF16 else PEAK["fp8"]
     t_mfma = 2.0 * B * D * L / fwd_peak + 4.0 * B * D * L / PEAK["bf16"]
     alg_bytes = 2.0 * L * D * wl.wbytes
     t_hbm = alg_bytes / PEAK["hbm"]
@@ -319,7 +326,10 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
                     "per_label": per_label_b if hbm_bound else per_label_f}
     dom = max(kern, key=lambda k: kern[k]["ms_total"])
     kd = kern[dom]
-    kname = {"bwd": "k_bwd_update", "fwd": "k_fwd_g"}
+    # the forward kernel the launcher picks for this workload
+    fwd_kernel = ("k_fwd_mx" if wl.wfmt == wk.W_MXFP4 else
+                  "k_fwd_xs" if wl.wfmt == wk.W_E4M3 and D == 768 and B > 128 else "k_fwd_g")
+    kname = {"bwd": "k_bwd_update", "fwd": fwd_kernel}
     scale = 1e9 if kd["unit"] == "GB/s" else 1e12
     tr = measured_traffic(name, kname[dom])
     roofline = {"kernel": kname[dom], "bound": kd["bound"],
@@ -343,8 +353,9 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     out = {"ms_per_step": round(ms_step, 4), "samples_s": round(samples_s, 1), "steps": steps, "warmup": warmup,
            "first_step_ms": None if first_ms is None else round(first_ms, 4),
            "config": {"workload": wl.name, "B": B, "D": D, "L": L, "chunk": wl.chunk,
-                      "weights": "e4m3" if wl.wfmt == wk.W_E4M3 else "bf16", "lr": wl.lr},
-           "dtype": "e4m3+bf16" if wl.wfmt == wk.W_E4M3 else "bf16",
+                      "weights": {wk.W_BF16: "bf16", wk.W_E4M3: "e4m3", wk.W_MXFP4: "mxfp4"}[wl.wfmt],
+                      "lr": wl.lr},
+           "dtype": {wk.W_BF16: "bf16", wk.W_E4M3: "e4m3+bf16", wk.W_MXFP4: "e4m3xe2m1+bf16"}[wl.wfmt],
            "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
            "mfma_roofline_frac": round(t_mfma / (ms_step / 1e3), 4),
            "alg_hbm_gbs": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
@@ -363,11 +374,11 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
         Xe_host = wk.make_eval_x(wl, N)
         Xe = torch.from_numpy(Xe_host.view(np.int16)).to(dev)
         tws = torch.empty((elmo.topk_workspace_bytes(N, D, L, k, wl.wfmt),), dtype=torch.uint8, device=dev)
-        elmo.topk(W, Xe, k, workspace=tws)
+        elmo.topk(W, Xe, k, workspace=tws, wfmt=wl.wfmt)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        elmo.topk(W, Xe, k, workspace=tws)
+        elmo.topk(W, Xe, k, workspace=tws, wfmt=wl.wfmt)
         e1.record(stream)
         torch.cuda.synchronize()
         tk = e0.elapsed_time(e1)
@@ -425,12 +436,14 @@ def main():
     # the second label space the method is measured on (default: 8.6M labels in BF16 with B = 128,
     # bound by HBM), in an object of its own keyed by the workload's name
     second = "none" if args.no_8p6m else args.second_workload
-    if second != "none":
-        out[second] = bench_workload(second, args.steps_8p6m, 2, args, with_topk=not args.no_topk,
-                                     with_cpu=not args.no_cpu_baseline)
+    extra = [(second, args.steps_8p6m), (args.third_workload, args.steps_third)]
+    for name, nsteps in extra:
+        if name != "none":
+            out[name] = bench_workload(name, nsteps, 2, args, with_topk=not args.no_topk,
+                                       with_cpu=not args.no_cpu_baseline)
 
     info = cpu_info()
-    for obj in (out, out.get(second, {})):
+    for obj in [out] + [out.get(name, {}) for name, _ in extra]:
         for cb in (obj.get("cpu_baseline"), obj.get("topk", {}).get("cpu_baseline")):
             if cb is not None:
                 cb.update(info)

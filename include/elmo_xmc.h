@@ -123,7 +123,8 @@ int elmo_xmc_step_flags(const void* workspace, uint32_t* flags, void* stream);
 
 /*
  * Top-k scoring for precision@k (summary page, "Experimental setup": P@1, P@3, P@5).
- *   W [L, D] codes, X [N, D] BF16 codes (E4M3 weights score against E4M3-RNE(X), as in training).
+ *   W [L, D] codes, X [N, D] BF16 codes (E4M3 and MXFP4 weights score against E4M3-RNE(X), as in
+ *   training).
  *   out_idx [N, k] int32: labels ranked by (FP32 logit desc, label asc), NaN logits last.
  *   out_score [N, k] FP32 logits, nullable.  1 <= k <= min(ELMO_MAX_TOPK, L), N >= 1.
  */
@@ -197,6 +198,9 @@ int elmo_kahan_update(uint16_t* w, uint16_t* c, const float* g, int64_t n, float
  *                               32-element block): in0 uint8[3200] = A codes [32][64], B codes [32][32]
  *                               (two per byte), A scales [32][2], B scales [32][2]; out float[1024] = C
  *                               [32][32] row-major; n must be 1
+ *   op 14 the device's scaled FP4 conversion with stochastic rounding (a test hook for its rounding
+ *                               rule): in0 float[2n] pairs, in1 uint32[2n] (random operand, scale
+ *                               bits) per pair -> out uint32[n] (the two codes in byte 0)
  */
 int elmo_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n,
                         uint64_t seed, uint64_t step, void* stream);

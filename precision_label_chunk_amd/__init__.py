@@ -243,9 +243,9 @@ def numerics_probe(op, in0=None, in1=None, n=None, seed=0, step=0, idx0=0):
     """Device codec / SR / RNG / gradient applied elementwise (test hook; see elmo_xmc.h)."""
     out_dtype = {0: torch.int16, 1: torch.uint8, 2: torch.float32, 3: torch.int16, 4: torch.uint8,
                  5: torch.int32, 6: torch.int16, 7: torch.int32, 8: torch.float32, 9: torch.float32,
-                 10: torch.uint8, 11: torch.uint8, 12: torch.int32, 13: torch.float32}[op]
+                 10: torch.uint8, 11: torch.uint8, 12: torch.int32, 13: torch.float32, 14: torch.int32}[op]
     if n is None:
-        n = in0.numel() if op not in (11, 13) else (in0.numel() // 32 if op == 11 else 1)
+        n = {11: in0.numel() // 32, 13: 1, 14: in0.numel() // 2}.get(op, in0.numel())
     dev = in0.device if in0 is not None else torch.device("cuda")
     size = {7: 2 * n, 11: 33 * n, 12: 4 * n, 13: 1024}.get(op, n)
     out = torch.empty((size,), dtype=out_dtype, device=dev)

@@ -130,13 +130,14 @@ int elmo_xmc_logits(const void* W, int wdtype, int64_t L, int D, int64_t l0, int
 size_t elmo_xmc_topk_workspace_bytes(int N, int D, int64_t L, int k, int wdtype) {
   if (N < 1 || D < 64 || D > ELMO_MAX_D || D % 64 != 0 || L < 1 || L >= (int64_t(1) << 31)) return 0;
   if (k < 1 || k > ELMO_MAX_TOPK || k > L) return 0;
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return 0;
+  if (check_format(wdtype, D) != ELMO_OK) return 0;
   return elmo::topk_layout(N, D, L, k, wdtype).total;
 }
 
 int elmo_xmc_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, int k, int32_t* out_idx,
                   float* out_score, void* workspace, size_t workspace_bytes, void* stream) {
-  if (wdtype != ELMO_W_BF16 && wdtype != ELMO_W_E4M3) return ELMO_EDTYPE;
+  const int rc = check_format(wdtype, D);
+  if (rc != ELMO_OK) return rc;
   if (N < 1 || D < 64 || D > ELMO_MAX_D || D % 64 != 0 || L < 1 || L >= (int64_t(1) << 31)) return ELMO_ESHAPE;
   if (k < 1 || k > ELMO_MAX_TOPK || k > L) return ELMO_ESHAPE;
   if (!W || !X || !out_idx || !aligned16(W) || !aligned16(X)) return ELMO_EINVAL;

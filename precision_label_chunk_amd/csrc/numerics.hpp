@@ -92,21 +92,19 @@ __device__ __forceinline__ uint32_t sr_e4m3(float t, uint32_t r16) { return sr_e
 
 // ---- MX-scaled FP4 (OCP Microscaling: 32 E2M1 elements share one E8M0 scale) -------------------
 // E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7, bit 3 the sign); E8M0 code c is 2^(c - 127).
-// Stochastic rounding of a value v already divided by its block's scale, with the 16 random bits r:
-// the spacing u is 0.5 below 2, 1 below 4 and 2 below 6 (|v| >= 6 saturates to 6); the magnitude in
-// units of u splits exactly into its floor n and fraction f, and it rounds up iff
-// floor(f * 2^16) + r >= 2^16 (the rule of the BF16 and E4M3 roundings). Returns the 4-bit code.
-__device__ __forceinline__ uint32_t sr_e2m1(float v, uint32_t r16) {
-  const float a = __builtin_fabsf(v);
-  const uint32_t sgn = (f2u(v) >> 28) & 8u;
-  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);          // 1 / u, exact
-  const float au = a * inv;                                                 // exact (power of two)
-  const float n = __builtin_floorf(au);
-  const uint32_t q = (uint32_t)((au - n) * 65536.0f);                       // exact, < 2^16
-  const uint32_t up = q + r16 >= 65536u ? 1u : 0u;
-  const uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);              // code of value 0 in units of u
-  const uint32_t code = a >= 6.0f ? 7u : (uint32_t)n + up + base;
-  return sgn | code;
+// Stochastic rounding of t / scale (scale = 2^X, X in [-127, 127]) to E2M1 with the 16 random
+// bits r: the spacing u of the E2M1 grid is 0.5 below 2, 1 below 4 and 2 below 6 (magnitudes of 6
+// and above saturate to 6); the magnitude in units of u splits into its floor n and fraction f, and
+// it rounds up iff floor(f * 2^16) + r >= 2^16 (the rule of the BF16 and E4M3 roundings). gfx950's
+// scaled FP4 conversion with stochastic rounding computes exactly this for the first value of its
+// pair when r sits in bits 31..16 of its random operand and bits 15..0 are zero (checked on the
+// device against the rule over every range of the grid, signed zeros, subnormal inputs, infinities
+// and scales 2^-127 .. 2^127); the pair's second value (here +0, code 0) would take the operand
+// shifted left by one bit, so one conversion serves one element. Only the low nibble of the result
+// is defined here. rhi: the draw in bits 31..16. Returns the 4-bit code.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t sr_e2m1_scaled(float t, float scale, uint32_t rhi) {
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{t, 0.0f}, rhi, scale, 0) & 15u;
 }
 
 // the block exponent X = clamp(floor(log2 amax) - 2, -127, 127) for a finite amax > 0 (v_frexp_exp:

@@ -34,7 +34,7 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
         break;
       }
       case 10: {
-        ((uint8_t*)out)[i] = (uint8_t)sr_e2m1(((const float*)in0)[i], ((const uint32_t*)in1)[i] & 0xffffu);
+        ((uint8_t*)out)[i] = (uint8_t)sr_e2m1_scaled(((const float*)in0)[i], 1.0f, ((const uint32_t*)in1)[i] << 16);
         break;
       }
       case 11: {
@@ -50,9 +50,18 @@ __global__ void k_numerics(int op, const void* __restrict__ in0, const void* __r
           o[32] = 255;
         } else {
           const int x = mx_block_exponent(amax);
-          for (int k = 0; k < 32; ++k) o[k] = (uint8_t)sr_e2m1(__builtin_ldexpf(t[k], -x), r[k] & 0xffffu);
+          const float sc = e8m0_to_f32((uint32_t)(x + 127));
+          for (int k = 0; k < 32; ++k) o[k] = (uint8_t)sr_e2m1_scaled(t[k], sc, r[k] << 16);
           o[32] = (uint8_t)(x + 127);
         }
+        break;
+      }
+      case 14: {
+        // the scaled FP4 conversion with stochastic rounding as it stands: the float pair in0[2i],
+        // in0[2i+1], random operand in1[2i], scale bits in1[2i+1] -> the result word
+        const f32x2_t v = {((const float*)in0)[2 * i], ((const float*)in0)[2 * i + 1]};
+        const uint32_t* r = (const uint32_t*)in1 + 2 * i;
+        ((uint32_t*)out)[i] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, r[0], u2f(r[1]), 0);
         break;
       }
       case 12: {
@@ -99,9 +108,9 @@ __global__ void k_mx_mfma_probe(const uint8_t* __restrict__ in, float* __restric
 
 int run_numerics_probe(int op, const void* in0, const void* in1, void* out, int64_t n, uint64_t seed,
                        uint64_t step, hipStream_t st) {
-  if (op < 0 || op > 13 || n < 0 || !out) return ELMO_EINVAL_;
+  if (op < 0 || op > 14 || n < 0 || !out) return ELMO_EINVAL_;
   if (op != 5 && !in0) return ELMO_EINVAL_;
-  if ((op == 3 || op == 4 || op == 6 || op == 8 || op == 9 || op == 10 || op == 11 || op == 12) && !in1)
+  if ((op == 3 || op == 4 || op == 6 || op == 8 || op == 9 || op == 10 || op == 11 || op == 12 || op == 14) && !in1)
     return ELMO_EINVAL_;
   if (n == 0) return ELMO_OK_;
   if (op == 13) {

@@ -23,6 +23,7 @@
 
 #include <type_traits>
 
+#include "fwd_mx.hpp"
 #include "fwd_tile.hpp"
 #include "mfma.hpp"
 #include "numerics.hpp"
@@ -212,14 +213,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_g(const uint8_t* __restrict__ W,
 // ------------------------------------------------------------------------------------------------
 // forward + gradient for MX-scaled FP4 weights (E2M1 elements, one E8M0 scale per 32 features)
 // ------------------------------------------------------------------------------------------------
-// One work-group per 128-label tile, 4 waves (the wave tiles of k_fwd_g). Z = X~ W_c^T on the scaled
-// matrix cores: E4M3 features (scale 1) times E2M1 weights with each lane's E8M0 block scale, one
-// 32 x 32 x 64 MFMA per K step and block. Every lane loads its own operand fragments from global
-// memory (the features from the E4M3 copy in the workspace, which stays in L2; the weight rows once
-// per work-group), one K step ahead of their use. Weight rows: D/2 code bytes then D/32 scale bytes
-// (17 D / 32 bytes: with D % 256 == 0 every row, and so every weight load, is 8-byte aligned, which
-// is why the code fragments are fetched in 8-byte pieces); rows past the chunk read as zero. The
-// epilogue is the tiled forward's.
+// One work-group per 128-label tile, 4 waves (the wave tiles of k_fwd_g), the logits on the scaled
+// matrix cores (mx_logit_tile: every lane loads its own operand fragments, the features from the
+// E4M3 copy in the workspace, which stays in L2, the weight rows once per work-group); rows past
+// the chunk read as zero. The epilogue is the tiled forward's.
 template <int MB, bool LOSS, bool ZOUT>
 __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq,
                                                 int D, int64_t c0, int clen,
@@ -243,7 +240,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
   const int64_t tg = c0 / TJ1 + tile;
   const int jbase = tile * TJ1;
   const int rb = D / 2 + D / 32;                     // bytes per weight row
-  const int nk = D / 64;
   const int nvalid = clen - jbase < TJ1 ? clen - jbase : TJ1;
   const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + (c0 + jbase) * (int64_t)rb, nvalid * rb);
   const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xq, MB * D);
@@ -260,44 +256,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
     }
   }
 
-  // operand fragments of K step kk: A rows wb RW + 32 mi + l32 (16 bytes at kk 64 + 16 hi and 16 at
-  // kk 64 + 32 + 16 hi), B rows wj CW + 32 ni + l32 (16 code bytes at kk 32 + 16 hi, scale byte
-  // D/2 + 2 kk + hi)
-  struct Frag { i32x8_t a[MI]; i32x4_t b[NI]; int sc[NI]; };
-  auto load = [&](int kk, Frag& f) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int o = (wb * RW + 32 * mi + l32) * D + kk * 64 + hi * 16;
-      const i32x4_t a0 = buffer_load16(xres, o), a1 = buffer_load16(xres, o + 32);
-      f.a[mi] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    }
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int row = wj * CW + 32 * ni + l32;
-      const i32x2_t b0 = __builtin_amdgcn_raw_buffer_load_b64(wres, row * rb + kk * 32 + hi * 16, 0, 0);
-      const i32x2_t b1 = __builtin_amdgcn_raw_buffer_load_b64(wres, row * rb + kk * 32 + hi * 16 + 8, 0, 0);
-      f.b[ni] = i32x4_t{b0[0], b0[1], b1[0], b1[1]};
-      f.sc[ni] = (int)__builtin_amdgcn_raw_buffer_load_b8(wres, row * rb + D / 2 + 2 * kk + hi, 0, 0);
-    }
-  };
   f32x16_t acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16_t{};
-  Frag cur, nxt;
-  load(0, cur);
-  for (int kk = 0; kk < nk; ++kk) {
-    if (kk + 1 < nk) load(kk + 1, nxt);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const i32x8_t bv = {cur.b[ni][0], cur.b[ni][1], cur.b[ni][2], cur.b[ni][3], 0, 0, 0, 0};
-        acc[mi][ni] = mfma_e4m3_fp4(cur.a[mi], bv, acc[mi][ni], 127, cur.sc[ni]);
-      }
-    cur = nxt;
-  }
+  mx_logit_tile<MI, NI>(acc, xres, wb * RW, D, wres, wj * CW, rb, l32, hi);
   __syncthreads();                                   // label bits complete
   fwd_epilogue<MB, RW, CW, LOSS, ZOUT>(acc, smem, ybits, lred, tid, wb, wj, jbase, clen, B, c0, G, gpitch, loss_part, tg,
                                       Z, Gout, zpitch, zoff);
@@ -538,17 +498,20 @@ struct UpdState {
   i32x4_t ow[2];
   uint32_t pk[8];                              // packed results: 4 words per block (BF16), 2 (E4M3)
   uint32_t amax;                               // MXFP4: largest |t| (bit pattern; NaN above +inf)
-  int x;                                       // MXFP4: the block exponent (128: NaN block)
+  float scale;                                 // MXFP4: the block's scale 2^X (NaN: a NaN block)
 };
 
 // MXFP4 (the 32 features are one scale block): phases 12..15 compute four values t each and the
 // lane's largest magnitude, 16 takes the block's from the lane pair and its shared exponent X,
-// 17..20 recompute four values t each (one FMA: cheaper than keeping all 16 live) and round
-// t / 2^X to E2M1, packing runs of four codes (16 bits); then the lane pair swaps halves so that
+// 17..20 recompute four values t each (re-reading the old weights from LDS: cheaper than keeping
+// all 16 values or their weights live) and round
+// t / 2^X to E2M1 (the hardware's scaled conversion, one element each), packing runs of four codes
+// (16 bits); then the lane pair swaps halves so that
 // lane half hi holds bytes 8 hi .. 8 hi + 7 of the block's 16 code bytes, and lane half 0 also
 // stores the scale byte (at soff).
 template <int WF>
-__device__ __forceinline__ void upd_phase_mx(int p, UpdState& st, const f32x16_t& acc, __amdgpu_buffer_rsrc_t wres,
+__device__ __forceinline__ void upd_phase_mx(int p, UpdState& st, const f32x16_t& acc, const uint16_t* ow,
+                                             const int (&owa)[2], const int (&owb)[2], __amdgpu_buffer_rsrc_t wres,
                                              int roff, int soff, int hi, float lr) {
   auto tval = [&](int u, int hf, int e) {                      // register 8u + 4 hf + e
     const uint32_t wb = (uint32_t)st.ow[u][2 * hf + (e >> 1)];
@@ -565,17 +528,22 @@ __device__ __forceinline__ void upd_phase_mx(int p, UpdState& st, const f32x16_t
   } else if (p == 16) {
     const auto sw = __builtin_amdgcn_permlane32_swap(st.amax, st.amax, false, false);
     const uint32_t m = (uint32_t)sw[0] > (uint32_t)sw[1] ? (uint32_t)sw[0] : (uint32_t)sw[1];
-    st.x = m > 0x7f800000u ? 128 : mx_block_exponent(u2f(m));
+    // 2^X, or NaN for a block with a NaN (scale code 255); its E8M0 code is its bits >> 23 (2^-127,
+    // the one subnormal scale, is 0x00400000: code 0)
+    st.scale = e8m0_to_f32(m > 0x7f800000u ? 255u : (uint32_t)(mx_block_exponent(u2f(m)) + 127));
   } else {
     const int u = (p - 17) >> 1, hf = (p - 17) & 1;
+    if (hf == 0) {
+      // the old weights of block u again from the LDS tile (shorter register lifetimes than
+      // keeping all of them from phase 11)
+      const i32x2_t a = *(const i32x2_t*)(ow + owa[u]), b = *(const i32x2_t*)(ow + owb[u]);
+      st.ow[u] = i32x4_t{a[0], a[1], b[0], b[1]};
+    }
     uint32_t run = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t r16 = rng_pick_hi(st.c[u], 4 * hf + e) >> 16;
-      const uint32_t c = st.x == 128 ? 0u : sr_e2m1(__builtin_amdgcn_ldexpf(tval(u, hf, e), -st.x), r16);
-      run |= c << (4 * e);
-    }
-    st.pk[2 * u + hf] = run;
+    for (int e = 0; e < 4; ++e)
+      run |= sr_e2m1_scaled(tval(u, hf, e), st.scale, rng_pick_hi(st.c[u], 4 * hf + e)) << (4 * e);
+    st.pk[2 * u + hf] = st.scale != st.scale ? 0u : run;
     if (p == 20) {
       // runs 4u + 2 hf + hi of the block; A = runs hi | 2 + hi, B = runs 4 + hi | 6 + hi
       const auto sw = __builtin_amdgcn_permlane32_swap(st.pk[0] | (st.pk[1] << 16), st.pk[2] | (st.pk[3] << 16),
@@ -583,8 +551,7 @@ __device__ __forceinline__ void upd_phase_mx(int p, UpdState& st, const f32x16_t
       const uint32_t x = (uint32_t)sw[0], y = (uint32_t)sw[1];
       const i32x2_t v = {(int)((x & 0xffffu) | (y << 16)), (int)((x >> 16) | (y & 0xffff0000u))};
       __builtin_amdgcn_raw_buffer_store_b64(v, wres, roff + 8 * hi, 0, 0);
-      const uint8_t sc = (uint8_t)(st.x == 128 ? 255 : st.x + 127);
-      __builtin_amdgcn_raw_buffer_store_b8(sc, wres, hi == 0 ? soff : 0x7ffffff0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(f2u(st.scale) >> 23), wres, hi == 0 ? soff : 0x7ffffff0, 0, 0);
     }
   }
 }
@@ -597,7 +564,8 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
   constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   if constexpr (WF == W_MXFP4_) {
     if (p >= 12) {
-      upd_phase_mx<WF>(p, st, acc, wres, roff, soff, hi, lr);
+      upd_phase_mx<WF>(p, st, acc, ow, owa, owb, wres, roff, soff, hi, lr);
+      sched_fence();                           // (keeps the phases' register lifetimes apart)
       return;
     }
   }

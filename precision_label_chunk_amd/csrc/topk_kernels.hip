@@ -12,6 +12,7 @@
 // A second kernel merges the per-range lists of each sample.
 #include <float.h>
 
+#include "fwd_mx.hpp"
 #include "fwd_tile.hpp"
 #include "mfma.hpp"
 #include "numerics.hpp"
@@ -60,7 +61,6 @@ __global__ __launch_bounds__(256, KK > 32 ? 1 : 2) void k_topk_scan(const uint8_
                                                    const uint8_t* __restrict__ Xf, int nbn, int NRg,
                                                    float* __restrict__ cs, int* __restrict__ ci) {
   constexpr int MB = TN, RW = 64, CW = 64, MI = 2, NI = 2;
-  constexpr int ESZ = WF == W_BF16_ ? 2 : 1;
   constexpr int SP = TJ1 + 4;           // score tile pitch (floats)
   // K slice bytes (two work-groups per CU either way; 64 for E4M3 lists of 32, whose registers are
   // short for the larger staging)
@@ -81,8 +81,9 @@ __global__ __launch_bounds__(256, KK > 32 ? 1 : 2) void k_topk_scan(const uint8_
   if (r >= NRg) return;
   const int64_t ntile = (L + TJ1 - 1) / TJ1;
   const int64_t t0 = ntile * r / NRg, t1 = ntile * (r + 1) / NRg;
-  const int64_t rowbytes = (int64_t)D * ESZ;
-  const uint8_t* Xblk = Xf + (int64_t)nb * MB * rowbytes;
+  const int64_t rowbytes = w_row_bytes(WF, D);
+  // the block's feature rows: BF16 codes, or E4M3 codes for E4M3 and MXFP4 weights
+  const uint8_t* Xblk = Xf + (int64_t)nb * MB * D * (WF == W_BF16_ ? 2 : 1);
 
   float ls[KK]; int lj[KK];
   list_init<KK>(ls, lj);
@@ -95,7 +96,14 @@ __global__ __launch_bounds__(256, KK > 32 ? 1 : 2) void k_topk_scan(const uint8_
     const int64_t j0 = t * TJ1;
     const int nvalid = (int)((L - j0) < TJ1 ? (L - j0) : TJ1);
     f32x16_t acc[MI][NI];
-    fwd_tile<MB, WF, RW, CW, KS, KK <= 8>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj, [] {});
+    if constexpr (WF == W_MXFP4_) {
+      // (the tile's operands come straight from memory: the LDS staging area only holds scores)
+      __syncthreads();                  // the previous tile's score reads are done
+      mx_logit_tile<MI, NI>(acc, buffer_rsrc(Xblk, MB * D), wb * RW, D,
+                            buffer_rsrc(W + j0 * rowbytes, nvalid * (int)rowbytes), wj * CW, (int)rowbytes, l32, hi);
+    } else {
+      fwd_tile<MB, WF, RW, CW, KS, KK <= 8>(acc, smem, W + j0 * rowbytes, nvalid, Xblk, rowbytes, tid, wb, wj, [] {});
+    }
 
     if constexpr (KK <= 8) {
       // candidates: a score may enter its list only if the list's bound is NaN or not above it
@@ -273,7 +281,7 @@ TopkLayout topk_layout(int N, int D, int64_t L, int k, int wdtype) {
   s.ncand = (int64_t)s.NRg * s.MB * KK;
   size_t off = 0;
   s.xb = off; off = align256(off + (wdtype == W_BF16_ ? 2 * (size_t)s.MB * D : 0));
-  s.xq = off; off = align256(off + (wdtype == W_E4M3_ ? (size_t)s.MB * D : 0));
+  s.xq = off; off = align256(off + (wdtype != W_BF16_ ? (size_t)s.MB * D : 0));
   s.cand_s = off; off = align256(off + 4 * (size_t)s.ncand);
   s.cand_i = off; off = align256(off + 4 * (size_t)s.ncand);
   s.total = off;
@@ -290,8 +298,11 @@ static int topk_launch(const void* W, int wdtype, int64_t L, int D, int N, int k
   if (wdtype == W_BF16_)
     hipLaunchKernelGGL((k_topk_scan<W_BF16_, KK>), dim3(grid), dim3(256), 0, st, (const uint8_t*)W, L, D,
                        (const uint8_t*)(ws + s.xb), nbn, s.NRg, cs, ci);
-  else
+  else if (wdtype == W_E4M3_)
     hipLaunchKernelGGL((k_topk_scan<W_E4M3_, KK>), dim3(grid), dim3(256), 0, st, (const uint8_t*)W, L, D,
+                       (const uint8_t*)(ws + s.xq), nbn, s.NRg, cs, ci);
+  else
+    hipLaunchKernelGGL((k_topk_scan<W_MXFP4_, KK>), dim3(grid), dim3(256), 0, st, (const uint8_t*)W, L, D,
                        (const uint8_t*)(ws + s.xq), nbn, s.NRg, cs, ci);
   if (hipGetLastError() != hipSuccess) return ELMO_EHIP_;
   hipLaunchKernelGGL((k_topk_merge<KK>), dim3((N + 127) / 128), dim3(128), 0, st, cs, ci, N, s.MB, s.NRg, k, idx,
@@ -306,7 +317,7 @@ int run_topk(const void* W, int wdtype, int64_t L, int D, const void* X, int N, 
   const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
   hipLaunchKernelGGL(k_prep_eval_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)X, N, D, s.MB,
                      wdtype == W_BF16_ ? (uint16_t*)(ws + s.xb) : (uint16_t*)nullptr,
-                     wdtype == W_E4M3_ ? ws + s.xq : (uint8_t*)nullptr);
+                     wdtype != W_BF16_ ? ws + s.xq : (uint8_t*)nullptr);
   if (hipGetLastError() != hipSuccess) return ELMO_EHIP_;
   if (k <= 8) return topk_launch<8>(W, wdtype, L, D, N, k, idx, score, s, ws, st);
   if (k <= 32) return topk_launch<32>(W, wdtype, L, D, N, k, idx, score, s, ws, st);

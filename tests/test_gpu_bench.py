@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_json_line_on_the_tiny_workload():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3", "--warmup", "1",
            "--topk-n", "64", "--kahan-params", "100000", "--cpu-seconds", "0.3", "--second-workload", "bf16_131k",
-           "--steps-8p6m", "2"]
+           "--steps-8p6m", "2", "--third-workload", "mxfp4_131k", "--steps-third", "2"]
     print("  " + " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -45,3 +45,8 @@ def test_bench_json_line_on_the_tiny_workload():
     # (B = 256, BF16: the backward moves 2 D w = 3,072 bytes per 786,432 flops, 256 flop/B: below the ridge)
     assert s2["roofline"]["bound"] == "hbm" and s2["roofline"]["launches"] == 2 * 4
     assert s2["cpu_baseline"]["value"] > 0 and s2["topk"]["ms"] > 0 and s2["peak_hbm_bytes"] > 0
+    s3 = d["mxfp4_131k"]
+    assert s3["config"]["weights"] == "mxfp4" and s3["samples_s"] > 0 and s3["topk"]["ms"] > 0
+    # (B = 256, MXFP4: the backward moves 2 * 17 D / 32 bytes per 4 B D flops, 964 flop/B: above the
+    # BF16 ridge point; the forward's kernel is the scaled-MFMA one)
+    assert s3["roofline"]["bound"] == "mfma" and s3["roofline"]["other_kernel"]["kernel"] == "k_fwd_mx"

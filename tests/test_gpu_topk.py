@@ -29,7 +29,7 @@ def _check(elmo, orc, wfmt, W0, Wd, X, idx_g, sc_g, k, label=""):
     device's and the oracle's logits over all labels giving each row's measured error."""
     idx_r, sc_r = orc.topk(wfmt, W0, X, k)
     Zr = orc.logits(wfmt, W0, X, np.arange(W0.shape[0]))
-    Zg = np.concatenate([elmo.logits(Wd, _xdev(X[r:r + 256]), 0, W0.shape[0]).cpu().numpy()
+    Zg = np.concatenate([elmo.logits(Wd, _xdev(X[r:r + 256]), 0, W0.shape[0], wfmt=wfmt).cpu().numpy()
                          for r in range(0, X.shape[0], 256)])      # (the forward takes up to 256 rows)
     return check_topk_rows(idx_g, sc_g, idx_r, sc_r, Zg, Zr, label=label)
 
@@ -38,14 +38,16 @@ def _check(elmo, orc, wfmt, W0, Wd, X, idx_g, sc_g, k, label=""):
                                           (129, 768, 3000, 1, wk.W_BF16), (64, 192, 2000, 32, wk.W_BF16),
                                           (257, 256, 4099, 8, wk.W_E4M3), (4, 64, 40, 32, wk.W_E4M3),
                                           (70, 128, 3000, 64, wk.W_BF16), (130, 256, 2000, 64, wk.W_E4M3),
-                                          (3, 64, 64, 64, wk.W_BF16)])
+                                          (3, 64, 64, 64, wk.W_BF16), (300, 256, 5000, 5, wk.W_MXFP4),
+                                          (129, 768, 3000, 32, wk.W_MXFP4), (70, 512, 2000, 64, wk.W_MXFP4),
+                                          (1, 256, 130, 8, wk.W_MXFP4)])
 def test_topk_matches_oracle(elmo, orc, N, D, L, k, wfmt):
     wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
     W0 = wk.make_weights(wl)
     X = wk.make_eval_x(wl, N)
     print(f"  topk N={N} D={D} L={L} k={k} wfmt={wfmt}", flush=True)
     Wd = to_dev_codes(W0)
-    idx, sc = elmo.topk(Wd, _xdev(X), k)
+    idx, sc = elmo.topk(Wd, _xdev(X), k, wfmt=wfmt)
     torch.cuda.synchronize()
     _check(elmo, orc, wfmt, W0, Wd, X, idx.cpu().numpy(), sc.cpu().numpy(), k)
 
@@ -88,14 +90,14 @@ def test_topk_nan_scores_rank_last(elmo, orc):
     assert np.array_equal(idx.cpu().numpy(), idx_r)
 
 
-@pytest.mark.parametrize("wfmt", [wk.W_BF16, wk.W_E4M3])
-def test_topk_many_tiles_per_range(elmo, orc, wfmt):
+@pytest.mark.parametrize("wfmt,D", [(wk.W_BF16, 64), (wk.W_E4M3, 64), (wk.W_MXFP4, 256)])
+def test_topk_many_tiles_per_range(elmo, orc, wfmt, D):
     """4096 queries over 60k labels: each work-group scans some 30 label tiles, so the lists fill
     and later tiles take the bounded-candidate path (lists of up to 8). Its top-8 must equal, bit for
     bit, the first 8 of the top-32, and the top-32 the first 32 of the top-64 (lists of 32 and 64
     always take the full score-tile path); sampled queries must match the oracle. Duplicated weight
     rows across tiles force exact ties."""
-    N, D, L = 4096, 64, 60000
+    N, L = 4096, 60000
     wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
     W0 = wk.make_weights(wl).copy()
     for a, b in [(5, 40000), (12345, 129), (59999, 0), (777, 778)]:
@@ -103,14 +105,14 @@ def test_topk_many_tiles_per_range(elmo, orc, wfmt):
     X = wk.make_eval_x(wl, N)
     Wd, Xd = to_dev_codes(W0), _xdev(X)
     print(f"  topk N={N} D={D} L={L} wfmt={wfmt}", flush=True)
-    i8, s8 = elmo.topk(Wd, Xd, 8)
-    i32, s32 = elmo.topk(Wd, Xd, 32)
+    i8, s8 = elmo.topk(Wd, Xd, 8, wfmt=wfmt)
+    i32, s32 = elmo.topk(Wd, Xd, 32, wfmt=wfmt)
     i8, s8, i32, s32 = i8.cpu().numpy(), s8.cpu().numpy(), i32.cpu().numpy(), s32.cpu().numpy()
     assert np.array_equal(i32[:, :8], i8)
     assert np.array_equal(s32[:, :8].view(np.uint32), s8.view(np.uint32))
     qs = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4094, 4095], np.random.default_rng(9).integers(0, N, 25)]))
     _check(elmo, orc, wfmt, W0, Wd, X[qs], i8[qs], s8[qs], 8)
-    i64, s64 = elmo.topk(Wd, Xd, 64)
+    i64, s64 = elmo.topk(Wd, Xd, 64, wfmt=wfmt)
     i64, s64 = i64.cpu().numpy(), s64.cpu().numpy()
     assert np.array_equal(i64[:, :32], i32)
     assert np.array_equal(s64[:, :32].view(np.uint32), s32.view(np.uint32))

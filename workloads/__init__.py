@@ -72,6 +72,8 @@ WORKLOADS = {
     # the FP4 weights the pages leave open (with micro-tensor scaling), at the 3M-label head's shape
     "mxfp4_3m": Workload("xmc-mxfp4-L3000000-D768-B256", 256, 768, 3000000, 131072, W_MXFP4, 0.1, 10,
                          "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=5),
+    "mxfp4_131k": Workload("xmc-mxfp4-L131072-D768-B256", 256, 768, 131072, 32768, W_MXFP4, 0.1, 10,
+                           "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=6),
 }
 
 
