@@ -264,7 +264,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
 }
 
 // ------------------------------------------------------------------------------------------------
-// forward + gradient with the features stationary in registers (E4M3 weights, 256 samples, D = 768)
+// forward + gradient with the features stationary in registers (E4M3 or MXFP4 weights, 256
+// samples, D = 768)
 // ------------------------------------------------------------------------------------------------
 // The tiled forward above reloads every feature row for every 128-label tile and waits on those
 // loads in each K slice. Here each work-group holds all 256 E4M3 feature rows in registers for the
@@ -279,10 +280,23 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
 // work overlaps the other's epilogue arithmetic. One barrier per iteration. The positives of tile
 // i + 1 are gathered into label bits during iteration i (four buffers: A reads tile i's, B tile
 // i - 1's, i + 1's is being filled and i + 2's cleared).
+// MXFP4 weights: a tile's 64 rows (17 D / 32 bytes each) are contiguous in memory and 16-byte
+// aligned, so they are loaded as one flat run of 16-byte chunks and written to LDS in 8-byte halves
+// (which never straddle a row) at a row pitch of 432 bytes (108 banks: 16 consecutive rows' 16-byte
+// fragment reads fall on distinct banks). Per MFMA a lane reads its 16 code bytes; the 24 scale
+// bytes of its row are read once per tile and permuted so that dword m holds the lane's scales of
+// K steps 4m .. 4m + 3, each selected by the instruction's byte select. The features take the E4M3
+// operand's K order beside an FP4 operand.
 constexpr int XS_TJ = 64;                                      // labels per tile
 
+template <int OPSEL_B>
+__device__ __forceinline__ f32x16_t mfma_e4m3_fp4_sel(i32x8_t a, i32x4_t b, f32x16_t c, int scale_b) {
+  const i32x8_t bv = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bv, c, 0, 4, 0, 127, OPSEL_B, scale_b);
+}
+
 // NK: 64-byte K steps of the FP8 MFMA (D = 64 NK; the features take 8 NK registers)
-template <int NK, bool LOSS, bool ZOUT>
+template <int WF, int NK, bool LOSS, bool ZOUT>
 __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq,
                                                 int D, int64_t c0, int clen,
                                                 const uint32_t* __restrict__ tile_off,
@@ -292,10 +306,16 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
                                                 float* __restrict__ Z, uint16_t* __restrict__ Gout,
                                                 int64_t zpitch, int64_t zoff) {
   constexpr int MB = 256;
+  constexpr bool MX = WF == W_MXFP4_;
   constexpr int D_ = 64 * NK;
-  constexpr int PITCH = D_ + 16;                      // LDS row pitch: 16 consecutive rows on distinct banks
-  constexpr int PPR = D_ / 16;                        // 16-byte parts per weight row
-  constexpr int CPT = (XS_TJ * PPR + 511) / 512;      // 16-byte weight chunks per thread and tile
+  constexpr int RB = MX ? D_ / 2 + D_ / 32 : D_;     // bytes per weight row
+  static_assert(!MX || (XS_TJ * RB) % 16 == 0, "MXFP4 tiles are whole 16-byte chunks");
+  // LDS row pitch: 16 consecutive rows on distinct banks for the 16-byte fragment reads
+  constexpr int PITCH = MX ? 432 : D_ + 16;
+  static_assert(PITCH >= RB && (PITCH / 4) % 8 == 4, "pitch: whole rows, an odd number of 4-bank groups");
+  constexpr int PPR = D_ / 16;                        // (E4M3) 16-byte parts per weight row
+  constexpr int NCH = MX ? XS_TJ * RB / 16 : XS_TJ * PPR;   // 16-byte chunks per tile
+  constexpr int CPT = (NCH + 511) / 512;              // 16-byte weight chunks per thread and tile
   __shared__ __attribute__((aligned(16))) uint8_t Ws[3][XS_TJ * PITCH];
   __shared__ uint32_t ybits[4][XS_TJ * (MB / 32)];   // label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[8];
@@ -309,25 +329,41 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   const int nmy = ntl > (int)blockIdx.x ? (ntl - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   auto tile_of = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
   (void)D;
-  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)D_, clen * D_);
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)RB, clen * RB);
   constexpr int OOB = 0x7ffffff0;
 
   // weight tile staging through registers: chunk c of this thread is ci = tid + 512 c, row ci / PPR,
-  // part ci % PPR; rows past the chunk read as zero (resource bound), chunks past the tile are idle
+  // part ci % PPR (E4M3), or bytes 16 ci .. 16 ci + 15 of the tile's flat rows (MXFP4); rows past
+  // the chunk read as zero (resource bound), chunks past the tile are idle
   i32x4_t stg[CPT];
   auto wload = [&](int t) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + 512 * c, row = ci / PPR, part = ci % PPR;
-      const bool in = row < XS_TJ;
-      stg[c] = buffer_load16(wres, in ? (t * XS_TJ + row) * D_ + part * 16 : OOB);
+      const int ci = tid + 512 * c;
+      if constexpr (MX) {
+        stg[c] = buffer_load16(wres, ci < NCH ? t * XS_TJ * RB + ci * 16 : OOB);
+      } else {
+        const int row = ci / PPR, part = ci % PPR;
+        stg[c] = buffer_load16(wres, row < XS_TJ ? (t * XS_TJ + row) * D_ + part * 16 : OOB);
+      }
     }
   };
   auto wstore = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + 512 * c, row = ci / PPR, part = ci % PPR;
-      if (row < XS_TJ) *(i32x4_t*)(&Ws[buf][row * PITCH + part * 16]) = stg[c];
+      const int ci = tid + 512 * c;
+      if constexpr (MX) {
+        if (ci < NCH) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int b = ci * 16 + 8 * h, row = b / RB, off = b - row * RB;
+            *(i32x2_t*)(&Ws[buf][row * PITCH + off]) = i32x2_t{stg[c][2 * h], stg[c][2 * h + 1]};
+          }
+        }
+      } else {
+        const int row = ci / PPR, part = ci % PPR;
+        if (row < XS_TJ) *(i32x4_t*)(&Ws[buf][row * PITCH + part * 16]) = stg[c];
+      }
     }
   };
   // positives of tile t (64 labels: half (c0 / 64 + t) & 1 of 128-label bucket tile (c0 / 64 + t) >> 1)
@@ -356,10 +392,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   if (nmy > 0) yscan(tile_of(0), 0);
   i32x8_t xf[NK];
   {
-    const uint8_t* xr = Xq + (int64_t)(bb + l32) * D_ + hi * 32;
+    // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15
+    const uint8_t* xr = Xq + (int64_t)(bb + l32) * D_ + (MX ? hi * 16 : hi * 32);
+    constexpr int O2 = MX ? 32 : 16;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const i32x4_t a0 = *(const i32x4_t*)(xr + kk * 64), a1 = *(const i32x4_t*)(xr + kk * 64 + 16);
+      const i32x4_t a0 = *(const i32x4_t*)(xr + kk * 64), a1 = *(const i32x4_t*)(xr + kk * 64 + O2);
       xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
   }
@@ -369,7 +407,38 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   float lsum = 0.0f;
   // the tile's 2 NK MFMAs (slot z: K step z / 2, label block z % 2), each slot's weight fragment read
   // from LDS two slots ahead; a scheduling fence closes every slot so that the reads stay spread
+  auto mfmas_mx = [&](int buf) {
+    acc[0] = f32x16_t{}; acc[1] = f32x16_t{};
+    const uint8_t* wb = &Ws[buf][l32 * PITCH + hi * 16];
+    // scale dword m of label block ni: bytes 2 (4m + j) + hi of the row's scales, j = 0..3
+    uint32_t scl[2][NK / 4];
+    static_assert(NK % 4 == 0, "whole scale dwords");
+    const uint32_t psel = hi ? 0x07050301u : 0x06040200u;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const uint8_t* sp = wb - hi * 16 + ni * 32 * PITCH + D_ / 2;
+#pragma unroll
+      for (int m = 0; m < NK / 4; ++m) {
+        const i32x2_t r = *(const i32x2_t*)(sp + 8 * m);
+        scl[ni][m] = __builtin_amdgcn_perm((uint32_t)r[1], (uint32_t)r[0], psel);
+      }
+    }
+    auto rd = [&](int z) { return *(const i32x4_t*)(wb + (z & 1) * 32 * PITCH + (z >> 1) * 32); };
+    constexpr int NS = 2 * NK;
+    i32x4_t f[3];
+    f[0] = rd(0); f[1] = rd(1);
+    static_for<0, NS>([&](auto Z) {
+      constexpr int z = decltype(Z)::value, kk = z >> 1;
+      if constexpr (z + 2 < NS) f[(z + 2) % 3] = rd(z + 2);
+      acc[z & 1] = mfma_e4m3_fp4_sel<kk % 4>(xf[kk], f[z % 3], acc[z & 1], (int)scl[z & 1][kk / 4]);
+      sched_fence();
+    });
+  };
   auto mfmas = [&](int buf) {
+    if constexpr (MX) {
+      mfmas_mx(buf);
+      return;
+    }
     acc[0] = f32x16_t{}; acc[1] = f32x16_t{};
     const uint8_t* wb = &Ws[buf][l32 * PITCH + hi * 32];
     auto rd = [&](int z) {
@@ -1006,7 +1075,7 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
   const int64_t l_end = a.l1;
   // the forward with the features stationary in registers where it is built (E4M3, 256 padded
   // samples, D = 768); the tiled forward elsewhere
-  constexpr bool XS_OK = MB == 256 && WF == W_E4M3_;
+  constexpr bool XS_OK = MB == 256 && (WF == W_E4M3_ || WF == W_MXFP4_);
   const bool xs = XS_OK && a.D == 768;
   for (int64_t c0 = a.l0; c0 < l_end; c0 += s.Cc) {
     const int clen = (int)((l_end - c0) < s.Cc ? (l_end - c0) : s.Cc);
@@ -1017,7 +1086,7 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
       constexpr bool L_ = decltype(LOSS)::value, Z_ = decltype(ZOUT)::value;
       if constexpr (XS_OK) {
         if (xs) {
-          hipLaunchKernelGGL((k_fwd_xs<12, L_, Z_>), dim3(gx), dim3(512), 0, st, W, ws + s.xq, a.D, c0, clen, toff,
+          hipLaunchKernelGGL((k_fwd_xs<WF, 12, L_, Z_>), dim3(gx), dim3(512), 0, st, W, ws + s.xq, a.D, c0, clen, toff,
                              bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
           return;
         }
