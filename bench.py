@@ -60,7 +60,84 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times) and exit: the "
                          "known-size reference for scaling HBM byte counters")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="no GPU: print the markdown kernel-time table of a rocprofv3 --stats output folder")
+    ap.add_argument("--summarize-traffic", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                              "COPY_WRITE_DIR"),
+                    help="no GPU: print the HBM-bytes-per-launch file (the format bench.py reads for "
+                         "roofline.traffic) from four rocprofv3 --pmc output folders")
     return ap.parse_args()
+
+
+# ---- summaries of rocprofv3 output (CSV), written into profiles/ --------------------------------
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    return rows
+
+
+def summarize_stats(folder):
+    """Markdown table of a --kernel-trace --stats run: calls, total and average time per kernel."""
+    rows = _csv_rows(folder, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| kernel | calls | total ms | average us | share % |")
+    print("|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"] if len(r["Name"]) <= 70 else r["Name"][:67] + "..."
+        t = float(r["TotalDurationNs"])
+        print(f"| `{name}` | {r['Calls']} | {t / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.2f} | {100 * t / total:.2f} |")
+
+
+def _counter_per_kernel(folder, counter):
+    """{kernel template name: (mean KiB per dispatch, dispatches)} of one counter's pass."""
+    per = {}
+    for r in _csv_rows(folder, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        name = name.split("(")[0].replace("elmo::", "").replace(" ", "")
+        v = per.setdefault(name, {})
+        key = r["Dispatch_Id"]
+        v[key] = v.get(key, 0.0) + float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """The HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a plain copy of known size (read and written once)."""
+    def copy_factor(folder, counter):
+        per = _counter_per_kernel(folder, counter)
+        kib, _ = max(per.values(), key=lambda v: v[0])         # the copy kernel dominates the run
+        return kib, (1 << 30) / 1024 / kib
+    cf, ff = copy_factor(copy_fetch_dir, "FETCH_SIZE")
+    cw, fw = copy_factor(copy_write_dir, "WRITE_SIZE")
+    import workloads as wk
+    print(f"# HBM bytes per launch, workload {wk.WORKLOADS[workload].name}")
+    print("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from one rocprofv3 pass each, scaled by what the same")
+    print("# counter reads for a plain 1 GiB device copy (1048576 KiB read and written per launch).")
+    print("# commands (from the repository root on the GPU box):")
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 2 "
+              f"--warmup 1 --no-cpu-baseline --no-topk --no-kahan --second-workload none --third-workload none "
+              f"--workload {workload}")
+    for c, d in (("FETCH_SIZE", copy_fetch_dir), ("WRITE_SIZE", copy_write_dir)):
+        print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
+              f"--copy-bytes 1073741824")
+    print(f"#   python3 bench.py --summarize-traffic {workload} {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}")
+    print(f"source_sha256 {kernel_source_hash()}")
+    print(f"copy_fetch_size_kib {cf:.1f} factor {ff:.4f}")
+    print(f"copy_write_size_kib {cw:.1f} factor {fw:.4f}")
+    for counter, folder, f, tag in (("FETCH_SIZE", fetch_dir, ff, "fetch_size_kib"),
+                                    ("WRITE_SIZE", write_dir, fw, "write_size_kib")):
+        for k, (kib, n) in sorted(_counter_per_kernel(folder, counter).items()):
+            if k.startswith("k_") or k.startswith("elmo"):
+                print(f"{k} {tag} {kib:.1f} bytes {int(kib * 1024 * f)} dispatches {n}")
 
 
 def kahan_bench(n, stream):
@@ -401,6 +478,12 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: runs on exactly one GPU (--gpus 1); multi-GPU runs are not implemented",

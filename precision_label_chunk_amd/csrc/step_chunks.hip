@@ -336,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   // part ci % PPR (E4M3), or bytes 16 ci .. 16 ci + 15 of the tile's flat rows (MXFP4); rows past
   // the chunk read as zero (resource bound), chunks past the tile are idle
   i32x4_t stg[CPT];
-  auto wload = [&](int t) {
+  auto wload = [&](int t, i32x4_t (&stg)[CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ci = tid + 512 * c;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
       }
     }
   };
-  auto wstore = [&](int buf) {
+  auto wstore = [&](int buf, const i32x4_t (&stg)[CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ci = tid + 512 * c;
@@ -384,12 +384,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
     }
   };
 
-  // prologue: tiles 0 and 1 into LDS, tile 0's positives, the stationary feature fragments
-  if (nmy > 0) { wload(tile_of(0)); wstore(0); }
-  if (nmy > 1) { wload(tile_of(1)); wstore(1); }
-  yclear(0); yclear(1); yclear(2);
-  __syncthreads();
-  if (nmy > 0) yscan(tile_of(0), 0);
+  // prologue: the stationary feature fragments and tiles 0 and 1 loaded together (one memory
+  // latency, not three in a row; a tile this work-group does not have lies past the chunk and
+  // reads as zero), the tiles into LDS, then tile 0's positives
   i32x8_t xf[NK];
   {
     // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15
@@ -401,6 +398,16 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
       xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
   }
+  {
+    i32x4_t stg1[CPT];
+    wload(tile_of(0), stg);
+    wload(tile_of(1), stg1);
+    yclear(0); yclear(1); yclear(2);
+    wstore(0, stg);
+    wstore(1, stg1);
+  }
+  __syncthreads();
+  if (nmy > 0) yscan(tile_of(0), 0);
   __syncthreads();
 
   f32x16_t acc[2];
@@ -497,15 +504,15 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   constexpr bool LATE_STORE = !ZOUT;
   for (int i = 0; i <= nmy; ++i) {
     if (i + 2 < nmy) {
-      wload(tile_of(i + 2));
-      if constexpr (!LATE_STORE) wstore((i + 2) % 3);
+      wload(tile_of(i + 2), stg);
+      if constexpr (!LATE_STORE) wstore((i + 2) % 3, stg);
     }
     // group A: MFMAs of tile i, then its epilogue; group B: epilogue of tile i - 1, then MFMAs of tile i
     const int ie = i - grp;                           // the tile index whose epilogue this wave runs
     if (grp == 0 && i < nmy) mfmas(i % 3);
     if (ie >= 0 && ie < nmy) epilogue(tile_of(ie), ie & 3);
     if (grp == 1 && i < nmy) mfmas(i % 3);
-    if constexpr (LATE_STORE) if (i + 2 < nmy) wstore((i + 2) % 3);
+    if constexpr (LATE_STORE) if (i + 2 < nmy) wstore((i + 2) % 3, stg);
     if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
     yclear((i + 2) & 3);
     __syncthreads();

@@ -46,7 +46,8 @@ def test_status_strings_and_version(L):
 
 @pytest.mark.parametrize("B,D,Lab,chunk,wd", [(0, 768, 1000, 128, 0), (257, 768, 1000, 128, 0), (4, 96, 1000, 128, 0),
                                               (4, 2048, 1000, 128, 0), (4, 768, 0, 128, 0), (4, 768, 1000, 0, 0),
-                                              (4, 768, 1000, 128, 7), (4, 768, 2**31, 128, 0)])
+                                              (4, 768, 1000, 128, 7), (4, 768, 2**31, 128, 0),
+                                              (4, 192, 1000, 128, 2), (4, 640, 1000, 128, 2)])   # MXFP4: D % 256
 def test_workspace_query_rejects_bad_shapes(L, B, D, Lab, chunk, wd):
     assert L.elmo_xmc_step_workspace_bytes(B, D, Lab, chunk, wd, 10) == 0
 
@@ -67,6 +68,9 @@ def test_step_rejects_invalid_arguments_before_launch(L):
     assert L.elmo_xmc_step(q, 0, 1000, 128, p, 4, p, p, 1, 0.1, 0, 0, 128, p, null, p, 1 << 30, null) == -1
     # workspace too small (validation precedes any device work)
     assert L.elmo_xmc_step(p, 0, 1000, 128, p, 4, p, p, 1, 0.1, 0, 0, 128, p, null, p, 16, null) == -4
+    # MXFP4 rows need D % 256 == 0
+    assert L.elmo_xmc_step(p, 2, 1000, 192, p, 4, p, p, 1, 0.1, 0, 0, 128, p, null, p, 1 << 30, null) == -2
+    assert L.elmo_xmc_step_workspace_bytes(4, 256, 1000, 128, 2, 10) > 0
 
 
 def test_topk_rejects_invalid_arguments(L):
@@ -76,6 +80,8 @@ def test_topk_rejects_invalid_arguments(L):
     assert L.elmo_xmc_topk(null, 0, 10, 128, null, 4, 11, null, null, null, 0, null) == -2
     assert L.elmo_xmc_topk(null, 0, 1000, 128, null, 4, 5, null, null, null, 0, null) == -1
     assert L.elmo_xmc_topk_workspace_bytes(4, 128, 1000, 0, 0) == 0
+    assert L.elmo_xmc_topk_workspace_bytes(4, 128, 1000, 5, 2) == 0       # MXFP4 with D % 256 != 0
+    assert L.elmo_xmc_topk(null, 2, 1000, 128, null, 4, 5, null, null, null, 0, null) == -2
 
 
 def test_numerics_probe_rejects_bad_op(L):

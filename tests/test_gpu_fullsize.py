@@ -9,8 +9,9 @@ import pytest
 import torch
 
 import workloads as wk
-from tests._helpers import (RTOL, assert_close, assert_grad_codes_match, assert_weights_free_running, batch_to_dev,
-                            check_topk_rows, weight_report)
+from tests._helpers import (RTOL, assert_close, assert_grad_codes_match, assert_weights_free_running,
+                            assert_weights_free_running_mx, batch_to_dev, check_topk_rows, mx_weight_report,
+                            weight_report)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -35,7 +36,7 @@ def _sample_labels(wl, n_random=24):
     return js.astype(np.int64)
 
 
-@pytest.mark.parametrize("name", ["bf16_131k", "bf16_670k", "e4m3_3m", "bf16_8p6m"])
+@pytest.mark.parametrize("name", ["bf16_131k", "bf16_670k", "e4m3_3m", "bf16_8p6m", "mxfp4_3m"])
 def test_full_size_step_sampled(elmo, orc, name):
     wl = wk.WORKLOADS[name]
     dev = torch.device("cuda:0")
@@ -51,13 +52,13 @@ def test_full_size_step_sampled(elmo, orc, name):
     Zg = np.empty((B, js.size), np.float32)
     Gg = np.empty((B, js.size), np.uint16)
     for i, j in enumerate(js):
-        z, gcol = elmo.forward(W, X, rp, ids, int(j), int(j) + 1)
+        z, gcol = elmo.forward(W, X, rp, ids, int(j), int(j) + 1, wfmt=wl.wfmt)
         Zg[:, i] = z.cpu().numpy()[:, 0]
         Gg[:, i] = gcol.cpu().numpy().view(np.uint16)[:, 0]
     Zr = orc.logits(wl.wfmt, W0, bt.X, js)
     ez = assert_close(Zg, Zr, RTOL[wl.wfmt])
 
-    dX, _ = elmo.step(W, X, rp, ids, wl.lr, wl.seed, 0, wl.chunk)
+    dX, _ = elmo.step(W, X, rp, ids, wl.lr, wl.seed, 0, wl.chunk, wfmt=wl.wfmt)
     torch.cuda.synchronize()
     Wg = _host_codes(W[torch.from_numpy(js).to(dev)])
     assert elmo.step_flags(elmo.last_workspace) == 0
@@ -66,10 +67,14 @@ def test_full_size_step_sampled(elmo, orc, name):
     Wf, Gr, Tf = orc.update_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, wl.lr, wl.seed, 0, js, want_detail=True)
     flips = assert_grad_codes_match(Gg, Gr)
     R = np.stack([orc.r16(wl.seed, 0, int(j) * wl.D, wl.D) for j in js])
-    c = assert_weights_free_running(orc, Wg, Wf, Tf, R, wl.wfmt, bt.X, Gg, Gr, wl.lr, label=f" ({js.size} rows)")
+    if wl.wfmt == wk.W_MXFP4:
+        c = assert_weights_free_running_mx(orc, Wg, Wf, Tf, R, bt.X, Gg, Gr, wl.lr, label=f" ({js.size} rows)")
+    else:
+        c = assert_weights_free_running(orc, Wg, Wf, Tf, R, wl.wfmt, bt.X, Gg, Gr, wl.lr, label=f" ({js.size} rows)")
     eq = c["equal"] / c["n"]
     # diagnostic: the oracle's weight half on the device's own gradient codes (the update kernel alone)
-    eq_tf = weight_report(Wg, orc.update_rows_from_g(wl.wfmt, W0, bt.X, Gg, wl.lr, wl.seed, 0, js), wl.wfmt)[0]
+    Wtf = orc.update_rows_from_g(wl.wfmt, W0, bt.X, Gg, wl.lr, wl.seed, 0, js)
+    eq_tf = mx_weight_report(Wg, Wtf)[0] if wl.wfmt == wk.W_MXFP4 else weight_report(Wg, Wtf, wl.wfmt)[0]
     assert eq_tf >= 0.999, f"weights given the device's gradient codes only {eq_tf:.6f} equal"
 
     # dX rows: sums over every label
@@ -80,7 +85,7 @@ def test_full_size_step_sampled(elmo, orc, name):
           flush=True)
 
 
-@pytest.mark.parametrize("name", ["e4m3_3m", "bf16_8p6m"])
+@pytest.mark.parametrize("name", ["e4m3_3m", "bf16_8p6m", "mxfp4_3m"])
 @pytest.mark.timeout(900)
 def test_full_size_topk_sampled_queries(elmo, orc, name):
     """Top-k over all labels of the full weight matrix for N = 1024 held-out queries in one call; 64 of
@@ -94,11 +99,11 @@ def test_full_size_topk_sampled_queries(elmo, orc, name):
     Xe = wk.make_eval_x(wl, N)
     print(f"  {wl.name}: top-{k} of N={N}", flush=True)
     Xd = torch.from_numpy(Xe.view(np.int16)).to(dev)
-    idx, score = elmo.topk(W, Xd, k)
+    idx, score = elmo.topk(W, Xd, k, wfmt=wl.wfmt)
     idx = idx.cpu().numpy(); score = score.cpu().numpy()
     qs = np.unique(np.concatenate([[0, 1, 127, 128, 511, 512, N - 2, N - 1],
                                    np.random.default_rng(77).choice(N, 56, replace=False)]))[:64]
-    Zg = elmo.logits(W, Xd[torch.from_numpy(qs).to(dev)], 0, wl.L).cpu().numpy()
+    Zg = elmo.logits(W, Xd[torch.from_numpy(qs).to(dev)], 0, wl.L, wfmt=wl.wfmt).cpu().numpy()
     W0 = _host_codes(W)
     del W
     torch.cuda.empty_cache()

@@ -20,16 +20,17 @@ def elmo():
 
 
 def _both(elmo, B, D, L, chunk, wfmt, seed):
-    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=B, D=D, L=L, wfmt=wfmt, lam=5.0, seed=seed)
+    base = "mxfp4_3m" if wfmt == wk.W_MXFP4 else "bf16_131k"
+    wl = wk.scaled(wk.WORKLOADS[base], B=B, D=D, L=L, wfmt=wfmt, lam=5.0, seed=seed)
     W0, bt = wk.make_weights(wl), wk.make_batch(wl)
     X, rp, ids = batch_to_dev(bt)
     print(f"  noalloc vs workspace step: B={B} D={D} L={L} chunk={chunk} wfmt={wfmt}", flush=True)
     Wa = to_dev_codes(W0)
-    dXa, la = elmo.step(Wa, X, rp, ids, 0.05, 9, 4, chunk, want_loss=True)
+    dXa, la = elmo.step(Wa, X, rp, ids, 0.05, 9, 4, chunk, want_loss=True, wfmt=wfmt)
     Wb = to_dev_codes(W0)
     dXb = torch.empty((B, D), dtype=torch.float32, device="cuda")
     lb = torch.empty((1,), dtype=torch.float32, device="cuda")
-    elmo.step_noalloc(Wb, X, rp, ids, 0.05, 9, 4, chunk, dXb, lb)
+    elmo.step_noalloc(Wb, X, rp, ids, 0.05, 9, 4, chunk, dXb, lb, wfmt=wfmt)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev_codes(Wa), from_dev_codes(Wb))
     assert np.array_equal(dXa.cpu().numpy(), dXb.cpu().numpy())
@@ -37,10 +38,11 @@ def _both(elmo, B, D, L, chunk, wfmt, seed):
     assert not np.array_equal(from_dev_codes(Wb), W0)
 
 
-@pytest.mark.parametrize("wfmt", [wk.W_E4M3, wk.W_BF16])
+@pytest.mark.parametrize("wfmt", [wk.W_E4M3, wk.W_BF16, wk.W_MXFP4])
 def test_noalloc_step_equals_workspace_step_twice(elmo, wfmt):
     _both(elmo, 256, 768, 20000, 8192, wfmt, seed=1)       # the larger call first
-    _both(elmo, 37, 128, 3000, 1024, wfmt, seed=2)         # then a smaller one over the same scratch
+    # then a smaller one over the same scratch (MXFP4 rows need D % 256 == 0)
+    _both(elmo, 37, 256 if wfmt == wk.W_MXFP4 else 128, 3000, 1024, wfmt, seed=2)
 
 
 def test_noalloc_rejects_steps_beyond_the_scratch(elmo):
