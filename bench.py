@@ -62,6 +62,9 @@ def parse():
                          "known-size reference for scaling HBM byte counters")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="no GPU: print the markdown kernel-time table of a rocprofv3 --stats output folder")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="no GPU: print the per-dispatch table of every counter in these rocprofv3 --pmc output "
+                         "folders for the step's chunk kernels")
     ap.add_argument("--summarize-traffic", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                               "COPY_WRITE_DIR"),
                     help="no GPU: print the HBM-bytes-per-launch file (the format bench.py reads for "
@@ -89,7 +92,9 @@ def summarize_stats(folder):
     print("| kernel | calls | total ms | average us | share % |")
     print("|---|---|---|---|---|")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"] if len(r["Name"]) <= 70 else r["Name"][:67] + "..."
+        name = r["Name"].split("(")[0].strip()
+        name = name[5:] if name.startswith("void ") else name
+        name = name if len(name) <= 70 else name[:67] + "..."
         t = float(r["TotalDurationNs"])
         print(f"| `{name}` | {r['Calls']} | {t / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.2f} | {100 * t / total:.2f} |")
 
@@ -100,12 +105,42 @@ def _counter_per_kernel(folder, counter):
     for r in _csv_rows(folder, "counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
-        name = r["Kernel_Name"]
-        name = name.split("(")[0].replace("elmo::", "").replace(" ", "")
+        name = _kernel_key(r["Kernel_Name"])
         v = per.setdefault(name, {})
         key = r["Dispatch_Id"]
         v[key] = v.get(key, 0.0) + float(r["Counter_Value"])
     return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def summarize_counters(folders):
+    """Markdown table: every counter of the passes (rows) per chunk kernel (columns), as the mean
+    over its dispatches of the device-wide sum per dispatch."""
+    table = {}
+    for folder in folders:
+        for r in _csv_rows(folder, "counter_collection.csv"):
+            name = _kernel_key(r["Kernel_Name"])
+            if not (name.startswith("k_bwd_update") or name.startswith("k_fwd")):
+                continue
+            d = table.setdefault(r["Counter_Name"], {}).setdefault(name, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    kernels = sorted({k for v in table.values() for k in v})
+    print("| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |")
+    print("|---|" + "---|" * len(kernels))
+    for c in sorted(table):
+        cells = []
+        for k in kernels:
+            v = table[c].get(k)
+            cells.append(f"{sum(v.values()) / len(v):.4g}" if v else "")
+        print(f"| {c} | " + " | ".join(cells) + " |")
+
+
+def _kernel_key(name):
+    """'k_name<args>' from a demangled kernel name (return type, namespace, parameters and spaces
+    dropped)."""
+    name = name.split("(")[0].strip()
+    if name.startswith("void "):
+        name = name[5:]
+    return name.replace("elmo::", "").replace(" ", "")
 
 
 def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
@@ -480,6 +515,9 @@ def main():
     args = parse()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
