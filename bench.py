@@ -440,6 +440,7 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     kd = kern[dom]
     # the forward kernel the launcher picks for this workload
     fwd_kernel = ("k_fwd_xs" if wl.wfmt != wk.W_BF16 and D == 768 and B > 128 else
+                  "k_fwd_xb" if wl.wfmt == wk.W_BF16 and D == 768 and 64 < B <= 128 else
                   "k_fwd_mx" if wl.wfmt == wk.W_MXFP4 else "k_fwd_g")
     kname = {"bwd": "k_bwd_update", "fwd": fwd_kernel}
     scale = 1e9 if kd["unit"] == "GB/s" else 1e12

@@ -1,5 +1,6 @@
-// Device numerics for the XMC head step on gfx950: BF16 and OCP-E4M3 codecs, stochastic rounding,
-// the counter-based RNG that drives it, and the sigmoid-BCE gradient.
+// Device numerics for the XMC head step on gfx950: BF16, OCP-E4M3 and MX-scaled FP4 (E2M1 with
+// E8M0 block scales) codecs, stochastic rounding, the counter-based RNG that drives it, and the
+// sigmoid-BCE gradient.
 //
 // Method context: "ELMO: Efficiency via Low-precision and Peak Memory Optimization in Large Output
 // Spaces" (summary page, "Approach" and "Surprising findings"): pure BF16/FP8-E4M3 classifier

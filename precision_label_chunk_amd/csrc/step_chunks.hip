@@ -1066,6 +1066,174 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------------
+// forward + gradient with BF16 features stationary in registers (BF16 weights, 65-128 samples,
+// D = 768)
+// ------------------------------------------------------------------------------------------------
+// The 8.6M-label head's shape, where the tiled forward re-stages every feature row for every tile.
+// Four waves, one per SIMD, so that a lane has the whole register file: wave w holds samples
+// 32 w .. 32 w + 31 as its MFMA A fragments of all 768 features (8 BF16 per 16-feature K step,
+// 192 registers) and the work-group streams the chunk's weights through LDS in 32-label tiles
+// (48 KiB each, row pitch 1,552 bytes: an odd number of 16-byte groups, so 16 consecutive rows'
+// fragment reads fall on distinct banks), three buffers deep as in k_fwd_xs: tile t is loaded into
+// registers at the start of iteration t - 2 and written to LDS at its end. Per tile a wave runs
+// 48 MFMAs into two accumulators (even and odd K steps, so that consecutive MFMAs are independent)
+// and the gradient epilogue of its 32 x 32 block; one barrier per iteration; the positives of tile
+// i + 1 are gathered into label bits during iteration i. Work-groups take tiles blockIdx.x,
+// + gridDim.x, ...; tiles past the chunk read as zero, and the tiles cover whole 64-label
+// backward tiles, so every G row the backward reads is written (zeros past the chunk).
+constexpr int XB_TJ = 32;                                      // labels per tile
+
+template <bool LOSS, bool ZOUT>
+__global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W, const uint16_t* __restrict__ Xb,
+                                                int D, int64_t c0, int clen,
+                                                const uint32_t* __restrict__ tile_off,
+                                                const uint32_t* __restrict__ bucket, int64_t bucket_cap,
+                                                int B, uint16_t* __restrict__ G, int64_t gpitch,
+                                                float* __restrict__ loss_part,
+                                                float* __restrict__ Z, uint16_t* __restrict__ Gout,
+                                                int64_t zpitch, int64_t zoff) {
+  constexpr int MB = 128, D_ = 768, NK = D_ / 16;    // 48 K steps of the BF16 MFMA
+  constexpr int RB = 2 * D_;                         // bytes per weight row
+  constexpr int PITCH = RB + 16;
+  static_assert((PITCH / 16) % 2 == 1, "an odd number of 16-byte groups per row");
+  constexpr int PPR = RB / 16;                       // 16-byte parts per row
+  constexpr int CPT = XB_TJ * PPR / 256;             // 16-byte chunks per thread and tile
+  static_assert(CPT * 256 == XB_TJ * PPR, "whole chunks per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t Ws[3][XB_TJ * PITCH];
+  __shared__ uint32_t ybits[4][XB_TJ * (MB / 32)];   // label-major: bit b & 31 of word [j][b >> 5]
+  __shared__ float lred[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int bb = 32 * wave;                           // the wave's first sample
+  // tiles of the chunk, rounded up to whole 64-label backward tiles: the backward reads G rows up
+  // to the next multiple of 64, so those past the chunk are written too (as zeros)
+  const int ntl = 2 * ((clen + 2 * XB_TJ - 1) / (2 * XB_TJ));
+  const int nmy = ntl > (int)blockIdx.x ? (ntl - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  auto tile_of = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
+  (void)D;
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + c0 * (int64_t)RB, clen * RB);
+
+  // chunk c of this thread: ci = tid + 256 c, row ci / PPR, part ci % PPR
+  i32x4_t stg[CPT];
+  auto wload = [&](int t, i32x4_t (&st)[CPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + 256 * c, row = ci / PPR, part = ci % PPR;
+      st[c] = buffer_load16(wres, (t * XB_TJ + row) * RB + part * 16);
+    }
+  };
+  auto wstore = [&](int buf, const i32x4_t (&st)[CPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = tid + 256 * c, row = ci / PPR, part = ci % PPR;
+      *(i32x4_t*)(&Ws[buf][row * PITCH + part * 16]) = st[c];
+    }
+  };
+  // positives of tile t: quarter t & 3 of 128-label bucket tile c0 / 128 + t / 4 (c0 is a multiple
+  // of 128)
+  auto yclear = [&](int buf) {
+    for (int i = tid; i < XB_TJ * (MB / 32); i += 256) ybits[buf][i] = 0u;
+  };
+  auto yscan = [&](int t, int buf) {
+    const int64_t tb = c0 / TJ1 + (t >> 2);
+    const uint32_t quarter = (uint32_t)(t & 3);
+    const uint64_t e0 = tile_off[tb];
+    const uint64_t e1 = tile_off[tb + 1] < (uint64_t)bucket_cap ? tile_off[tb + 1] : (uint64_t)bucket_cap;
+    for (uint64_t e = e0 + tid; e < e1; e += 256) {
+      const uint32_t v = bucket[e];
+      const uint32_t b = v >> 16, jl = v & (TJ1 - 1);
+      if (b < (uint32_t)MB && (jl >> 5) == quarter)
+        atomicOr(&ybits[buf][(jl & (XB_TJ - 1)) * (MB / 32) + (b >> 5)], 1u << (b & 31));
+    }
+  };
+
+  // prologue: the feature fragments and tiles 0 and 1 loaded together, the tiles into LDS, then
+  // tile 0's positives
+  s16x8_t xf[NK];
+  {
+    const uint16_t* xr = Xb + (int64_t)(bb + l32) * D_ + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) xf[kk] = *(const s16x8_t*)(xr + kk * 16);
+  }
+  {
+    i32x4_t stg1[CPT];
+    wload(tile_of(0), stg);
+    wload(tile_of(1), stg1);
+    yclear(0); yclear(1); yclear(2);
+    wstore(0, stg);
+    wstore(1, stg1);
+  }
+  __syncthreads();
+  if (nmy > 0) yscan(tile_of(0), 0);
+  __syncthreads();
+
+  float lsum = 0.0f;
+  for (int i = 0; i < nmy; ++i) {
+    if (i + 2 < nmy) wload(tile_of(i + 2), stg);
+    // the tile's 48 MFMAs, each weight fragment read from LDS two K steps ahead
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+    {
+      const uint8_t* wb = &Ws[i % 3][l32 * PITCH + hi * 16];
+      auto rd = [&](int kk) { return *(const s16x8_t*)(wb + kk * 32); };
+      s16x8_t f[3];
+      f[0] = rd(0); f[1] = rd(1);
+      static_for<0, NK>([&](auto K) {
+        constexpr int kk = decltype(K)::value;
+        if constexpr (kk + 2 < NK) f[(kk + 2) % 3] = rd(kk + 2);
+        acc[kk & 1] = mfma_bf16(xf[kk], f[kk % 3], acc[kk & 1]);
+        sched_fence();
+      });
+    }
+    f32x16_t z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = acc[0][r] + acc[1][r];
+    {
+      const int t = tile_of(i);
+      const int jc = t * XB_TJ + l32;                 // label within the chunk
+      const bool jvalid = jc < clen;
+      const uint32_t yw = ybits[i & 3][l32 * (MB / 32) + wave];
+      float gv[16];
+      fwd_grad_block(z, yw, jvalid, bb, B, hi, gv);
+      if constexpr (LOSS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bl = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (jvalid && (bb + bl < B)) lsum += bce_loss(z[r], (yw >> bl) & 1u);
+        }
+      }
+      if constexpr (ZOUT) {
+        const int64_t lab = c0 + jc;
+        const bool lok = jvalid && lab >= zoff;
+        const int64_t base = (int64_t)(bb + 4 * hi) * zpitch + (lab - zoff);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + (r & 3);
+          if (lok && bb + 4 * hi + rr < B) {
+            const int64_t o = base + rr * zpitch;
+            if (Z) Z[o] = z[r];
+            if (Gout) Gout[o] = (uint16_t)f32_to_bf16_rne(gv[r]);
+          }
+        }
+      }
+      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)jc * gpitch, bb, hi);
+    }
+    if (i + 2 < nmy) wstore((i + 2) % 3, stg);
+    if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
+    yclear((i + 2) & 3);
+    __syncthreads();
+  }
+
+  if constexpr (LOSS) {
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) lred[wave] = lsum;
+    __syncthreads();
+    if (tid == 0) loss_part[c0 / XB_TJ + blockIdx.x] = lred[0] + lred[1] + lred[2] + lred[3];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // chunk scheduler: per label chunk the forward + gradient kernel, then the backward + update kernel
 // ------------------------------------------------------------------------------------------------
 #define LAUNCH_CHECK() do { if (hipGetLastError() != hipSuccess) return ELMO_EHIP_; } while (0)
@@ -1080,21 +1248,33 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
   float* part = (float*)(ws + s.part);
   float* lpart = (float*)(ws + s.loss);
   const int64_t l_end = a.l1;
-  // the forward with the features stationary in registers where it is built (E4M3, 256 padded
-  // samples, D = 768); the tiled forward elsewhere
+  // the forward with the features stationary in registers where it is built (E4M3 and MXFP4 at 256
+  // padded samples, D = 768); the tiled forward elsewhere
   constexpr bool XS_OK = MB == 256 && (WF == W_E4M3_ || WF == W_MXFP4_);
   const bool xs = XS_OK && a.D == 768;
+  // and for BF16 weights at 65-128 padded samples (the 8.6M-label head's shape)
+  constexpr bool XB_OK = MB == 128 && WF == W_BF16_;
+  const bool xb = XB_OK && a.D == 768;
   for (int64_t c0 = a.l0; c0 < l_end; c0 += s.Cc) {
     const int clen = (int)((l_end - c0) < s.Cc ? (l_end - c0) : s.Cc);
     const int nt1 = (clen + TJ1 - 1) / TJ1;
     const int ntx = (clen + XS_TJ - 1) / XS_TJ;
     const int gx = ntx < s.cus ? ntx : s.cus;
+    const int ntb = 2 * ((clen + 2 * XB_TJ - 1) / (2 * XB_TJ));   // (as the kernel counts its tiles)
+    const int gb = ntb < s.cus ? ntb : s.cus;
     auto forward = [&](auto LOSS, auto ZOUT, float* Z, uint16_t* Gout, int64_t zpitch, int64_t zoff) {
       constexpr bool L_ = decltype(LOSS)::value, Z_ = decltype(ZOUT)::value;
       if constexpr (XS_OK) {
         if (xs) {
           hipLaunchKernelGGL((k_fwd_xs<WF, 12, L_, Z_>), dim3(gx), dim3(512), 0, st, W, ws + s.xq, a.D, c0, clen, toff,
                              bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
+          return;
+        }
+      }
+      if constexpr (XB_OK) {
+        if (xb) {
+          hipLaunchKernelGGL((k_fwd_xb<L_, Z_>), dim3(gb), dim3(256), 0, st, W, (const uint16_t*)(ws + s.xb), a.D, c0,
+                             clen, toff, bucket, a.nnz, a.B, Gc, (int64_t)MB, lpart, Z, Gout, zpitch, zoff);
           return;
         }
       }

@@ -314,7 +314,8 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   s.xbt = off;      off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
   s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
-  s.loss = off;     off = align_up(off + 4 * (size_t)(2 * s.ntiles + 2), A);
+  // loss partials: one slot per 128-, 64- or 32-label tile of the forward kernel in use
+  s.loss = off;     off = align_up(off + 4 * (size_t)(4 * s.ntiles + 4), A);
   s.total = off;
   return s;
 }
@@ -332,9 +333,9 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, cnt, s.ntiles + 1, 0u);
   LAUNCH_CHECK();
   if (a.loss) {
-    // loss partials: one slot per 128-label tile (tiled forward) or per work-group and 64 labels
-    // (stationary-feature forward); the slots a launch does not write stay zero
-    hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, (uint32_t*)(ws + s.loss), 2 * s.ntiles + 2, 0u);
+    // loss partials: one slot per 128-label tile (tiled forward) or per work-group and 64 or 32
+    // labels (stationary-feature forwards); the slots a launch does not write stay zero
+    hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, (uint32_t*)(ws + s.loss), 4 * s.ntiles + 4, 0u);
     LAUNCH_CHECK();
   }
   if (!a.forward_only()) {
@@ -388,7 +389,7 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     LAUNCH_CHECK();
   }
   if (a.loss) {
-    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, st, (const float*)(ws + s.loss), 2 * s.ntiles + 2, a.loss);
+    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, st, (const float*)(ws + s.loss), 4 * s.ntiles + 4, a.loss);
     LAUNCH_CHECK();
   }
   return ELMO_OK_;

@@ -49,6 +49,10 @@ CASES = [  # B, D, L, chunk, wfmt
     (129, 768, 70, 128, wk.W_E4M3),        # one chunk of two 64-label tiles, the second ragged
     (256, 768, 5000, 65536, wk.W_E4M3),    # chunk larger than L
     (160, 768, 1337, 128, wk.W_E4M3),      # eleven chunks of one 128-label tile each
+    # BF16 with 65..128 samples and D = 768: the forward with BF16 features held in registers
+    (128, 768, 3000, 1024, wk.W_BF16),
+    (100, 768, 1337, 256, wk.W_BF16),      # ragged last chunk and last 32-label tile
+    (65, 768, 70, 128, wk.W_BF16),         # one chunk of three 32-label tiles, the last ragged
 ]
 
 
@@ -98,7 +102,7 @@ def test_step_matches_oracle(elmo, orc, B, D, L, chunk, wfmt):
     check_step(elmo, orc, W0, bt, wfmt, lr, seed, step, Wg, dXg, lossg)
 
 
-@pytest.mark.parametrize("B,D,wfmt", [(20, 128, wk.W_BF16), (200, 768, wk.W_E4M3)])
+@pytest.mark.parametrize("B,D,wfmt", [(20, 128, wk.W_BF16), (200, 768, wk.W_E4M3), (100, 768, wk.W_BF16)])
 def test_logits_subrange(elmo, orc, B, D, wfmt):
     wl, W0, bt = _case(B, D, 1000, wfmt)
     Wd, Xd = to_dev_codes(W0), batch_to_dev(bt)[0]
@@ -109,7 +113,8 @@ def test_logits_subrange(elmo, orc, B, D, wfmt):
         assert_close(Zg, Zr, RTOL[wfmt])
 
 
-@pytest.mark.parametrize("B,D,wfmt", [(48, 128, wk.W_BF16), (48, 128, wk.W_E4M3), (256, 768, wk.W_E4M3)])
+@pytest.mark.parametrize("B,D,wfmt", [(48, 128, wk.W_BF16), (48, 128, wk.W_E4M3), (256, 768, wk.W_E4M3),
+                                      (128, 768, wk.W_BF16)])
 def test_chunk_size_invariance(elmo, B, D, wfmt):
     wl, W0, bt = _case(B, D, 2000, wfmt)
     outs = [_run(elmo, W0, bt, wfmt, 0.1, 5, 1, c) for c in (128, 1000, 2000, 1 << 20)]
