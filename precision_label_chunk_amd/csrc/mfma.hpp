@@ -48,6 +48,14 @@ __device__ __forceinline__ f32x16_t mfma_e4m3_fp4(i32x8_t a, i32x8_t b, f32x16_t
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, scale_b);
 }
 
+// the same with the B operand's four code dwords and its scale taken from byte OPSEL_B of scale_b
+// (the A operand's scale 1.0)
+template <int OPSEL_B>
+__device__ __forceinline__ f32x16_t mfma_e4m3_fp4_sel(i32x8_t a, i32x4_t b, f32x16_t c, int scale_b) {
+  const i32x8_t bv = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bv, c, 0, 4, 0, 127, OPSEL_B, scale_b);
+}
+
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // p must point into __shared__ memory and be 8-byte aligned

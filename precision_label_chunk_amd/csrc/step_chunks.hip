@@ -289,12 +289,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
 // operand's K order beside an FP4 operand.
 constexpr int XS_TJ = 64;                                      // labels per tile
 
-template <int OPSEL_B>
-__device__ __forceinline__ f32x16_t mfma_e4m3_fp4_sel(i32x8_t a, i32x4_t b, f32x16_t c, int scale_b) {
-  const i32x8_t bv = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bv, c, 0, 4, 0, 127, OPSEL_B, scale_b);
-}
-
 // NK: 64-byte K steps of the FP8 MFMA (D = 64 NK; the features take 8 NK registers)
 template <int WF, int NK, bool LOSS, bool ZOUT>
 __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq,

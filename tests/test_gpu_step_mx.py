@@ -166,3 +166,40 @@ def test_mx_feature_sizes_rejected(elmo):
     ids = torch.zeros(0, dtype=torch.int32, device="cuda")
     with pytest.raises(elmo.ElmoError):
         elmo.step(W, X, rp, ids, 0.1, 0, 0, 128, wfmt=elmo.ELMO_W_MXFP4)
+
+
+def test_mx_nan_feature_propagates_as_in_the_oracle(elmo, orc):
+    """A NaN feature makes every logit of its sample NaN, so every label's dW and every block's t
+    hold a NaN: every block becomes a NaN block (scale 255, zero codes), as in the oracle; its
+    sample's dX row is NaN and the other rows stay finite and close."""
+    wl, W0, bt = _case(40, 256, 1500)
+    lr, seed, step = 0.05, 3, 1
+    Xb = bt.X.copy(); Xb[5, 17] = 0x7FC0
+    btn = wk.Batch(Xb, bt.row_ptr, bt.ids)
+    Wg, dXg, _ = _run(elmo, W0, btn, lr, seed, step, 512)
+    Wr, dXr, _, _, _ = orc.step(MX, W0, Xb, bt.row_ptr, bt.ids, lr, seed, step)
+    cg, sg = mx_split(Wg)
+    cr, sr = mx_split(Wr)
+    assert (sg == 255).all() and (sr == 255).all() and (cg == 0).all()
+    assert np.isnan(dXg[5]).all() and np.isnan(dXr[5]).all()
+    rows = np.arange(40) != 5
+    assert_close(dXg[rows], dXr[rows], RTOL[MX])
+
+
+def test_mx_sample_permutation_general(elmo, orc):
+    """Permuting the samples of a general MXFP4 batch: the permuted step meets the block weight bar
+    against the oracle's step on the permuted batch, its dX rows are the unpermuted run's rows
+    permuted (to the FP32 summation order), and the two runs' blocks are >= 99.9% equal."""
+    wl, W0, bt = _case(100, 256, 2500, lam=6.0)
+    perm = np.random.default_rng(21).permutation(100)
+    rows = [bt.ids[bt.row_ptr[p]:bt.row_ptr[p + 1]] for p in perm]
+    rp = np.zeros(101, np.int32); rp[1:] = np.cumsum([len(r) for r in rows])
+    btp = wk.Batch(bt.X[perm], rp, np.concatenate(rows).astype(np.int32))
+    lr, seed, step = 0.05, 6, 2
+    Wa, dXa, _ = _run(elmo, W0, bt, lr, seed, step, 1024)
+    Wp, dXp, _ = _run(elmo, W0, btp, lr, seed, step, 1024)
+    check_step(elmo, orc, W0, btp, lr, seed, step, Wp, dXp)
+    assert_close(dXp, dXa[perm], 1e-5)
+    eq, nan = mx_weight_report(Wp, Wa)
+    print(f"  permuted vs unpermuted blocks: equal {eq:.6f}", flush=True)
+    assert eq >= 0.999 and nan == 0

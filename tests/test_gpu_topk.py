@@ -40,7 +40,11 @@ def _check(elmo, orc, wfmt, W0, Wd, X, idx_g, sc_g, k, label=""):
                                           (70, 128, 3000, 64, wk.W_BF16), (130, 256, 2000, 64, wk.W_E4M3),
                                           (3, 64, 64, 64, wk.W_BF16), (300, 256, 5000, 5, wk.W_MXFP4),
                                           (129, 768, 3000, 32, wk.W_MXFP4), (70, 512, 2000, 64, wk.W_MXFP4),
-                                          (1, 256, 130, 8, wk.W_MXFP4)])
+                                          (1, 256, 130, 8, wk.W_MXFP4),
+                                          # D = 768, k <= 8 in MXFP4: the stationary-query scan
+                                          (300, 768, 5000, 5, wk.W_E4M3), (257, 768, 4099, 8, wk.W_MXFP4),
+                                          (1, 768, 130, 1, wk.W_MXFP4), (600, 768, 20000, 5, wk.W_MXFP4),
+                                          (13, 768, 40, 8, wk.W_MXFP4)])
 def test_topk_matches_oracle(elmo, orc, N, D, L, k, wfmt):
     wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
     W0 = wk.make_weights(wl)
@@ -90,13 +94,15 @@ def test_topk_nan_scores_rank_last(elmo, orc):
     assert np.array_equal(idx.cpu().numpy(), idx_r)
 
 
-@pytest.mark.parametrize("wfmt,D", [(wk.W_BF16, 64), (wk.W_E4M3, 64), (wk.W_MXFP4, 256)])
+@pytest.mark.parametrize("wfmt,D", [(wk.W_BF16, 64), (wk.W_E4M3, 64), (wk.W_MXFP4, 256), (wk.W_E4M3, 768),
+                                    (wk.W_MXFP4, 768)])
 def test_topk_many_tiles_per_range(elmo, orc, wfmt, D):
     """4096 queries over 60k labels: each work-group scans some 30 label tiles, so the lists fill
     and later tiles take the bounded-candidate path (lists of up to 8). Its top-8 must equal, bit for
     bit, the first 8 of the top-32, and the top-32 the first 32 of the top-64 (lists of 32 and 64
-    always take the full score-tile path); sampled queries must match the oracle. Duplicated weight
-    rows across tiles force exact ties."""
+    always take the full score-tile path; at D = 768 in MXFP4 the top-8 comes from the
+    stationary-query scan, so this also checks the two scans against each other); sampled queries
+    must match the oracle. Duplicated weight rows across tiles force exact ties."""
     N, L = 4096, 60000
     wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=N, D=D, L=L, wfmt=wfmt)
     W0 = wk.make_weights(wl).copy()
