@@ -378,10 +378,14 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
     }
   };
 
-  // prologue: the stationary feature fragments and tiles 0 and 1 loaded together (one memory
-  // latency, not three in a row; a tile this work-group does not have lies past the chunk and
-  // reads as zero), the tiles into LDS, then tile 0's positives
+  // prologue: tiles 0 and 1, then the stationary feature fragments, all in flight together (a tile
+  // this work-group does not have lies past the chunk and reads as zero); the tiles' LDS writes
+  // wait only for the tile loads, which were issued first, so the feature loads complete under
+  // the LDS writes, the barriers and the first MFMAs, each MFMA waiting only for its own fragment
   i32x8_t xf[NK];
+  i32x4_t stg1[CPT];
+  wload(tile_of(0), stg);
+  wload(tile_of(1), stg1);
   {
     // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15
     const uint8_t* xr = Xq + (int64_t)(bb + l32) * D_ + (MX ? hi * 16 : hi * 32);
@@ -392,14 +396,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
       xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
   }
-  {
-    i32x4_t stg1[CPT];
-    wload(tile_of(0), stg);
-    wload(tile_of(1), stg1);
-    yclear(0); yclear(1); yclear(2);
-    wstore(0, stg);
-    wstore(1, stg1);
-  }
+  yclear(0); yclear(1); yclear(2);
+  wstore(0, stg);
+  wstore(1, stg1);
   __syncthreads();
   if (nmy > 0) yscan(tile_of(0), 0);
   __syncthreads();
@@ -1143,22 +1142,20 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
     }
   };
 
-  // prologue: the feature fragments and tiles 0 and 1 loaded together, the tiles into LDS, then
-  // tile 0's positives
+  // prologue: tiles 0 and 1, then the feature fragments, all in flight together; the tiles' LDS
+  // writes wait only for the tile loads (issued first), then tile 0's positives
   s16x8_t xf[NK];
+  i32x4_t stg1[CPT];
+  wload(tile_of(0), stg);
+  wload(tile_of(1), stg1);
   {
     const uint16_t* xr = Xb + (int64_t)(bb + l32) * D_ + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) xf[kk] = *(const s16x8_t*)(xr + kk * 16);
   }
-  {
-    i32x4_t stg1[CPT];
-    wload(tile_of(0), stg);
-    wload(tile_of(1), stg1);
-    yclear(0); yclear(1); yclear(2);
-    wstore(0, stg);
-    wstore(1, stg1);
-  }
+  yclear(0); yclear(1); yclear(2);
+  wstore(0, stg);
+  wstore(1, stg1);
   __syncthreads();
   if (nmy > 0) yscan(tile_of(0), 0);
   __syncthreads();

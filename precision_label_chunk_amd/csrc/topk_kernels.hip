@@ -321,8 +321,12 @@ __global__ __launch_bounds__(512, 1) void k_topk_xs(const uint8_t* __restrict__ 
     }
   };
 
-  // prologue: the query fragments and tiles 0 and 1 loaded together, the tiles into LDS
+  // prologue: tiles 0 and 1, then the query fragments, all in flight together; the tiles' LDS
+  // writes wait only for the tile loads (issued first)
   i32x8_t xf[NK];
+  i32x4_t stg1[CPT];
+  wload(0, stg);
+  wload(1, stg1);
   {
     const uint8_t* xr = Xq + (int64_t)(qb * TQ + bb + l32) * D_ + (MX ? hi * 16 : hi * 32);
     constexpr int O2 = MX ? 32 : 16;
@@ -332,13 +336,8 @@ __global__ __launch_bounds__(512, 1) void k_topk_xs(const uint8_t* __restrict__ 
       xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
   }
-  {
-    i32x4_t stg1[CPT];
-    wload(0, stg);
-    wload(1, stg1);
-    wstore(0, stg);
-    wstore(1, stg1);
-  }
+  wstore(0, stg);
+  wstore(1, stg1);
   float ls[KK]; int lj[KK];
   list_init<KK>(ls, lj);
   const int qo = lane >> 1, half = lane & 1;          // the list this lane owns
