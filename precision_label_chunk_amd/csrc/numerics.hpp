@@ -230,6 +230,25 @@ __device__ __forceinline__ float bce_grad_small_m(float z, uint32_t ys) {
   return u2f(__builtin_amdgcn_bitop3_b32(f2u(r), ys, 0x80000000u, 0x78));
 }
 
+// the same two forms for y = 0, g = sigmoid(z), with a = -z taken by the operations' sign
+// modifiers (bit-identical to the forms above with the label mask 0)
+__device__ __forceinline__ float bce_grad_fast_y0(float z) {
+  constexpr float L2E_HI = 1.44269502162933349609375f;
+  constexpr float LN2 = 0.693147180559945309f;
+  constexpr float L2E_LO_LN2 = 1.33498838e-08f;
+  const float a = -z;
+  const float p = a * L2E_HI;
+  const float t = fmaf(a, L2E_HI, -p);
+  const float c = fmaf(t, LN2, a * L2E_LO_LN2);
+  float e = __builtin_amdgcn_exp2f(p);
+  e = fmaf(e, c, e);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ float bce_grad_small_y0(float z) {
+  constexpr float L2E_HI = 1.44269502162933349609375f;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * L2E_HI));
+}
+
 __device__ __forceinline__ float bce_grad_fast(float z, bool y) { return bce_grad_fast_m(z, y ? 0x80000000u : 0u); }
 
 // the exact-division form, for |z| > 80

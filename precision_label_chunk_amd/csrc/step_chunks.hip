@@ -48,7 +48,16 @@ __device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, b
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(!common) == 0, 1)) {
     // every element in range and valid: no select; label bit bl of yw moved to bit 31
     const uint32_t yh = yw >> (4 * hi);
-    if (__builtin_amdgcn_ballot_w64(m > 2.0f) == 0) {
+    if (__builtin_amdgcn_ballot_w64(yh != 0u) == 0) {
+      // (the usual block: no positives, so no label bits and no sign operations)
+      if (__builtin_amdgcn_ballot_w64(m > 2.0f) == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gv[i] = bce_grad_small_y0(a[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gv[i] = bce_grad_fast_y0(a[i]);
+      }
+    } else if (__builtin_amdgcn_ballot_w64(m > 2.0f) == 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) gv[i] = bce_grad_small_m(a[i], yh << (31 - (8 * (i >> 2) + (i & 3))));
     } else {
