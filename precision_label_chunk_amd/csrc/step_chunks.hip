@@ -396,12 +396,14 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   wload(tile_of(0), stg);
   wload(tile_of(1), stg1);
   {
-    // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15
-    const uint8_t* xr = Xq + (int64_t)(bb + l32) * D_ + (MX ? hi * 16 : hi * 32);
-    constexpr int O2 = MX ? 32 : 16;
+    // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15,
+    // as the step's preparation lays them out: part p of K step kk at ((wave NK + kk) 2 + p) KiB
+    // (one lane offset, the K step's in the instructions' scalar offsets)
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xq, MB * D_);
+    const int xo = (wave * NK * 2 * 64 + lane) * 16;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const i32x4_t a0 = *(const i32x4_t*)(xr + kk * 64), a1 = *(const i32x4_t*)(xr + kk * 64 + O2);
+      const i32x4_t a0 = buffer_load16(xres, xo, 2 * kk * 1024), a1 = buffer_load16(xres, xo, (2 * kk + 1) * 1024);
       xf[kk] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
   }
@@ -789,13 +791,14 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   const int jb0 = NH == 2 ? h : 0;             // first label block of this wave
   const int nb0 = h * NBW;                     // first sample block of this wave
 
-  // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples), from the
-  // feature-major copy XbT[d][b]
+  // stationary X^T fragments of this wave's 32 features: lane (d, 8 samples), from the step
+  // preparation's fragment-ordered copy (sample step kk of feature block fb at (fb MB / 16 + kk) KiB)
   s16x8_t xT[KK];
   {
-    const int d = dsl + dblk * 32 + l32;
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(XbT, MB * D * 2);
+    const int xo = (((dsl + dblk * 32) >> 5) * (MB / 16) * 64 + lane) * 16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) xT[kk] = *(const s16x8_t*)(XbT + (int64_t)d * MB + kk * 16 + hi * 8);
+    for (int kk = 0; kk < KK; ++kk) xT[kk] = __builtin_bit_cast(s16x8_t, buffer_load16(xres, xo, kk * 1024));
   }
   // dX^T accumulators, starting from this range's running partial sum (a fixed slot per range:
   // deterministic; zero in the step's first chunk, where every slot has a range), read here under
@@ -1158,9 +1161,12 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
   wload(tile_of(0), stg);
   wload(tile_of(1), stg1);
   {
-    const uint16_t* xr = Xb + (int64_t)(bb + l32) * D_ + hi * 8;
+    // (in the step preparation's fragment order: K step kk of this wave at (wave NK + kk) KiB; one
+    // lane offset, the K step's in the instructions' scalar offsets)
+    const __amdgpu_buffer_rsrc_t xres = buffer_rsrc(Xb, MB * D_ * 2);
+    const int xo = (wave * NK * 64 + lane) * 16;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) xf[kk] = *(const s16x8_t*)(xr + kk * 16);
+    for (int kk = 0; kk < NK; ++kk) xf[kk] = __builtin_bit_cast(s16x8_t, buffer_load16(xres, xo, kk * 1024));
   }
   yclear(0); yclear(1); yclear(2);
   wstore(0, stg);
@@ -1251,10 +1257,10 @@ int run_chunks(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t 
   // the forward with the features stationary in registers where it is built (E4M3 and MXFP4 at 256
   // padded samples, D = 768); the tiled forward elsewhere
   constexpr bool XS_OK = MB == 256 && (WF == W_E4M3_ || WF == W_MXFP4_);
-  const bool xs = XS_OK && a.D == 768;
+  const bool xs = XS_OK && (fwd_x_layout(MB, WF, a.D) == XLAY_XS_E4M3 || fwd_x_layout(MB, WF, a.D) == XLAY_XS_MX);
   // and for BF16 weights at 65-128 padded samples (the 8.6M-label head's shape)
   constexpr bool XB_OK = MB == 128 && WF == W_BF16_;
-  const bool xb = XB_OK && a.D == 768;
+  const bool xb = XB_OK && fwd_x_layout(MB, WF, a.D) == XLAY_XB;
   for (int64_t c0 = a.l0; c0 < l_end; c0 += s.Cc) {
     const int clen = (int)((l_end - c0) < s.Cc ? (l_end - c0) : s.Cc);
     const int nt1 = (clen + TJ1 - 1) / TJ1;

@@ -168,17 +168,46 @@ __global__ __launch_bounds__(256) void k_label_scatter(const int32_t* __restrict
   }
 }
 
-// zero-padded BF16 copy of X ([MB][D]) and, in FP8 mode, its E4M3-RNE cast for the forward MFMA
-__global__ void k_prep_x(const uint16_t* __restrict__ X, int B, int D, int MB, uint16_t* __restrict__ Xb,
+// The prepared feature copies, zero-padded to MB samples, each element i of a copy taken from
+// the sample b and feature k that position i holds:
+//   Xb  BF16 X: row-major [MB][D], or (XLAY_XB) the BF16 stationary forward's A fragments: K step
+//       kk (16 features) of wave w's 32 samples at ((w (D / 16) + kk) 64 + lane) 8, lane (l, h)
+//       holding sample 32 w + l, features 16 kk + 8 h .. + 7;
+//   Xq  (E4M3 and MXFP4 weights) E4M3-RNE(X): row-major, or (XLAY_XS_*) the stationary forward's A
+//       fragments: 16-byte part p of K step kk (64 features) of wave w at (((w (D / 64) + kk) 2 +
+//       p) 64 + lane) 16, lane (l, h) holding sample 32 w + l, features 64 kk + 32 h + 16 p .. + 15
+//       (beside E4M3 weights) or 64 kk + 32 p + 16 h .. + 15 (beside E2M1 weights);
+//   XbT BF16 X^T for the backward's stationary operand: feature block fb (32 features), sample
+//       step kk (16 samples) at ((fb (MB / 16) + kk) 64 + lane) 8, lane (l, h) holding feature
+//       32 fb + l, samples 16 kk + 8 h .. + 7.
+// Every fragment load of the consuming kernels is then 1 KiB contiguous per wave.
+__global__ void k_prep_x(const uint16_t* __restrict__ X, int B, int D, int MB, int xlay, uint16_t* __restrict__ Xb,
                          uint8_t* __restrict__ Xq, uint16_t* __restrict__ XbT) {
   const int64_t n = (int64_t)MB * D;
+  auto at = [&](int64_t b, int64_t k) { return b < B ? (uint32_t)X[b * D + k] : 0u; };
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    uint32_t v = (i / D) < B ? X[i] : 0u;
-    Xb[i] = (uint16_t)v;
-    if (Xq) Xq[i] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(v));
-    // the feature-major copy XbT[d][b] (element i of it: d = i / MB, b = i % MB)
-    const int64_t d = i / MB, b = i % MB;
-    XbT[i] = b < B ? X[b * D + d] : (uint16_t)0;
+    if (xlay == XLAY_XB) {
+      const int e = (int)(i & 7), lane = (int)((i >> 3) & 63);
+      const int64_t r = i >> 9, kk = r % (D / 16), w = r / (D / 16);
+      Xb[i] = (uint16_t)at(32 * w + (lane & 31), 16 * kk + 8 * (lane >> 5) + e);
+    } else {
+      Xb[i] = (uint16_t)at(i / D, i % D);
+    }
+    if (Xq) {
+      int64_t b = i / D, k = i % D;
+      if (xlay == XLAY_XS_E4M3 || xlay == XLAY_XS_MX) {
+        const int e = (int)(i & 15), lane = (int)((i >> 4) & 63), part = (int)((i >> 10) & 1), h = lane >> 5;
+        const int64_t r = i >> 11, kk = r % (D / 64), w = r / (D / 64);
+        b = 32 * w + (lane & 31);
+        k = 64 * kk + (xlay == XLAY_XS_MX ? 32 * part + 16 * h : 32 * h + 16 * part) + e;
+      }
+      Xq[i] = (uint8_t)f32_to_e4m3_rne_sat(bf16_to_f32(at(b, k)));
+    }
+    {
+      const int e = (int)(i & 7), lane = (int)((i >> 3) & 63);
+      const int64_t r = i >> 9, kk = r % (MB / 16), fb = r / (MB / 16);
+      XbT[i] = (uint16_t)at(16 * kk + 8 * (lane >> 5) + e, 32 * fb + (lane & 31));
+    }
   }
 }
 
@@ -364,7 +393,8 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     const int64_t n = (int64_t)s.MB * a.D;
     const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
     hipLaunchKernelGGL(k_prep_x, dim3(blocks), dim3(256), 0, st, (const uint16_t*)a.X, a.B, a.D, s.MB,
-                       (uint16_t*)(ws + s.xb), a.wdtype != W_BF16_ ? ws + s.xq : (uint8_t*)nullptr,
+                       fwd_x_layout(s.MB, a.wdtype, a.D), (uint16_t*)(ws + s.xb),
+                       a.wdtype != W_BF16_ ? ws + s.xq : (uint8_t*)nullptr,
                        (uint16_t*)(ws + s.xbt));
     LAUNCH_CHECK();
   }

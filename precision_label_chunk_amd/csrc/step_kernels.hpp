@@ -20,6 +20,19 @@ constexpr uint32_t ELMO_FLAG_LABEL_RANGE_ = 1u, ELMO_FLAG_ROW_PTR_ = 2u;
 constexpr int TJ1 = 128;       // labels per forward tile (and label-bucket granularity)
 constexpr int TJ2 = 64;        // labels per backward tile
 
+// The forward a step shape takes, and so the order the prepared feature copies are written in:
+// features stationary in registers for E4M3 / MXFP4 weights at 256 padded samples and for BF16
+// weights at 128, both at D = 768 (each lane's fragments then lie 1 KiB-contiguous per wave, in
+// the order the kernel loads them), else the tiled forward over row-major copies.
+constexpr int XLAY_ROWS = 0, XLAY_XS_E4M3 = 1, XLAY_XS_MX = 2, XLAY_XB = 3;
+__host__ __device__ constexpr int fwd_x_layout(int MB, int wf, int D) {
+  return D != 768 ? XLAY_ROWS
+         : (MB == 256 && wf == W_E4M3_) ? XLAY_XS_E4M3
+         : (MB == 256 && wf == W_MXFP4_) ? XLAY_XS_MX
+         : (MB == 128 && wf == W_BF16_) ? XLAY_XB
+                                        : XLAY_ROWS;
+}
+
 struct StepLayout {
   int MB, DS, NS, NR;
   int cus;                              // compute units of the device
