@@ -280,8 +280,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(const uint8_t* __restrict__ W
 // loads in each K slice. Here each work-group holds all 256 E4M3 feature rows in registers for the
 // whole launch (wave w: samples 32 w .. 32 w + 31, lane (l32, hi) the MFMA A fragments of row
 // 32 w + l32, 32 bytes per 64-byte K step: D / 8 registers) and streams the chunk's weights through
-// LDS in 64-label tiles, three tile buffers deep: tile t's rows are loaded (into registers) at the
-// start of iteration t - 2 and written to LDS at its end, a whole iteration ahead of their use. One
+// LDS in 64-label tiles, two tile buffers: tile t's rows are loaded (into registers) at the start
+// of iteration t - 1 and written to LDS at its end, into the buffer tile t - 1 used. One
 // work-group per CU takes tiles blockIdx.x, + gridDim.x, ...
 // The waves come in two groups of four, one wave of each per SIMD, in complementary phases: in
 // iteration i group A (waves 0-3) runs tile i's MFMAs and then its gradient epilogue, group B (4-7)
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   constexpr int PPR = D_ / 16;                        // (E4M3) 16-byte parts per weight row
   constexpr int NCH = MX ? XS_TJ * RB / 16 : XS_TJ * PPR;   // 16-byte chunks per tile
   constexpr int CPT = (NCH + 511) / 512;              // 16-byte weight chunks per thread and tile
-  __shared__ __attribute__((aligned(16))) uint8_t Ws[3][XS_TJ * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t Ws[2][XS_TJ * PITCH];
   __shared__ uint32_t ybits[4][XS_TJ * (MB / 32)];   // label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[8];
 
@@ -387,14 +387,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
     }
   };
 
-  // prologue: tiles 0 and 1, then the stationary feature fragments, all in flight together (a tile
-  // this work-group does not have lies past the chunk and reads as zero); the tiles' LDS writes
-  // wait only for the tile loads, which were issued first, so the feature loads complete under
-  // the LDS writes, the barriers and the first MFMAs, each MFMA waiting only for its own fragment
+  // prologue: tile 0, then the stationary feature fragments, all in flight together (a tile this
+  // work-group does not have lies past the chunk and reads as zero); the tile's LDS writes wait
+  // only for the tile loads, which were issued first, so the feature loads complete under the LDS
+  // writes, the barriers and the first MFMAs, each MFMA waiting only for its own fragment
   i32x8_t xf[NK];
-  i32x4_t stg1[CPT];
   wload(tile_of(0), stg);
-  wload(tile_of(1), stg1);
   {
     // E4M3 beside E4M3: bytes 32 hi .. +31 of each K step; beside FP4: 16 hi .. +15 and 32 + 16 hi .. +15,
     // as the step's preparation lays them out: part p of K step kk at ((wave NK + kk) 2 + p) KiB
@@ -409,7 +407,6 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   }
   yclear(0); yclear(1); yclear(2);
   wstore(0, stg);
-  wstore(1, stg1);
   __syncthreads();
   if (nmy > 0) yscan(tile_of(0), 0);
   __syncthreads();
@@ -507,16 +504,16 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
   // after loading it: the same arithmetic, without the loads in flight across the iteration)
   constexpr bool LATE_STORE = !ZOUT;
   for (int i = 0; i <= nmy; ++i) {
-    if (i + 2 < nmy) {
-      wload(tile_of(i + 2), stg);
-      if constexpr (!LATE_STORE) wstore((i + 2) % 3, stg);
+    if (i + 1 < nmy) {
+      wload(tile_of(i + 1), stg);
+      if constexpr (!LATE_STORE) wstore((i + 1) & 1, stg);
     }
     // group A: MFMAs of tile i, then its epilogue; group B: epilogue of tile i - 1, then MFMAs of tile i
     const int ie = i - grp;                           // the tile index whose epilogue this wave runs
-    if (grp == 0 && i < nmy) mfmas(i % 3);
+    if (grp == 0 && i < nmy) mfmas(i & 1);
     if (ie >= 0 && ie < nmy) epilogue(tile_of(ie), ie & 3);
-    if (grp == 1 && i < nmy) mfmas(i % 3);
-    if constexpr (LATE_STORE) if (i + 2 < nmy) wstore((i + 2) % 3, stg);
+    if (grp == 1 && i < nmy) mfmas(i & 1);
+    if constexpr (LATE_STORE) if (i + 1 < nmy) wstore((i + 1) & 1, stg);
     if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
     yclear((i + 2) & 3);
     __syncthreads();
@@ -1079,8 +1076,8 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 // 32 w .. 32 w + 31 as its MFMA A fragments of all 768 features (8 BF16 per 16-feature K step,
 // 192 registers) and the work-group streams the chunk's weights through LDS in 32-label tiles
 // (48 KiB each, row pitch 1,552 bytes: an odd number of 16-byte groups, so 16 consecutive rows'
-// fragment reads fall on distinct banks), three buffers deep as in k_fwd_xs: tile t is loaded into
-// registers at the start of iteration t - 2 and written to LDS at its end. Per tile a wave runs
+// fragment reads fall on distinct banks), two buffers as in k_fwd_xs: tile t is loaded into
+// registers at the start of iteration t - 1 and written to LDS at its end. Per tile a wave runs
 // 48 MFMAs into two accumulators (even and odd K steps, so that consecutive MFMAs are independent)
 // and the gradient epilogue of its 32 x 32 block; one barrier per iteration; the positives of tile
 // i + 1 are gathered into label bits during iteration i. Work-groups take tiles blockIdx.x,
@@ -1104,7 +1101,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
   constexpr int PPR = RB / 16;                       // 16-byte parts per row
   constexpr int CPT = XB_TJ * PPR / 256;             // 16-byte chunks per thread and tile
   static_assert(CPT * 256 == XB_TJ * PPR, "whole chunks per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t Ws[3][XB_TJ * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t Ws[2][XB_TJ * PITCH];
   __shared__ uint32_t ybits[4][XB_TJ * (MB / 32)];   // label-major: bit b & 31 of word [j][b >> 5]
   __shared__ float lred[4];
 
@@ -1154,12 +1151,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
     }
   };
 
-  // prologue: tiles 0 and 1, then the feature fragments, all in flight together; the tiles' LDS
-  // writes wait only for the tile loads (issued first), then tile 0's positives
+  // prologue: tile 0, then the feature fragments, all in flight together; the tile's LDS writes
+  // wait only for the tile loads (issued first), then tile 0's positives
   s16x8_t xf[NK];
-  i32x4_t stg1[CPT];
   wload(tile_of(0), stg);
-  wload(tile_of(1), stg1);
   {
     // (in the step preparation's fragment order: K step kk of this wave at (wave NK + kk) KiB; one
     // lane offset, the K step's in the instructions' scalar offsets)
@@ -1170,18 +1165,17 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
   }
   yclear(0); yclear(1); yclear(2);
   wstore(0, stg);
-  wstore(1, stg1);
   __syncthreads();
   if (nmy > 0) yscan(tile_of(0), 0);
   __syncthreads();
 
   float lsum = 0.0f;
   for (int i = 0; i < nmy; ++i) {
-    if (i + 2 < nmy) wload(tile_of(i + 2), stg);
+    if (i + 1 < nmy) wload(tile_of(i + 1), stg);
     // the tile's 48 MFMAs, each weight fragment read from LDS two K steps ahead
     f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
     {
-      const uint8_t* wb = &Ws[i % 3][l32 * PITCH + hi * 16];
+      const uint8_t* wb = &Ws[i & 1][l32 * PITCH + hi * 16];
       auto rd = [&](int kk) { return *(const s16x8_t*)(wb + kk * 32); };
       s16x8_t f[3];
       f[0] = rd(0); f[1] = rd(1);
@@ -1225,7 +1219,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
       }
       if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)jc * gpitch, bb, hi);
     }
-    if (i + 2 < nmy) wstore((i + 2) % 3, stg);
+    if (i + 1 < nmy) wstore((i + 1) & 1, stg);
     if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
     yclear((i + 2) & 3);
     __syncthreads();
