@@ -73,43 +73,33 @@ __device__ __forceinline__ void fwd_grad_block(const f32x16_t& a, uint32_t yw, b
   }
 }
 
+// The chunk gradient buffer G holds, per 64-label backward tile, MB x 64 BF16 values in blocks of
+// 32 labels x 32 samples, each the 2 KiB that one wave's accumulator block packs to:
+//   tile T = label >> 6, block (jb = (label >> 5) & 1, sb = sample >> 5) at elements
+//   T 64 MB + (jb MB / 32 + sb) 1024; within it, half u at 512 u, lane (l, h) at 8 lane: label
+//   32 (label >> 5) + l, samples 32 sb + 16 u + 8 h .. + 7.
 // Packing pairs to BF16 and swapping register groups 1 <-> 0 and 3 <-> 2 across the lane halves
-// leaves 8 consecutive samples per lane and group pair, written with one 16-byte store each into
-// the label's row `grow` of the label-major chunk buffer G[label][sample].
-__device__ __forceinline__ void fwd_store_block(const float (&gv)[16], uint16_t* grow, int bb, int hi) {
+// leaves each lane exactly those 8 samples of its label for u = 0 and 1, so each half of a block
+// leaves in one 16-byte store per lane, 1 KiB contiguous per wave. jc is any label of the block
+// (chunk-relative), bb its first sample.
+__device__ __forceinline__ void fwd_store_block(const float (&gv)[16], uint16_t* G, int MB, int jc, int bb, int lane) {
   uint32_t pk[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
+  uint16_t* blk = G + (int64_t)(jc >> 6) * 64 * MB + (((jc >> 5) & 1) * (MB / 32) + (bb >> 5)) * 1024 + lane * 8;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
     const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
     const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-    *(i32x4_t*)(grow + bb + 16 * u + 8 * hi) = out;
-  }
-}
-
-// The same 16-byte pieces into a wave's LDS staging rows instead (row `lrow`, byte column c0b of
-// the block's first sample): the rows then go out as whole 128-byte segments.
-__device__ __forceinline__ void fwd_stage_block(const float (&gv)[16], uint8_t* lrow, int c0b, int hi) {
-  uint32_t pk[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(gv[2 * k], gv[2 * k + 1]);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * u], pk[4 * u + 2], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * u + 1], pk[4 * u + 3], false, false);
-    const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-    *(i32x4_t*)(lrow + c0b + 32 * u + 16 * hi) = out;
+    *(i32x4_t*)(blk + 512 * u) = out;
   }
 }
 
 // The epilogue of a 128-label forward tile (4 waves; wave (wb, wj) holds samples wb RW .. + RW - 1
 // and labels wj CW .. + CW - 1 of the tile in 32 x 32 accumulator blocks): the gradient straight
-// from the accumulators, block by block, into the label-major chunk buffer G. With 128 or 256
-// samples each wave's rows of G (CW = 64 labels) are staged in LDS (`smem`, free after the K loop:
-// at least 4 CW 144 bytes) 64 samples at a time, so that every row leaves as one whole 128-byte
-// segment instead of 16-byte pieces of 32 rows. The loss partial of the tile goes to loss_part[lslot].
+// from the accumulators, block by block, into the chunk buffer G. The loss partial of the tile
+// goes to loss_part[lslot].
 template <int MB, int RW, int CW, bool LOSS, bool ZOUT>
 __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], uint8_t* smem,
                                              const uint32_t* ybits, float* lred, int tid, int wb, int wj,
@@ -119,9 +109,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], 
                                              int64_t zoff) {
   constexpr int MI = RW / 32, NI = CW / 32;
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  constexpr bool GST = MB >= 128 && !ZOUT;
-  constexpr int GSP = 144;                     // staging row pitch (bytes): 16 rows per bank cycle
-  uint8_t* gst = smem + wave * (CW * GSP);
+  (void)smem; (void)gpitch;
   float lsum = 0.0f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -149,19 +137,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], 
           }
         }
       }
-      if constexpr (GST) fwd_stage_block(gv, gst + (ni * 32 + l32) * GSP, (mi & 1) * 64, hi);
-      else if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)(jbase + jl) * gpitch, bb, hi);
-    }
-    if constexpr (GST) {
-      if (mi & 1) {                            // 64 samples of the wave's CW rows staged
-        const int sb0 = wb * RW + (mi - 1) * 32;
-#pragma unroll
-        for (int k = 0; k < CW / 8; ++k) {
-          const int row = k * 8 + (lane >> 3);
-          const i32x4_t v = *(const i32x4_t*)(gst + row * GSP + (lane & 7) * 16);
-          *(i32x4_t*)(G + (int64_t)(jbase + wj * CW + row) * gpitch + sb0 + (lane & 7) * 8) = v;
-        }
-      }
+      if constexpr (!ZOUT) fwd_store_block(gv, G, MB, jbase + jl, bb, lane);
     }
   }
   if constexpr (LOSS) {
@@ -496,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_xs(const uint8_t* __restrict__ W
           }
         }
       }
-      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)jc * gpitch, bb, hi);
+      if constexpr (!ZOUT) fwd_store_block(gv, G, MB, jc, bb, lane);
     }
   };
 
@@ -722,7 +698,8 @@ __device__ __forceinline__ void upd_phase(int p, UpdState& st, const f32x16_t& a
 //   dX^T[d][b] += sum_j W^T[d][j] G^T[j][b]    MB/32/NH sample blocks, K = 64 labels (MB/8/NH MFMAs)
 // with A = stationary X^T fragments in registers (dW), B = G rows by ds_read_b128 (dW), and
 // A = W^T, B = G^T by ds_read_b64_tr_b16 (dX). Per 64-label tile t:
-//   G tile  [64][MB] BF16 (label-major, as the forward kernel writes it), double buffered in two
+//   G tile  the chunk buffer's 64-label tile (contiguous, in the forward's 32 x 32 blocks), in LDS
+//           as [64][MB] BF16 label-major rows, double buffered in two
 //           LDS arrays used alternately by an unrolled pair of tiles; staged through registers
 //           (loaded at the start of the previous tile, written at its end) rather than with
 //           global_load_lds, whose in-flight LDS writes make the compiler drain every LDS read
@@ -890,7 +867,11 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   auto store_item = [&](auto K, uint16_t* gdst, int wb) {
     constexpr int k = decltype(K)::value;
     if constexpr (k < GPT) {
-      const int ci = tid + k * NT, row = ci / GCPR, ch = ci % GCPR;
+      // chunk ci of the tile's G blocks (lane (l, h) of half u of block (jb, sb)): label row
+      // 32 jb + l, 16-byte sample chunk 4 sb + 2 u + h
+      const int ci = tid + k * NT, cl = ci & 63, blk = ci >> 7;
+      const int row = 32 * (blk / (MB / 32)) + (cl & 31);
+      const int ch = 4 * (blk % (MB / 32)) + 2 * ((ci >> 6) & 1) + (cl >> 5);
       *(i32x4_t*)(gdst + row * MB + ((ch ^ row_swz<MB / 8>(row)) << 3)) = gst[k];
     } else {
       constexpr int c = k - GPT;
@@ -1217,7 +1198,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
           }
         }
       }
-      if constexpr (!ZOUT) fwd_store_block(gv, G + (int64_t)jc * gpitch, bb, hi);
+      if constexpr (!ZOUT) fwd_store_block(gv, G, MB, jc, bb, lane);
     }
     if (i + 1 < nmy) wstore((i + 1) & 1, stg);
     if (i + 1 < nmy) yscan(tile_of(i + 1), (i + 1) & 3);
