@@ -101,6 +101,26 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B,
                   uint64_t step, int64_t chunk, float* dX, float* loss_sum, void* workspace,
                   size_t workspace_bytes, void* stream);
 /*
+ * The same step as elmo_xmc_step computed in a single pass over the weights (summary page,
+ * "Approach": the classifier gradient fused with the SGD update; arXiv abstract: "gradient
+ * fusion"): one kernel per label chunk holds each 32-label weight tile in LDS while it computes the
+ * tile's logits, its gradient G (kept on chip), the tile's share of dX and the update, so the
+ * weights are read once and written once and no chunk of G goes to device memory. Built for
+ * B <= 32 and D = 256, 512 or 768 (every weight format): there each work-group keeps its B x D FP32
+ * dX accumulator in registers for the whole chunk; other shapes return ELMO_EUNSUPPORTED and
+ * enqueue nothing. Arguments, workspace (elmo_xmc_step_workspace_bytes), results and errors as
+ * elmo_xmc_step; the weights follow the same rule with the same random bits. Logits are summed in
+ * a different order than in elmo_xmc_step, so a gradient code can round the other way and move its
+ * row's updated weights; both paths meet the same tolerances against the rule.
+ *   g_out    nullable diagnostic: if given, [B, L] uint16 (2-byte aligned), receives the BF16
+ *            gradient codes the step used (costs a write of 2 B L bytes); otherwise untouched.
+ */
+int elmo_xmc_step_single_pass(void* W, int wdtype, int64_t L, int D, const void* X, int B,
+                              const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr,
+                              uint64_t seed, uint64_t step, int64_t chunk, float* dX,
+                              float* loss_sum, uint16_t* g_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+/*
  * The same step for callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): arguments, results and errors as elmo_xmc_step,
  * with the workspace replaced by a static device array of ELMO_NOALLOC_SCRATCH_BYTES bytes inside

@@ -59,6 +59,9 @@ def lib():
         L.elmo_xmc_step_workspace_bytes.restype = sz
         L.elmo_xmc_step.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P, sz, P]
         L.elmo_xmc_step.restype = i32
+        L.elmo_xmc_step_single_pass.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P,
+                                                P, sz, P]
+        L.elmo_xmc_step_single_pass.restype = i32
         L.elmo_xmc_step_flags.argtypes = [P, P, P]; L.elmo_xmc_step_flags.restype = i32
         L.elmo_xmc_step_noalloc.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P]
         L.elmo_xmc_step_noalloc.restype = i32
@@ -122,8 +125,11 @@ def step_workspace_bytes(B, D, L, chunk, wdtype, max_nnz):
     return int(lib().elmo_xmc_step_workspace_bytes(B, D, L, chunk, wdtype, max_nnz))
 
 
-def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, workspace=None, wfmt=None):
-    """One fused training step; W is updated in place. Returns (dX [B, D] float32, loss tensor|None)."""
+def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, workspace=None, wfmt=None,
+         single_pass=False, g_out=None):
+    """One fused training step; W is updated in place. Returns (dX [B, D] float32, loss tensor|None).
+    single_pass=True calls elmo_xmc_step_single_pass (B <= 32, D in 256/512/768) instead; g_out (an
+    int16 [B, L] device tensor) then receives the gradient codes it used."""
     _check_dev(W, X, row_ptr, ids)
     wd, L, D = _wdims(W, wfmt)
     B = X.shape[0]
@@ -136,10 +142,24 @@ def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, wo
         raise ElmoError("elmo_xmc_step_workspace_bytes", -2)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=W.device)
-    rc = lib().elmo_xmc_step(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None, nnz,
-                             float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss),
-                             _ptr(workspace), workspace.numel(), _stream())
-    _chk("elmo_xmc_step", rc)
+    if single_pass:
+        name = "elmo_xmc_step_single_pass"
+        if g_out is not None:
+            _check_dev(g_out)
+            if g_out.dtype != torch.int16 or tuple(g_out.shape) != (B, L):
+                raise ValueError("g_out must be an int16 [B, L] device tensor")
+        rc = lib().elmo_xmc_step_single_pass(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr),
+                                             _ptr(ids) if nnz else None, nnz, float(lr), int(seed), int(step),
+                                             int(chunk), _ptr(dX), _ptr(loss), _ptr(g_out), _ptr(workspace),
+                                             workspace.numel(), _stream())
+    else:
+        if g_out is not None:
+            raise ValueError("g_out is a diagnostic of the single-pass step")
+        name = "elmo_xmc_step"
+        rc = lib().elmo_xmc_step(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None, nnz,
+                                 float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss),
+                                 _ptr(workspace), workspace.numel(), _stream())
+    _chk(name, rc)
     global last_workspace
     last_workspace = workspace
     return dX, loss

@@ -27,6 +27,28 @@ int check_shapes(int B, int D, int64_t L) {
   return ELMO_OK;
 }
 
+int step_entry(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
+               const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk, float* dX,
+               float* loss_sum, uint16_t* g_out, void* workspace, size_t workspace_bytes, void* stream,
+               bool single) {
+  int rc = check_format(wdtype, D);
+  if (rc != ELMO_OK) return rc;
+  if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
+  if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
+  if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
+  if (single && !elmo::single_pass_shape(elmo::padded_batch(B), D)) return ELMO_EUNSUPPORTED;
+  if (!workspace || !aligned16(workspace)) return ELMO_EWORKSPACE;
+  const elmo::StepLayout s = elmo::step_layout(B, D, L, chunk, wdtype, nnz);
+  if (workspace_bytes < s.total) return ELMO_EWORKSPACE;
+  elmo::StepArgs a{};
+  a.W = W; a.wdtype = wdtype; a.L = L; a.D = D; a.X = X; a.B = B;
+  a.row_ptr = row_ptr; a.ids = ids; a.nnz = nnz; a.lr = lr; a.seed = seed; a.step = step;
+  a.dX = dX; a.loss = loss_sum; a.l0 = 0; a.l1 = L; a.Z = nullptr; a.single = single;
+  a.Gout = g_out;                        // (single pass only: its diagnostic gradient copy)
+  return elmo::run_step(a, s, workspace, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,20 +78,17 @@ size_t elmo_xmc_step_workspace_bytes(int B, int D, int64_t L, int64_t chunk, int
 int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
                   const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
                   float* dX, float* loss_sum, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_format(wdtype, D);
-  if (rc != ELMO_OK) return rc;
-  if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
-  if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
-  if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
-  if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
-  if (!workspace || !aligned16(workspace)) return ELMO_EWORKSPACE;
-  const elmo::StepLayout s = elmo::step_layout(B, D, L, chunk, wdtype, nnz);
-  if (workspace_bytes < s.total) return ELMO_EWORKSPACE;
-  elmo::StepArgs a{};
-  a.W = W; a.wdtype = wdtype; a.L = L; a.D = D; a.X = X; a.B = B;
-  a.row_ptr = row_ptr; a.ids = ids; a.nnz = nnz; a.lr = lr; a.seed = seed; a.step = step;
-  a.dX = dX; a.loss = loss_sum; a.l0 = 0; a.l1 = L; a.Z = nullptr;
-  return elmo::run_step(a, s, workspace, (hipStream_t)stream);
+  return step_entry(W, wdtype, L, D, X, B, row_ptr, ids, nnz, lr, seed, step, chunk, dX, loss_sum, nullptr,
+                    workspace, workspace_bytes, stream, false);
+}
+
+int elmo_xmc_step_single_pass(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
+                              const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step,
+                              int64_t chunk, float* dX, float* loss_sum, uint16_t* g_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (g_out && ((uintptr_t)g_out & 1u)) return ELMO_EINVAL;
+  return step_entry(W, wdtype, L, D, X, B, row_ptr, ids, nnz, lr, seed, step, chunk, dX, loss_sum, g_out,
+                    workspace, workspace_bytes, stream, true);
 }
 
 int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,

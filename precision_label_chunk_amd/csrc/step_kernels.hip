@@ -332,6 +332,10 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   int cap = s.cus / s.NS;
   if (cap < 1) cap = 1;
   s.NR = (int)(nt2 < cap ? nt2 : cap);
+  // the single-pass step runs one work-group per CU over 32-label tiles, each with its own partial
+  const int64_t nt1 = (c + 31) / 32;
+  s.NR1 = single_pass_shape(s.MB, D) ? (int)(nt1 < s.cus ? nt1 : s.cus) : 0;
+  const int nslots = s.NR > s.NR1 ? s.NR : s.NR1;
   size_t off = 0;
   const size_t A = 256;
   s.flags = off;    off = align_up(off + 64, A);
@@ -342,7 +346,7 @@ StepLayout step_layout(int B, int D, int64_t L, int64_t chunk, int wdtype, int64
   s.xq = off;       off = align_up(off + (wdtype != W_BF16_ ? (size_t)s.MB * D : 0), A);
   s.xbt = off;      off = align_up(off + 2 * (size_t)s.MB * D, A);
   s.g = off;        off = align_up(off + 2 * (size_t)s.MB * (size_t)s.Cc, A);
-  s.part = off;     off = align_up(off + 4 * (size_t)s.NR * s.MB * D, A);
+  s.part = off;     off = align_up(off + 4 * (size_t)nslots * s.MB * D, A);
   // loss partials: one slot per 128-, 64- or 32-label tile of the forward kernel in use
   s.loss = off;     off = align_up(off + 4 * (size_t)(4 * s.ntiles + 4), A);
   s.total = off;
@@ -367,8 +371,9 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
     hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, st, (uint32_t*)(ws + s.loss), 4 * s.ntiles + 4, 0u);
     LAUNCH_CHECK();
   }
-  if (!a.forward_only()) {
+  if (!a.forward_only() && !a.single) {
     // the first chunk stores all partial slots unless it has fewer label ranges than there are slots
+    // (the single-pass kernel always launches one work-group per slot)
     const int64_t clen0 = (a.l1 - a.l0) < s.Cc ? (a.l1 - a.l0) : s.Cc;
     if ((clen0 + TJ2 - 1) / TJ2 < s.NR) {
       hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, st, (uint32_t*)(ws + s.part),
@@ -400,7 +405,10 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   }
   int rc;
   const int MB = s.MB;
-  if (a.wdtype == W_BF16_) {
+  if (a.single) {
+    rc = a.wdtype == W_BF16_ ? run_single<W_BF16_>(a, s, ws, st)
+       : a.wdtype == W_E4M3_ ? run_single<W_E4M3_>(a, s, ws, st) : run_single<W_MXFP4_>(a, s, ws, st);
+  } else if (a.wdtype == W_BF16_) {
     rc = MB == 32 ? run_chunks<32, W_BF16_>(a, s, ws, st) : MB == 64 ? run_chunks<64, W_BF16_>(a, s, ws, st)
        : MB == 128 ? run_chunks<128, W_BF16_>(a, s, ws, st) : run_chunks<256, W_BF16_>(a, s, ws, st);
   } else if (a.wdtype == W_E4M3_) {
@@ -414,7 +422,7 @@ int run_step(const StepArgs& a, const StepLayout& s, void* workspace, hipStream_
   {
     const int64_t n = (int64_t)s.MB * a.D;
     const int blocks = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
-    hipLaunchKernelGGL(k_dx_reduce, dim3(blocks), dim3(256), 0, st, (const float*)(ws + s.part), s.NR, s.MB,
+    hipLaunchKernelGGL(k_dx_reduce, dim3(blocks), dim3(256), 0, st, (const float*)(ws + s.part), a.single ? s.NR1 : s.NR, s.MB,
                        a.D, a.B, a.dX);
     LAUNCH_CHECK();
   }

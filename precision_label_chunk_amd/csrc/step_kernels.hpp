@@ -35,6 +35,7 @@ __host__ __device__ constexpr int fwd_x_layout(int MB, int wf, int D) {
 
 struct StepLayout {
   int MB, DS, NS, NR;
+  int NR1;                              // single-pass work-groups (label ranges); 0 where not built
   int cus;                              // compute units of the device
   int64_t Cc, ntiles;
   size_t flags, tile_cnt, tile_off, bucket, xb, xq, xbt, g, part, loss, total;
@@ -47,8 +48,10 @@ struct StepArgs {
   float* dX; float* loss;
   int64_t l0, l1;                       // label range processed (whole [0, L) for a step)
   // forward-only diagnostic: logits Z and/or gradient codes Gout, [B][zpitch] with column = label - zoff
+  // (for the single-pass step, Gout is its optional copy of the gradient codes, [B][L])
   float* Z; uint16_t* Gout; int64_t zpitch; int64_t zoff;
-  bool forward_only() const { return Z != nullptr || Gout != nullptr; }
+  bool single;                          // the single-pass kernel instead of the two chunk kernels
+  bool forward_only() const { return !single && (Z != nullptr || Gout != nullptr); }
 };
 
 // Optional per-launch HIP-event timing of the two chunk kernels (a measurement aid; off by default).
@@ -79,6 +82,15 @@ extern template int run_chunks<32, W_MXFP4_>(const StepArgs&, const StepLayout&,
 extern template int run_chunks<64, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 extern template int run_chunks<128, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 extern template int run_chunks<256, W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+
+// the single-pass step (step_single.hip): built for padded batches of 32 samples and D = 256, 512
+// or 768
+__host__ __device__ constexpr bool single_pass_shape(int MB, int D) { return MB == 32 && (D == 256 || D == 512 || D == 768); }
+template <int WF>
+int run_single(const StepArgs& a, const StepLayout& s, uint8_t* ws, hipStream_t st);
+extern template int run_single<W_BF16_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_single<W_E4M3_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
+extern template int run_single<W_MXFP4_>(const StepArgs&, const StepLayout&, uint8_t*, hipStream_t);
 
 // top-k
 struct TopkLayout { int MB, NRg; int64_t ncand; size_t xb, xq, cand_s, cand_i, total; };

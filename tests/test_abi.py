@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["elmo_xmc_step", "elmo_xmc_topk", "elmo_xmc_step_workspace_bytes", "elmo_xmc_topk_workspace_bytes",
               "elmo_xmc_logits", "elmo_numerics_probe", "elmo_status_str", "elmo_abi_version", "elmo_xmc_step_flags",
-              "elmo_kahan_update"]:
+              "elmo_kahan_update", "elmo_xmc_step_single_pass"]:
         assert n in names
 
 
@@ -99,3 +99,32 @@ def test_kahan_update_rejects_invalid_arguments(L):
     assert L.elmo_kahan_update(None, p, p, 8, 0.1, None) == -1
     assert L.elmo_kahan_update(p, p, ctypes.c_void_p(4098), 8, 0.1, None) == -1   # misaligned g
     assert L.elmo_kahan_update(ctypes.c_void_p(4097), p, p, 8, 0.1, None) == -1   # misaligned w
+
+
+def test_single_pass_step_rejects_shapes_it_does_not_build(L):
+    null = None
+    p = ctypes.c_void_p(4096)
+    f = L.elmo_xmc_step_single_pass
+    f.restype = ctypes.c_int
+    # the same host validation as elmo_xmc_step
+    assert f(null, 5, 1000, 768, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, null, 0, null) == -3
+    assert f(null, 0, 1000, 100, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, null, 0, null) == -2
+    assert f(p, 0, 1000, 768, p, 4, p, p, 1, float("nan"), 0, 0, 128, p, null, null, p, 1 << 30, null) == -1
+    # built for B <= 32 and D in {256, 512, 768} only: other valid shapes are unsupported, nothing runs
+    assert f(p, 0, 1000, 768, p, 33, p, p, 1, 0.1, 0, 0, 128, p, null, null, p, 1 << 30, null) == -6
+    assert f(p, 1, 1000, 640, p, 8, p, p, 1, 0.1, 0, 0, 128, p, null, null, p, 1 << 30, null) == -6
+    assert f(p, 0, 1000, 1024, p, 8, p, p, 1, 0.1, 0, 0, 128, p, null, null, p, 1 << 30, null) == -6
+    # workspace too small for a supported shape; a misaligned gradient-code output
+    assert f(p, 0, 1000, 768, p, 32, p, p, 1, 0.1, 0, 0, 128, p, null, null, p, 16, null) == -4
+    assert f(p, 0, 1000, 768, p, 32, p, p, 1, 0.1, 0, 0, 128, p, null, ctypes.c_void_p(4097), p, 1 << 30,
+             null) == -1
+
+
+def test_workspace_holds_the_single_pass_partials():
+    """At padded batch 32 and D = 768 the workspace has room for one dX partial (32 x 768 FP32) per
+    single-pass work-group, up to one per CU (or per 32-label tile of the chunk, if fewer)."""
+    import precision_label_chunk_amd as elmo
+    small = elmo.step_workspace_bytes(32, 768, 4096, 1024, 0, 100)
+    big = elmo.step_workspace_bytes(32, 768, 8_600_000, 262_144, 0, 100)
+    assert small >= 32 * (32 * 768 * 4)
+    assert big >= 256 * (32 * 768 * 4)
