@@ -55,6 +55,13 @@ def parse():
                     help="a third workload in its own object of the line ('none' to skip): by default the "
                          "3M-label head with MX-scaled FP4 weights")
     ap.add_argument("--steps-third", type=int, default=10, help="timed steps of the third workload")
+    ap.add_argument("--single-pass-workloads", default="bf16_8p6m_b32,e4m3_3m_b32",
+                    help="comma-separated workloads (B <= 32) timed with the single-pass step and the two-kernel "
+                         "step side by side, or 'none'")
+    ap.add_argument("--steps-single", type=int, default=10, help="timed steps of each single-pass comparison")
+    ap.add_argument("--single-pass", action="store_true",
+                    help="run the main workload (B <= 32) with the single-pass step (for profiling it alone); "
+                         "with --summarize-traffic: the file's commands carry this flag")
     ap.add_argument("--kahan-params", type=int, default=110_000_000,
                     help="encoder parameters of the Kahan-compensated BF16 update pass (768-wide, 12 layers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -143,7 +150,7 @@ def _kernel_key(name):
     return name.replace("elmo::", "").replace(" ", "")
 
 
-def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, single=False):
     """The HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled by what the same counter reads for a plain copy of known size (read and written once)."""
     def copy_factor(folder, counter):
@@ -160,11 +167,12 @@ def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 2 "
               f"--warmup 1 --no-cpu-baseline --no-topk --no-kahan --second-workload none --third-workload none "
-              f"--workload {workload}")
+              f"--single-pass-workloads none --workload {workload}{' --single-pass' if single else ''}")
     for c, d in (("FETCH_SIZE", copy_fetch_dir), ("WRITE_SIZE", copy_write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
               f"--copy-bytes 1073741824")
-    print(f"#   python3 bench.py --summarize-traffic {workload} {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}")
+    print(f"#   python3 bench.py --summarize-traffic {workload} {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}"
+          f"{' --single-pass' if single else ''}")
     print(f"source_sha256 {kernel_source_hash()}")
     print(f"copy_fetch_size_kib {cf:.1f} factor {ff:.4f}")
     print(f"copy_write_size_kib {cw:.1f} factor {fw:.4f}")
@@ -326,7 +334,7 @@ def cpu_info():
     return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
-def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
+def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True, single=False):
     """One workload: W resident in HBM, `warmup` untimed steps (the first timed on its own), `steps`
     timed steps with no event between kernels, then the same number again with events around every
     forward and backward launch for the per-kernel averages; the top-k pass; the CPU oracle on a
@@ -369,7 +377,8 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
         X, rp, ids = batches[s]
         if s == 0:
             evc[0].record(stream)
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt,
+                  single_pass=single)
         if s == 0:
             evc[1].record(stream)
     torch.cuda.synchronize()
@@ -381,7 +390,8 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     ev0.record(stream)
     for s in range(warmup, nb):
         X, rp, ids = batches[s]
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt,
+                  single_pass=single)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -395,7 +405,8 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     evs[0].record(stream)
     for i, s in enumerate(range(warmup, nb)):
         X, rp, ids = batches[s]
-        elmo.step(W, X, rp, ids, wl.lr, wl.seed, nb + s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt)
+        elmo.step(W, X, rp, ids, wl.lr, wl.seed, nb + s, wl.chunk, dX=dX, workspace=ws, wfmt=wl.wfmt,
+                  single_pass=single)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     elmo.kernel_timing(False)
@@ -421,9 +432,13 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     # per-kernel rooflines from the live per-launch events. Algorithmic work per label: forward
     # 2 B D flops and D w bytes (W read); backward 4 B D flops and 2 D w bytes (W read and write).
     # A kernel is MFMA- or HBM-bound by its arithmetic intensity against the ridge point.
+    # The single-pass kernel (timed in the backward's slot) does the whole step's work per label:
+    # 6 B D flops on the BF16 matrix cores and 2 D w bytes (W read and written once).
     kern = {}
-    for kn, per_label_f, per_label_b, peak_f in (("bwd", 4.0 * B * D, 2.0 * D * wl.wbytes, PEAK["bf16"]),
-                                                  ("fwd", 2.0 * B * D, 1.0 * D * wl.wbytes, fwd_peak)):
+    per_kernel = ((("bwd", 6.0 * B * D, 2.0 * D * wl.wbytes, PEAK["bf16"]),) if single else
+                  (("bwd", 4.0 * B * D, 2.0 * D * wl.wbytes, PEAK["bf16"]),
+                   ("fwd", 2.0 * B * D, 1.0 * D * wl.wbytes, fwd_peak)))
+    for kn, per_label_f, per_label_b, peak_f in per_kernel:
         ms, n, labels = kt[kn]
         if not n:
             continue
@@ -442,7 +457,7 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True):
     fwd_kernel = ("k_fwd_xs" if wl.wfmt != wk.W_BF16 and D == 768 and B > 128 else
                   "k_fwd_xb" if wl.wfmt == wk.W_BF16 and D == 768 and 64 < B <= 128 else
                   "k_fwd_mx" if wl.wfmt == wk.W_MXFP4 else "k_fwd_g")
-    kname = {"bwd": "k_bwd_update", "fwd": fwd_kernel}
+    kname = {"bwd": "k_step_single" if single else "k_bwd_update", "fwd": fwd_kernel}
     scale = 1e9 if kd["unit"] == "GB/s" else 1e12
     tr = measured_traffic(name, kname[dom])
     roofline = {"kernel": kname[dom], "bound": kd["bound"],
@@ -521,7 +536,7 @@ def main():
         summarize_counters(args.summarize_counters)
         return
     if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic)
+        summarize_traffic(*args.summarize_traffic, single=args.single_pass)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -541,7 +556,7 @@ def main():
     elmo.lib()
 
     main_w = bench_workload(args.workload, args.steps, args.warmup, args, with_topk=not args.no_topk,
-                            with_cpu=not args.no_cpu_baseline)
+                            with_cpu=not args.no_cpu_baseline, single=args.single_pass)
     out = {"metric": METRIC, "value": main_w["samples_s"], "unit": "samples/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_w["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -563,6 +578,17 @@ def main():
         if name != "none":
             out[name] = bench_workload(name, nsteps, 2, args, with_topk=not args.no_topk,
                                        with_cpu=not args.no_cpu_baseline)
+
+    # the single-pass step beside the two-kernel step on the same small-batch workloads
+    sp = [w for w in args.single_pass_workloads.split(",") if w and w != "none"]
+    if sp:
+        out["single_pass"] = {}
+        for name in sp:
+            one = bench_workload(name, args.steps_single, 2, args, with_topk=False, with_cpu=False, single=True)
+            two = bench_workload(name, args.steps_single, 2, args, with_topk=False, with_cpu=False)
+            out["single_pass"][name] = {
+                "single_pass": one, "two_kernel": two,
+                "speedup": round(two["ms_per_step"] / one["ms_per_step"], 3)}
 
     info = cpu_info()
     for obj in [out] + [out.get(name, {}) for name, _ in extra]:

@@ -111,3 +111,38 @@ def test_full_size_topk_sampled_queries(elmo, orc, name):
     Zr = orc.logits_dense(wl.wfmt, W0, Xe[qs])
     oi, osc = orc.rank_scores(Zr, k)
     check_topk_rows(idx[qs], score[qs], oi, osc, Zg, Zr, label=f" {wl.name}")
+
+
+@pytest.mark.parametrize("name", ["bf16_8p6m_b32", "e4m3_3m_b32"])
+def test_full_size_single_pass_sampled(elmo, orc, name):
+    """The single-pass step at full size (8.6M BF16 / 3M E4M3 labels, B = 32) in the benchmark's
+    launch configuration: the sampled rows' gradient codes (from its diagnostic copy) and updated
+    weights against the oracle's own step, and dX rows over all labels."""
+    wl = wk.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"  {wl.name}: single pass, B={wl.B} D={wl.D} L={wl.L} chunk={wl.chunk}", flush=True)
+    W = wk.make_w_device(wl.L, wl.D, wl.wfmt, seed=wl.seed, device=dev)
+    W0 = _host_codes(W)
+    bt = wk.make_batch(wl, step=0)
+    X, rp, ids = batch_to_dev(bt)
+    js = _sample_labels(wl)
+    g = torch.zeros((wl.B, wl.L), dtype=torch.int16, device=dev)
+    dX, _ = elmo.step(W, X, rp, ids, wl.lr, wl.seed, 0, wl.chunk, wfmt=wl.wfmt, single_pass=True, g_out=g)
+    torch.cuda.synchronize()
+    jd = torch.from_numpy(js).to(dev)
+    Wg = _host_codes(W[jd])
+    Gg = g[:, jd].cpu().numpy().view(np.uint16)
+    del g
+    assert elmo.step_flags(elmo.last_workspace) == 0
+    Wf, Gr, Tf = orc.update_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, wl.lr, wl.seed, 0, js, want_detail=True)
+    flips = assert_grad_codes_match(Gg, Gr)
+    R = np.stack([orc.r16(wl.seed, 0, int(j) * wl.D, wl.D) for j in js])
+    c = assert_weights_free_running(orc, Wg, Wf, Tf, R, wl.wfmt, bt.X, Gg, Gr, wl.lr, label=f" ({js.size} rows)")
+    Wtf = orc.update_rows_from_g(wl.wfmt, W0, bt.X, Gg, wl.lr, wl.seed, 0, js)
+    eq_tf = weight_report(Wg, Wtf, wl.wfmt)[0]
+    assert eq_tf >= 0.999, f"weights given the device's gradient codes only {eq_tf:.6f} equal"
+    bs = np.array([0, 17, wl.B - 1], np.int32)
+    dXr = orc.dx_rows(wl.wfmt, W0, bt.X, bt.row_ptr, bt.ids, bs)
+    edx = assert_close(dX.cpu().numpy()[bs], dXr, RTOL[wl.wfmt])
+    print(f"  G flips {flips:.2e}  W equal {c['equal'] / c['n']:.6f} (given device G {eq_tf:.6f})  dX rel {edx:.2e}",
+          flush=True)

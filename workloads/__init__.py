@@ -74,6 +74,11 @@ WORKLOADS = {
                          "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=5),
     "mxfp4_131k": Workload("xmc-mxfp4-L131072-D768-B256", 256, 768, 131072, 32768, W_MXFP4, 0.1, 10,
                            "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=6),
+    # the 8.6M- and 3M-label heads at a batch of 32 samples, where the single-pass step applies
+    "bf16_8p6m_b32": Workload("xmc-bf16-L8600000-D768-B32", 32, 768, 8600000, 262144, W_BF16, 0.05, 5,
+                              "rownorm", "zipf", lam=9.0, zipf_s=1.2, tag=7),
+    "e4m3_3m_b32": Workload("xmc-e4m3-L3000000-D768-B32", 32, 768, 3000000, 131072, W_E4M3, 0.1, 10,
+                            "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=8),
 }
 
 
