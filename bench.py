@@ -126,7 +126,7 @@ def summarize_counters(folders):
     for folder in folders:
         for r in _csv_rows(folder, "counter_collection.csv"):
             name = _kernel_key(r["Kernel_Name"])
-            if not (name.startswith("k_bwd_update") or name.startswith("k_fwd")):
+            if not (name.startswith("k_bwd_update") or name.startswith("k_fwd") or name.startswith("k_step_single")):
                 continue
             d = table.setdefault(r["Counter_Name"], {}).setdefault(name, {})
             d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])

@@ -27,10 +27,10 @@
 //   3. dW^T[d][j] = sum_b X^T[d][b] G[b][j] over the wave's NFW feature blocks (A = stationary X^T
 //      fragments, B = G rows) and dX^T[d][b] += sum_j W_t^T[d][j] G^T[j][b] (A = W^T, B = G^T, both
 //      transposing LDS reads); the dX^T accumulators live in registers for the whole launch;
-//   4. the update of the wave's 32 x 32 blocks from the dW accumulators (the same code as the
-//      two-kernel backward: Philox draws, fmaf, hardware SR), stored in place;
-//   5. the next tile, loaded into registers at the start of the iteration, is decoded to BF16 into
-//      the other LDS buffer, and its positives gathered into label bits.
+//   4. the next tile, loaded into registers at the start of the iteration, is decoded to BF16 into
+//      the other LDS buffer, and its positives gathered into label bits;
+//   5. the update of the wave's 32 x 32 blocks from the dW accumulators (the same code as the
+//      two-kernel backward: Philox draws, fmaf, hardware SR), stored in place.
 // Three barriers per tile. At the end each work-group stores its dX^T accumulators as its range's
 // running partial (the two-kernel step's partial layout), which the step's fixed-order reduction
 // sums. X~ is X for BF16 weights and E4M3-RNE(X) for E4M3 and MXFP4 weights, decoded to BF16
@@ -215,6 +215,10 @@ __global__ __launch_bounds__(512, 1) void k_step_single(uint8_t* __restrict__ W,
     yscan(t0, 0);
     __syncthreads();
   }
+  // every prologue load done here (one wait), so that no wait for them lands inside the loop (the
+  // compiler would otherwise wait on the vector-memory counter, which the loop's stores share,
+  // every iteration)
+  __builtin_amdgcn_s_waitcnt(0);
   for (int i = 0; t0 + i < t1; ++i) {
     const int t = t0 + i, buf = i & 1;
     const uint16_t* ws = Ws[buf];
@@ -247,8 +251,21 @@ __global__ __launch_bounds__(512, 1) void k_step_single(uint8_t* __restrict__ W,
       const uint32_t yw = ybits[i & 3][l32];
       const bool y0 = (yw >> b0) & 1u, y1 = (yw >> (b0 + 1)) & 1u;
       const bool v0 = jvalid && b0 < B, v1 = jvalid && b0 + 1 < B;
-      const float g0 = v0 ? bce_grad(z0, y0) : 0.0f;
-      const float g1 = v1 ? bce_grad(z1, y1) : 0.0f;
+      // the gradient forms chosen per wave as in the two-kernel forward: the short forms when every
+      // element is valid and |z| <= 80 (<= 2: the small-argument form), else the exact selection
+      float g0, g1;
+      const float m = fmaxf(__builtin_fabsf(z0), __builtin_fabsf(z1));
+      if (__builtin_amdgcn_ballot_w64(!(m <= 80.0f && v0 && v1)) == 0) {
+        const uint32_t m0 = y0 ? 0x80000000u : 0u, m1 = y1 ? 0x80000000u : 0u;
+        if (__builtin_amdgcn_ballot_w64(m > 2.0f) == 0) {
+          g0 = bce_grad_small_m(z0, m0); g1 = bce_grad_small_m(z1, m1);
+        } else {
+          g0 = bce_grad_fast_m(z0, m0); g1 = bce_grad_fast_m(z1, m1);
+        }
+      } else {
+        g0 = v0 ? bce_grad(z0, y0) : 0.0f;
+        g1 = v1 ? bce_grad(z1, y1) : 0.0f;
+      }
       if constexpr (LOSS) {
         if (v0) lsum += bce_loss(z0, y0);
         if (v1) lsum += bce_loss(z1, y1);
@@ -263,8 +280,7 @@ __global__ __launch_bounds__(512, 1) void k_step_single(uint8_t* __restrict__ W,
     }
     __syncthreads();
 
-    // 3. the tile's dX contribution over the wave's feature blocks; 4. per feature block, dW and
-    // the update of the wave's 32 x 32 block, in place (one block's dW live at a time)
+    // 3. the tile's dX contribution over the wave's feature blocks
     {
       const s16x8_t gt0 = join(lds_read_tr16(Gs + offB0), lds_read_tr16(Gs + offB1));
       const s16x8_t gt1 = join(lds_read_tr16(Gs + offB0 + 16 * MB), lds_read_tr16(Gs + offB1 + 16 * MB));
@@ -276,6 +292,14 @@ __global__ __launch_bounds__(512, 1) void k_step_single(uint8_t* __restrict__ W,
         accX[f] = mfma_bf16(a1, gt1, accX[f]);
       }
     }
+    // 4. the next tile (loaded at the top) into the other buffer, and its positives, before the
+    // update (the staging registers are then free across it)
+    if (t + 1 < t1) {
+      wstore(buf ^ 1);
+      yscan(t + 1, (i + 1) & 3);
+    }
+    // 5. per feature block, dW and the update of the wave's 32 x 32 block, in place (one block's dW
+    // live at a time)
     {
       const s16x8_t g0 = *(const s16x8_t*)(Gs + offW[0]), g1 = *(const s16x8_t*)(Gs + offW[1]);
       const int ro = (t * TJ + l32) * RB;
@@ -296,11 +320,6 @@ __global__ __launch_bounds__(512, 1) void k_step_single(uint8_t* __restrict__ W,
       }
     }
 
-    // 5. the next tile into the other buffer, its positives
-    if (t + 1 < t1) {
-      wstore(buf ^ 1);
-      yscan(t + 1, (i + 1) & 3);
-    }
     yclear((i + 2) & 3);
     __syncthreads();
   }
