@@ -55,6 +55,8 @@ def parse():
                     help="a third workload in its own object of the line ('none' to skip): by default the "
                          "3M-label head with MX-scaled FP4 weights")
     ap.add_argument("--steps-third", type=int, default=10, help="timed steps of the third workload")
+    ap.add_argument("--small-workloads", default="bf16_131k,bf16_670k",
+                    help="comma-separated further workloads timed without top-k and CPU baseline, or 'none'")
     ap.add_argument("--single-pass-workloads", default="bf16_8p6m_b32,e4m3_3m_b32",
                     help="comma-separated workloads (B <= 32) timed with the single-pass step and the two-kernel "
                          "step side by side, or 'none'")
@@ -416,7 +418,11 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True, sin
     h = len(per_step) // 2
     events_median = per_step[h] if len(per_step) % 2 else 0.5 * (per_step[h - 1] + per_step[h])
     peak_hbm = torch.cuda.max_memory_allocated(dev)
-    free_b, total_b = torch.cuda.mem_get_info(dev)   # hipMemGetInfo: the device's own view, for comparison
+    # hipMemGetInfo, the device's own view, with torch's cached free blocks returned first: what it
+    # reports beyond the live allocations is the runtime's own memory (context, code objects)
+    live = torch.cuda.memory_allocated(dev)
+    torch.cuda.empty_cache()
+    free_b, total_b = torch.cuda.mem_get_info(dev)
     reserved = torch.cuda.memory_reserved(dev)
 
     B, D, L = wl.B, wl.D, wl.L
@@ -493,7 +499,8 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True, sin
            "peak_hbm_bytes": int(peak_hbm),
            "peak_hbm_breakdown": {k: int(v) for k, v in hbm_parts.items()},
            "peak_hbm_budget_bytes": int(L * D * wl.wbytes + 2 * B * wl.chunk + 64 * 2**20),
-           "device_used_bytes": int(total_b - free_b), "torch_reserved_bytes": int(reserved),
+           "device_used_bytes": int(total_b - free_b), "live_bytes": int(live),
+           "device_used_beyond_live_bytes": int(total_b - free_b - live), "torch_reserved_bytes": int(reserved),
            "weights_bytes": int(L * D * wl.wbytes),
            "roofline": roofline}
 
@@ -562,7 +569,8 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": main_w["dtype"], "data": "synthetic", "config": main_w["config"]}
     for key in ("first_step_ms", "tflops", "mfma_roofline_frac", "alg_hbm_gbs", "hbm_frac", "peak_hbm_bytes",
-                "peak_hbm_breakdown", "peak_hbm_budget_bytes", "device_used_bytes", "torch_reserved_bytes",
+                "peak_hbm_breakdown", "peak_hbm_budget_bytes", "device_used_bytes", "live_bytes",
+                "device_used_beyond_live_bytes", "torch_reserved_bytes",
                 "weights_bytes", "roofline", "topk", "cpu_baseline"):
         if key in main_w:
             out[key] = main_w[key]
@@ -578,6 +586,10 @@ def main():
         if name != "none":
             out[name] = bench_workload(name, nsteps, 2, args, with_topk=not args.no_topk,
                                        with_cpu=not args.no_cpu_baseline)
+
+    # the 131k- and 670k-label BF16 heads (B = 256), each in an object of its own
+    for name in [w for w in args.small_workloads.split(",") if w and w != "none"]:
+        out[name] = bench_workload(name, args.steps_third, 2, args, with_topk=False, with_cpu=False)
 
     # the single-pass step beside the two-kernel step on the same small-batch workloads
     sp = [w for w in args.single_pass_workloads.split(",") if w and w != "none"]

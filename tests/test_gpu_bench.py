@@ -1,7 +1,8 @@
 """The benchmark's output contract on small workloads: one JSON line with the metric, the
 whole-step throughput, the dominant kernel's roofline from live event timing, the top-k pass and
-the CPU oracle baselines (with their bounded samples and the host CPU), and the second workload's
-object measured the same way."""
+the CPU oracle baselines (with their bounded samples and the host CPU), the second and third
+workloads' objects measured the same way, a further workload's object without top-k, and the
+single-pass step beside the two-kernel step on a 32-sample workload."""
 import json
 import os
 import subprocess
@@ -16,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_json_line_on_the_tiny_workload():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3", "--warmup", "1",
            "--topk-n", "64", "--kahan-params", "100000", "--cpu-seconds", "0.3", "--second-workload", "bf16_131k",
-           "--steps-8p6m", "2", "--third-workload", "mxfp4_131k", "--steps-third", "2"]
+           "--steps-8p6m", "2", "--third-workload", "mxfp4_131k", "--steps-third", "2",
+           "--small-workloads", "bf16_670k", "--single-pass-workloads", "e4m3_3m_b32", "--steps-single", "2"]
     print("  " + " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -28,6 +30,8 @@ def test_bench_json_line_on_the_tiny_workload():
                 "kahan_update", "first_step_ms", "peak_hbm_bytes"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
+    # the device's own count of used memory, torch's cached blocks returned, covers the live allocations
+    assert d["device_used_bytes"] >= d["live_bytes"] > 0
     assert d["config"]["workload"] == "xmc-bf16-L4096-D64-B32"
     ro = d["roofline"]
     # B = 32, D = 64: the backward's 4 B D flops per 2 D w bytes (32 flop/B) sit below the ridge point
@@ -50,3 +54,9 @@ def test_bench_json_line_on_the_tiny_workload():
     # (B = 256, MXFP4: the backward moves 2 * 17 D / 32 bytes per 4 B D flops, 964 flop/B: above the
     # BF16 ridge point; at 256 samples and D = 768 the forward is the stationary-feature kernel)
     assert s3["roofline"]["bound"] == "mfma" and s3["roofline"]["other_kernel"]["kernel"] == "k_fwd_xs"
+    s4 = d["bf16_670k"]
+    assert s4["config"]["L"] == 670000 and s4["samples_s"] > 0 and "topk" not in s4
+    sp = d["single_pass"]["e4m3_3m_b32"]
+    assert sp["single_pass"]["roofline"]["kernel"] == "k_step_single" and sp["single_pass"]["roofline"]["bound"] == "hbm"
+    assert sp["two_kernel"]["roofline"]["kernel"] == "k_bwd_update"
+    assert sp["speedup"] == pytest.approx(sp["two_kernel"]["ms_per_step"] / sp["single_pass"]["ms_per_step"], rel=1e-2)
