@@ -12,10 +12,10 @@
 // Why only B <= 32: the input gradient dX = G W_old reduces over every label into a B x D FP32
 // accumulator. A work-group that owns whole weight rows (which the logits need) can keep that
 // accumulator in registers for the whole launch only while B x D x 4 bytes, the stationary
-// features in both fragment orders and the dW accumulators fit beside each other: at D = 768 that
-// is 96 KiB + 2 x 48 KiB + 96 KiB of the 512 KiB register file at 32 samples, and twice as much at
-// 64 (with the 8 waves' per-wave limit of 256 registers, over it). Wider batches keep the two-kernel
-// step of step_chunks.hip.
+// features in both fragment orders and the dW accumulators of one 32 x 32 block per wave fit beside
+// the update's own state: at D = 768 that is 96 KiB + 2 x 48 KiB + 32 KiB of the 512 KiB register
+// file at 32 samples (243-247 of a wave's 256 registers in use), and the first three double at 64
+// samples. Wider batches keep the two-kernel step of step_chunks.hip.
 //
 // Work-group (one per CU, 8 waves, a contiguous range of the chunk's 32-label tiles): wave w owns
 // features [32 NFW w, 32 NFW (w + 1)) (NFW = D / 256 feature blocks of 32). Per tile:
