@@ -366,7 +366,9 @@ def bench_workload(name, steps, warmup, args, with_topk=True, with_cpu=True, sin
     dX = torch.empty((wl.B, wl.D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     # the step's peak HBM counts what is resident while it runs (the library allocates nothing),
-    # not the transients of generating the weights
+    # not the transients of generating the weights, nor the previous workload's workspace, which the
+    # binding keeps as its last one (for step_flags) until the next step replaces it
+    elmo.last_workspace = None
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats(dev)
     hbm_parts = {"weights": W.numel() * W.element_size(), "workspace": ws.numel(),
