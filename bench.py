@@ -169,7 +169,8 @@ def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 2 "
               f"--warmup 1 --no-cpu-baseline --no-topk --no-kahan --second-workload none --third-workload none "
-              f"--single-pass-workloads none --workload {workload}{' --single-pass' if single else ''}")
+              f"--single-pass-workloads none --small-workloads none --workload {workload}"
+              f"{' --single-pass' if single else ''}")
     for c, d in (("FETCH_SIZE", copy_fetch_dir), ("WRITE_SIZE", copy_write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
               f"--copy-bytes 1073741824")
