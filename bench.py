@@ -255,16 +255,23 @@ def measured_traffic(workload, kernel):
 
 
 def copy_reference(nbytes):
-    """A plain copy of `nbytes` bytes, three times: each launch reads and writes exactly nbytes."""
+    """A plain copy of `nbytes` bytes, three times: each launch reads and writes exactly nbytes. Also
+    reports the copy's own rate (bytes read plus written per second, HIP events around the three
+    launches): a practical ceiling for kernels that read and write HBM, beside the spec peak."""
     import torch
     dev = torch.device("cuda:0")
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(3):
         b.copy_(a)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+    ms = e0.elapsed_time(e1) / 3
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3, "ms_per_copy": round(ms, 4),
+                      "read_write_gbs": round(2 * nbytes / (ms / 1e3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(wl, W_dev, batch, target_s):
