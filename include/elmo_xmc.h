@@ -91,6 +91,10 @@ const char* elmo_status_str(int status);
  * Per element: z = X~ . w_j (X~ = X, or E4M3-RNE(X) for E4M3 and MXFP4 weights), g =
  * BF16-RNE(sigmoid(z) - y), dX += g W_old, dW = g^T X, t = fmaf(-lr, dW, w), W = SR(t) (for MXFP4
  * per 32-element block, as described with the formats).
+ * Kernels: the faster of the two implementations for the shape: the single-pass step of
+ * elmo_xmc_step_single_pass where it is built (B <= 32 and D = 256, 512 or 768), else the
+ * two-kernel step of elmo_xmc_step_two_kernel. Both follow the rule above with the same random
+ * bits; they sum each logit in a different order (see elmo_xmc_step_single_pass).
  */
 #define ELMO_FLAG_LABEL_RANGE 1u
 #define ELMO_FLAG_ROW_PTR 2u
@@ -100,6 +104,18 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B,
                   const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr, uint64_t seed,
                   uint64_t step, int64_t chunk, float* dX, float* loss_sum, void* workspace,
                   size_t workspace_bytes, void* stream);
+/*
+ * The step as two kernels per label chunk, for every supported shape (summary page, "Approach":
+ * the label dimension chunked, the gradient fused with the SGD update): a forward kernel writes the
+ * chunk's BF16 gradient G (the one chunk-sized transient), then a backward kernel computes dX and
+ * dW from it and updates the weights in place, dW never leaving its registers. Arguments,
+ * workspace, results and errors as elmo_xmc_step, which takes this path for B > 32 or D not in
+ * {256, 512, 768}.
+ */
+int elmo_xmc_step_two_kernel(void* W, int wdtype, int64_t L, int D, const void* X, int B,
+                             const int32_t* row_ptr, const int32_t* ids, int64_t nnz, float lr,
+                             uint64_t seed, uint64_t step, int64_t chunk, float* dX, float* loss_sum,
+                             void* workspace, size_t workspace_bytes, void* stream);
 /*
  * The same step as elmo_xmc_step computed in a single pass over the weights (summary page,
  * "Approach": the classifier gradient fused with the SGD update; arXiv abstract: "gradient
@@ -131,6 +147,7 @@ int elmo_xmc_step_single_pass(void* W, int wdtype, int64_t L, int D, const void*
  * 131,072 labels (3M-label E4M3 step: 97 MB); at B = 128, D = 768, chunks of 262,144 BF16 labels.
  * Every call on one GPU uses that GPU's array: calls that overlap on one GPU (other streams or
  * threads) race and give undefined results; serialise them. The flags word is not readable here.
+ * It runs the two-kernel step (elmo_xmc_step_two_kernel) for every shape.
  */
 #define ELMO_NOALLOC_SCRATCH_BYTES (128u << 20)
 int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B,

@@ -59,6 +59,8 @@ def lib():
         L.elmo_xmc_step_workspace_bytes.restype = sz
         L.elmo_xmc_step.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P, sz, P]
         L.elmo_xmc_step.restype = i32
+        L.elmo_xmc_step_two_kernel.argtypes = L.elmo_xmc_step.argtypes
+        L.elmo_xmc_step_two_kernel.restype = i32
         L.elmo_xmc_step_single_pass.argtypes = [P, i32, i64, i32, P, i32, P, P, i64, f32, u64, u64, i64, P, P, P,
                                                 P, sz, P]
         L.elmo_xmc_step_single_pass.restype = i32
@@ -126,9 +128,10 @@ def step_workspace_bytes(B, D, L, chunk, wdtype, max_nnz):
 
 
 def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, workspace=None, wfmt=None,
-         single_pass=False, g_out=None):
+         single_pass=None, g_out=None):
     """One fused training step; W is updated in place. Returns (dX [B, D] float32, loss tensor|None).
-    single_pass=True calls elmo_xmc_step_single_pass (B <= 32, D in 256/512/768) instead; g_out (an
+    single_pass=None calls elmo_xmc_step (the faster path for the shape), False
+    elmo_xmc_step_two_kernel, True elmo_xmc_step_single_pass (B <= 32, D in 256/512/768); g_out (an
     int16 [B, L] device tensor) then receives the gradient codes it used."""
     _check_dev(W, X, row_ptr, ids)
     wd, L, D = _wdims(W, wfmt)
@@ -155,10 +158,10 @@ def step(W, X, row_ptr, ids, lr, seed, step, chunk, want_loss=False, dX=None, wo
     else:
         if g_out is not None:
             raise ValueError("g_out is a diagnostic of the single-pass step")
-        name = "elmo_xmc_step"
-        rc = lib().elmo_xmc_step(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None, nnz,
-                                 float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss),
-                                 _ptr(workspace), workspace.numel(), _stream())
+        name = "elmo_xmc_step" if single_pass is None else "elmo_xmc_step_two_kernel"
+        rc = getattr(lib(), name)(_ptr(W), wd, L, D, _ptr(X), B, _ptr(row_ptr), _ptr(ids) if nnz else None,
+                                  nnz, float(lr), int(seed), int(step), int(chunk), _ptr(dX), _ptr(loss),
+                                  _ptr(workspace), workspace.numel(), _stream())
     _chk(name, rc)
     global last_workspace
     last_workspace = workspace

@@ -27,17 +27,23 @@ int check_shapes(int B, int D, int64_t L) {
   return ELMO_OK;
 }
 
+// which kernels a step runs: the faster for its shape (the single pass where it is built, B <= 32
+// and D = 256, 512 or 768), or the one the caller names
+enum { PATH_AUTO = 0, PATH_TWO_KERNEL = 1, PATH_SINGLE = 2 };
+
 int step_entry(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
                const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk, float* dX,
                float* loss_sum, uint16_t* g_out, void* workspace, size_t workspace_bytes, void* stream,
-               bool single) {
+               int path) {
   int rc = check_format(wdtype, D);
   if (rc != ELMO_OK) return rc;
   if ((rc = check_shapes(B, D, L)) != ELMO_OK) return rc;
   if (chunk < 1 || nnz < 0 || !std::isfinite(lr)) return ELMO_EINVAL;
   if (!W || !X || !row_ptr || !dX || (nnz > 0 && !ids)) return ELMO_EINVAL;
   if (!aligned16(W) || !aligned16(X) || !aligned16(dX)) return ELMO_EINVAL;
-  if (single && !elmo::single_pass_shape(elmo::padded_batch(B), D)) return ELMO_EUNSUPPORTED;
+  const bool fits = elmo::single_pass_shape(elmo::padded_batch(B), D);
+  if (path == PATH_SINGLE && !fits) return ELMO_EUNSUPPORTED;
+  const bool single = path == PATH_SINGLE || (path == PATH_AUTO && fits);
   if (!workspace || !aligned16(workspace)) return ELMO_EWORKSPACE;
   const elmo::StepLayout s = elmo::step_layout(B, D, L, chunk, wdtype, nnz);
   if (workspace_bytes < s.total) return ELMO_EWORKSPACE;
@@ -79,7 +85,14 @@ int elmo_xmc_step(void* W, int wdtype, int64_t L, int D, const void* X, int B, c
                   const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
                   float* dX, float* loss_sum, void* workspace, size_t workspace_bytes, void* stream) {
   return step_entry(W, wdtype, L, D, X, B, row_ptr, ids, nnz, lr, seed, step, chunk, dX, loss_sum, nullptr,
-                    workspace, workspace_bytes, stream, false);
+                    workspace, workspace_bytes, stream, PATH_AUTO);
+}
+
+int elmo_xmc_step_two_kernel(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
+                             const int32_t* ids, int64_t nnz, float lr, uint64_t seed, uint64_t step, int64_t chunk,
+                             float* dX, float* loss_sum, void* workspace, size_t workspace_bytes, void* stream) {
+  return step_entry(W, wdtype, L, D, X, B, row_ptr, ids, nnz, lr, seed, step, chunk, dX, loss_sum, nullptr,
+                    workspace, workspace_bytes, stream, PATH_TWO_KERNEL);
 }
 
 int elmo_xmc_step_single_pass(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,
@@ -88,7 +101,7 @@ int elmo_xmc_step_single_pass(void* W, int wdtype, int64_t L, int D, const void*
                               size_t workspace_bytes, void* stream) {
   if (g_out && ((uintptr_t)g_out & 1u)) return ELMO_EINVAL;
   return step_entry(W, wdtype, L, D, X, B, row_ptr, ids, nnz, lr, seed, step, chunk, dX, loss_sum, g_out,
-                    workspace, workspace_bytes, stream, true);
+                    workspace, workspace_bytes, stream, PATH_SINGLE);
 }
 
 int elmo_xmc_step_noalloc(void* W, int wdtype, int64_t L, int D, const void* X, int B, const int32_t* row_ptr,

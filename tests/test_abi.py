@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["elmo_xmc_step", "elmo_xmc_topk", "elmo_xmc_step_workspace_bytes", "elmo_xmc_topk_workspace_bytes",
               "elmo_xmc_logits", "elmo_numerics_probe", "elmo_status_str", "elmo_abi_version", "elmo_xmc_step_flags",
-              "elmo_kahan_update", "elmo_xmc_step_single_pass"]:
+              "elmo_kahan_update", "elmo_xmc_step_single_pass", "elmo_xmc_step_two_kernel"]:
         assert n in names
 
 
@@ -128,3 +128,13 @@ def test_workspace_holds_the_single_pass_partials():
     big = elmo.step_workspace_bytes(32, 768, 8_600_000, 262_144, 0, 100)
     assert small >= 32 * (32 * 768 * 4)
     assert big >= 256 * (32 * 768 * 4)
+
+
+def test_two_kernel_step_validates_like_the_step(L):
+    null = None
+    p = ctypes.c_void_p(4096)
+    f = L.elmo_xmc_step_two_kernel
+    assert f(null, 5, 1000, 768, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, 0, null) == -3
+    assert f(null, 0, 1000, 100, null, 4, null, null, 0, 0.1, 0, 0, 128, null, null, null, 0, null) == -2
+    assert f(p, 0, 1000, 768, p, 4, p, p, 1, float("nan"), 0, 0, 128, p, null, p, 1 << 30, null) == -1
+    assert f(p, 0, 1000, 768, p, 32, p, p, 1, 0.1, 0, 0, 128, p, null, p, 16, null) == -4

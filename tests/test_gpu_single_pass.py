@@ -158,3 +158,23 @@ def test_single_pass_no_labels(elmo, orc):
     empty = wk.Batch(bt.X, np.zeros(33, np.int32), np.zeros(0, np.int32))
     Wg, dXg, lossg, Gg = _run(elmo, W0, empty, wk.W_BF16, 0.05, 4, 2, 1024, want_loss=True)
     check_single(orc, W0, empty, wk.W_BF16, 0.05, 4, 2, Wg, dXg, lossg, Gg)
+
+
+@pytest.mark.parametrize("B,D,wfmt", [(32, 768, wk.W_BF16), (7, 256, wk.W_MXFP4), (33, 768, wk.W_E4M3),
+                                      (32, 640, wk.W_BF16)])
+def test_default_step_takes_the_faster_path(elmo, B, D, wfmt):
+    """elmo_xmc_step runs the single pass where it is built (B <= 32, D in 256/512/768) and the two
+    kernels elsewhere: its weights and dX are bit-identical to the entry point of that path."""
+    wl, W0, bt = _case(B, D, 1500, wfmt)
+    fmt = elmo.ELMO_W_MXFP4 if wfmt == wk.W_MXFP4 else None
+    single = B <= 32 and D in (256, 512, 768)
+    outs = []
+    for sp in (None, single if single else False):
+        W = to_dev_codes(W0)
+        X, rp, ids = batch_to_dev(bt)
+        print(f"  B={B} D={D} wfmt={wfmt} single_pass={sp}", flush=True)
+        dX, _ = elmo.step(W, X, rp, ids, 0.05, 3, 2, 512, wfmt=fmt, single_pass=sp)
+        torch.cuda.synchronize()
+        outs.append((W.cpu().numpy(), dX.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])

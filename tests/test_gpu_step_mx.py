@@ -31,7 +31,10 @@ def _run(elmo, W0, bt, lr, seed, step, chunk, want_loss=False):
     X, rp, ids = batch_to_dev(bt)
     D = W0.shape[1] * 32 // 17
     print(f"  mx step B={bt.X.shape[0]} D={D} L={W0.shape[0]} chunk={chunk}", flush=True)
-    dX, loss = elmo.step(W, X, rp, ids, lr, seed, step, chunk, want_loss=want_loss, wfmt=elmo.ELMO_W_MXFP4)
+    # (the two-kernel step, also at the shapes where elmo_xmc_step takes the single pass; that path
+    # has its own tests)
+    dX, loss = elmo.step(W, X, rp, ids, lr, seed, step, chunk, want_loss=want_loss, wfmt=elmo.ELMO_W_MXFP4,
+                         single_pass=False)
     torch.cuda.synchronize()
     return W.cpu().numpy(), dX.cpu().numpy(), (float(loss.item()) if want_loss else None)
 
