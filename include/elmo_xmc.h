@@ -180,8 +180,9 @@ int elmo_xmc_logits(const void* W, int wdtype, int64_t L, int D, int64_t l0, int
 
 /*
  * Diagnostic: the step's forward kernel over labels [l0, l1) with the step's label handling,
- * writing the FP32 logits Z and/or the BF16 gradient codes G = BF16(sigmoid(Z) - Y) that a step
- * with the same inputs uses (each [B, l1 - l0] row-major, nullable but not both). Weights are not
+ * writing the FP32 logits Z and/or the BF16 gradient codes G = BF16(sigmoid(Z) - Y) that a
+ * two-kernel step with the same inputs uses (each [B, l1 - l0] row-major, nullable but not both;
+ * the single-pass step reports its own codes through its g_out). Weights are not
  * touched. Labels as for elmo_xmc_step (row_ptr/ids may be NULL when nnz = 0). Workspace as for
  * elmo_xmc_step with chunk = l1 - l0 and max_nnz = nnz.
  */
