@@ -112,10 +112,13 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], 
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   (void)smem; (void)gpitch;
   float lsum = 0.0f;
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
+  // (unrolled at compile time: with the loss inlined, a pragma-directed unroll of 4 x 2 blocks at
+  // 256 samples exceeds the compiler's size limit, and the accumulators would then be indexed at
+  // run time, that is, through scratch memory)
+  static_for<0, MI>([&](auto MIc) {
+    constexpr int mi = decltype(MIc)::value;
+    static_for<0, NI>([&](auto NIc) {
+      constexpr int ni = decltype(NIc)::value;
       const int jl = wj * CW + ni * 32 + l32;
       const bool jvalid = jbase + jl < clen;
       const int bb = wb * RW + mi * 32;
@@ -139,8 +142,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16_t (&acc)[RW / 32][CW / 32], 
         }
       }
       if constexpr (!ZOUT) fwd_store_block(gv, G, MB, jbase + jl, bb, lane);
-    }
-  }
+    });
+  });
   if constexpr (LOSS) {
     for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
     if (lane == 0) lred[wave] = lsum;
