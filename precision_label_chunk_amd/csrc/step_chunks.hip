@@ -600,8 +600,10 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     for (int kk = 0; kk < KK; ++kk) xT[kk] = __builtin_bit_cast(s16x8_t, buffer_load16(xres, xo, kk * 1024));
   }
   // dX^T accumulators, starting from this range's running partial sum (a fixed slot per range:
-  // deterministic; zero in the step's first chunk, where every slot has a range), read here under
-  // the first tile's staging and stored back at the end. The partial keeps the accumulators' own
+  // deterministic; zero in the step's first chunk, where every slot has a range), read after the
+  // first tile's staging loads have been issued (so that the tile's LDS writes and first dW MFMAs
+  // do not wait for the 128 KiB of partials: the vector-memory counter retires in order) and
+  // stored back at the end. The partial keeps the accumulators' own
   // layout, lane l's registers 4 ig .. 4 ig + 3 of sample block sb at ((sb * 4 + ig) * 64 + l) * 4
   // within the wave's feature block, so that every access is 1 KiB contiguous.
   // With four sample blocks per wave and an even number of feature blocks, each wave takes a 2 x 2
@@ -615,13 +617,18 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
   float* slot = part + (int64_t)r * (D / 32) * (MB * 32) + 4 * lane;
   auto pslot = [&](int a, int ig) { return slot + (dsl / 32 + xfb(a)) * (MB * 32) + (xsb(a) * 4 + ig) * 256; };
   f32x16_t accX[NBW];
+  // (through a resource of zero bytes in the first chunk, which reads zeros without a branch per load)
+  const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(part + (int64_t)r * (D / 32) * (MB * 32), first ? 0 : D * MB * 4);
+  auto init_acc = [&]() {
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-    for (int ig = 0; ig < 4; ++ig) {
-      const f32x4_t o = first ? f32x4_t{} : *(const f32x4_t*)pslot(nb, ig);
-      accX[nb][4 * ig] = o[0]; accX[nb][4 * ig + 1] = o[1]; accX[nb][4 * ig + 2] = o[2]; accX[nb][4 * ig + 3] = o[3];
-    }
+      for (int ig = 0; ig < 4; ++ig) {
+        const int off = ((dsl / 32 + xfb(nb)) * (MB * 32) + (xsb(nb) * 4 + ig) * 256 + 4 * lane) * 4;
+        const f32x4_t o = __builtin_bit_cast(f32x4_t, buffer_load16(pres, off));
+        accX[nb][4 * ig] = o[0]; accX[nb][4 * ig + 1] = o[1]; accX[nb][4 * ig + 2] = o[2]; accX[nb][4 * ig + 3] = o[3];
+      }
+  };
 
   // loop-invariant LDS element offsets (rows of both label blocks share the swizzle: it only
   // depends on the row's low 4 bits)
@@ -821,10 +828,16 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
     wbP = wb;
   };
 
-  if (t0 < t1) {
+  // every range has a tile (the host launches at most as many ranges as the chunk has tiles), so
+  // every slot of the first chunk is written
+  if (t0 >= t1) return;
+  {
     using G0 = std::integral_constant<int, 0>;
     using G1 = std::integral_constant<int, 1>;
     static_for<0, NLD>([&](auto K) { load_item(K, t0); });
+    sched_fence();
+    init_acc();
+    sched_fence();
     static_for<0, NLD>([&](auto K) { store_item(K, Gs0, 0); });
     if constexpr (NH == 1) {
       // one wave per SIMD: the previous tile's update is spread between this tile's MFMAs
