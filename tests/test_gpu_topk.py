@@ -40,7 +40,9 @@ def _check(elmo, orc, wfmt, W0, Wd, X, idx_g, sc_g, k, label=""):
                                           (70, 128, 3000, 64, wk.W_BF16), (130, 256, 2000, 64, wk.W_E4M3),
                                           (3, 64, 64, 64, wk.W_BF16), (300, 256, 5000, 5, wk.W_MXFP4),
                                           (129, 768, 3000, 32, wk.W_MXFP4), (70, 512, 2000, 64, wk.W_MXFP4),
-                                          (1, 256, 130, 8, wk.W_MXFP4),
+                                          (1, 256, 130, 8, wk.W_MXFP4), (257, 768, 4099, 8, wk.W_E4M3),
+                                          (1, 768, 130, 1, wk.W_E4M3), (600, 768, 20000, 5, wk.W_E4M3),
+                                          (13, 768, 40, 8, wk.W_E4M3),
                                           # D = 768, k <= 8 in MXFP4: the stationary-query scan
                                           (300, 768, 5000, 5, wk.W_E4M3), (257, 768, 4099, 8, wk.W_MXFP4),
                                           (1, 768, 130, 1, wk.W_MXFP4), (600, 768, 20000, 5, wk.W_MXFP4),
