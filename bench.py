@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--steps-third", type=int, default=10, help="timed steps of the third workload")
     ap.add_argument("--small-workloads", default="bf16_131k,bf16_670k",
                     help="comma-separated further workloads timed without top-k and CPU baseline, or 'none'")
+    ap.add_argument("--shard-workloads", default="e4m3_375k,bf16_1075k",
+                    help="one GPU's share of the 3M- and 8.6M-label heads split over eight GPUs (none: skip)")
     ap.add_argument("--single-pass-workloads", default="bf16_8p6m_b32,e4m3_3m_b32",
                     help="comma-separated workloads (B <= 32) timed with the single-pass step and the two-kernel "
                          "step side by side, or 'none'")
@@ -169,7 +171,7 @@ def summarize_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 2 "
               f"--warmup 1 --no-cpu-baseline --no-topk --no-kahan --second-workload none --third-workload none "
-              f"--single-pass-workloads none --small-workloads none --workload {workload}"
+              f"--single-pass-workloads none --small-workloads none --shard-workloads none --workload {workload}"
               f"{' --single-pass' if single else ''}")
     for c, d in (("FETCH_SIZE", copy_fetch_dir), ("WRITE_SIZE", copy_write_dir)):
         print(f"#   export TMPDIR=/tmp && rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
@@ -604,6 +606,13 @@ def main():
     # the 131k- and 670k-label BF16 heads (B = 256), each in an object of its own
     for name in [w for w in args.small_workloads.split(",") if w and w != "none"]:
         out[name] = bench_workload(name, args.steps_third, 2, args, with_topk=False, with_cpu=False)
+
+    # one GPU's share of each head split by label ranges over eight GPUs: the kernels at a shard's
+    # real shape (the one exchange such a split needs, an all-reduce of dX, is not run here)
+    shards = [w for w in args.shard_workloads.split(",") if w and w != "none"]
+    if shards:
+        out["label_shard_of_8"] = {name: bench_workload(name, args.steps_third, 2, args, with_topk=False, with_cpu=False)
+                                   for name in shards}
 
     # the single-pass step beside the two-kernel step on the same small-batch workloads
     sp = [w for w in args.single_pass_workloads.split(",") if w and w != "none"]

@@ -18,7 +18,8 @@ def test_bench_json_line_on_the_tiny_workload():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3", "--warmup", "1",
            "--topk-n", "64", "--kahan-params", "100000", "--cpu-seconds", "0.3", "--second-workload", "bf16_131k",
            "--steps-8p6m", "2", "--third-workload", "mxfp4_131k", "--steps-third", "2",
-           "--small-workloads", "bf16_670k", "--single-pass-workloads", "e4m3_3m_b32", "--steps-single", "2"]
+           "--small-workloads", "bf16_670k", "--single-pass-workloads", "e4m3_3m_b32", "--steps-single", "2",
+           "--shard-workloads", "e4m3_375k"]
     print("  " + " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -60,3 +61,6 @@ def test_bench_json_line_on_the_tiny_workload():
     assert sp["single_pass"]["roofline"]["kernel"] == "k_step_single" and sp["single_pass"]["roofline"]["bound"] == "hbm"
     assert sp["two_kernel"]["roofline"]["kernel"] == "k_bwd_update"
     assert sp["speedup"] == pytest.approx(sp["two_kernel"]["ms_per_step"] / sp["single_pass"]["ms_per_step"], rel=1e-2)
+    sh = d["label_shard_of_8"]["e4m3_375k"]
+    assert sh["config"]["L"] == 375000 and sh["config"]["B"] == 256 and sh["samples_s"] > 0
+    assert sh["roofline"]["kernel"] == "k_bwd_update" and sh["roofline"]["launches"] == 2 * 3   # 3 chunks per step

@@ -79,6 +79,12 @@ WORKLOADS = {
                               "rownorm", "zipf", lam=9.0, zipf_s=1.2, tag=7),
     "e4m3_3m_b32": Workload("xmc-e4m3-L3000000-D768-B32", 32, 768, 3000000, 131072, W_E4M3, 0.1, 10,
                             "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=8),
+    # one GPU's share of each head when its labels are split into eight contiguous ranges (the same
+    # batch; positives drawn by the same recipe over the shard's own labels)
+    "e4m3_375k": Workload("xmc-e4m3-L375000-D768-B256", 256, 768, 375000, 131072, W_E4M3, 0.1, 10,
+                          "rownorm", "zipf", lam=35.0, zipf_s=1.0, tag=9),
+    "bf16_1075k": Workload("xmc-bf16-L1075000-D768-B128", 128, 768, 1075000, 262144, W_BF16, 0.05, 5,
+                           "rownorm", "zipf", lam=9.0, zipf_s=1.2, tag=10),
 }
 
 
