@@ -897,8 +897,8 @@ __global__ __launch_bounds__(DS * 2 * NH) void k_bwd_update(uint8_t* __restrict_
 // (48 KiB each, row pitch 1,552 bytes: an odd number of 16-byte groups, so 16 consecutive rows'
 // fragment reads fall on distinct banks), two buffers as in k_fwd_xs: tile t is loaded into
 // registers at the start of iteration t - 1 and written to LDS at its end. Per tile a wave runs
-// 48 MFMAs into two accumulators (even and odd K steps, so that consecutive MFMAs are independent)
-// and the gradient epilogue of its 32 x 32 block; one barrier per iteration; the positives of tile
+// 48 MFMAs into one accumulator in K order and the gradient epilogue of its 32 x 32 block; one
+// barrier per iteration; the positives of tile
 // i + 1 are gathered into label bits during iteration i. Work-groups take tiles blockIdx.x,
 // + gridDim.x, ...; tiles past the chunk read as zero, and the tiles cover whole 64-label
 // backward tiles, so every G row the backward reads is written (zeros past the chunk).
@@ -991,8 +991,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
   float lsum = 0.0f;
   for (int i = 0; i < nmy; ++i) {
     if (i + 1 < nmy) wload(tile_of(i + 1), stg);
-    // the tile's 48 MFMAs, each weight fragment read from LDS two K steps ahead
-    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+    // the tile's 48 MFMAs, one chain in K order (the sums of the tiled forward and of the top-k
+    // scans, so that a BF16 logit has the same bits whichever kernel computes it), each weight
+    // fragment read from LDS two K steps ahead
+    f32x16_t z = f32x16_t{};
     {
       const uint8_t* wb = &Ws[i & 1][l32 * PITCH + hi * 16];
       auto rd = [&](int kk) { return *(const s16x8_t*)(wb + kk * 32); };
@@ -1001,13 +1003,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_xb(const uint8_t* __restrict__ W
       static_for<0, NK>([&](auto K) {
         constexpr int kk = decltype(K)::value;
         if constexpr (kk + 2 < NK) f[(kk + 2) % 3] = rd(kk + 2);
-        acc[kk & 1] = mfma_bf16(xf[kk], f[kk % 3], acc[kk & 1]);
+        z = mfma_bf16(xf[kk], f[kk % 3], z);
         sched_fence();
       });
     }
-    f32x16_t z;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) z[r] = acc[0][r] + acc[1][r];
     {
       const int t = tile_of(i);
       const int jc = t * XB_TJ + l32;                 // label within the chunk

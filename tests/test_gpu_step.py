@@ -311,3 +311,21 @@ def test_sample_permutation_general(elmo, orc, wfmt):
     eq, mx, _ = weight_report(Wp, Wa, wfmt)
     print(f"  permuted vs unpermuted weights: equal {eq:.6f}, max code distance {mx}", flush=True)
     assert eq >= 0.999
+
+
+def test_bf16_logits_have_the_same_bits_in_every_forward(elmo):
+    """Every BF16 forward sums a logit as one MFMA chain over the features in order (the tiled
+    forward at 256 and at 32 padded samples, the stationary-feature forward at 65-128, and the
+    tiled top-k scan): the same queries' logits, computed in batches that take different forward
+    kernels, are bit-identical."""
+    wl = wk.scaled(wk.WORKLOADS["bf16_131k"], B=256, D=768, L=3000)
+    W0 = wk.make_weights(wl)
+    X = wk.make_batch(wl).X
+    Wd = to_dev_codes(W0)
+    Z = {}
+    for n in (256, 100, 20):
+        print(f"  BF16 logits of {n} queries over {W0.shape[0]} labels", flush=True)
+        Xd = torch.from_numpy(np.ascontiguousarray(X[:n]).view(np.int16)).cuda()
+        Z[n] = elmo.logits(Wd, Xd, 0, W0.shape[0]).cpu().numpy()
+    assert np.array_equal(Z[256][:100].view(np.uint32), Z[100].view(np.uint32))
+    assert np.array_equal(Z[256][:20].view(np.uint32), Z[20].view(np.uint32))

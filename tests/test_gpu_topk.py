@@ -43,6 +43,11 @@ def _check(elmo, orc, wfmt, W0, Wd, X, idx_g, sc_g, k, label=""):
                                           (1, 256, 130, 8, wk.W_MXFP4), (257, 768, 4099, 8, wk.W_E4M3),
                                           (1, 768, 130, 1, wk.W_E4M3), (600, 768, 20000, 5, wk.W_E4M3),
                                           (13, 768, 40, 8, wk.W_E4M3),
+                                          # BF16 at D = 768: the scores of 600 queries against logits from
+                                          # both BF16 forwards (256-row blocks tiled, the last 88 rows
+                                          # stationary), bit for bit
+                                          (257, 768, 4099, 8, wk.W_BF16), (1, 768, 130, 1, wk.W_BF16),
+                                          (600, 768, 20000, 5, wk.W_BF16), (13, 768, 40, 8, wk.W_BF16),
                                           # D = 768, k <= 8 in MXFP4: the stationary-query scan
                                           (300, 768, 5000, 5, wk.W_E4M3), (257, 768, 4099, 8, wk.W_MXFP4),
                                           (1, 768, 130, 1, wk.W_MXFP4), (600, 768, 20000, 5, wk.W_MXFP4),
@@ -97,7 +102,7 @@ def test_topk_nan_scores_rank_last(elmo, orc):
 
 
 @pytest.mark.parametrize("wfmt,D", [(wk.W_BF16, 64), (wk.W_E4M3, 64), (wk.W_MXFP4, 256), (wk.W_E4M3, 768),
-                                    (wk.W_MXFP4, 768)])
+                                    (wk.W_MXFP4, 768), (wk.W_BF16, 768)])
 def test_topk_many_tiles_per_range(elmo, orc, wfmt, D):
     """4096 queries over 60k labels: each work-group scans some 30 label tiles, so the lists fill
     and later tiles take the bounded-candidate path (lists of up to 8). Its top-8 must equal, bit for
